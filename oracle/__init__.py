@@ -1,0 +1,127 @@
+"""CPU oracle for segmented reduction and run-length encoding.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline
+leg of the benchmark may import this package; the product (the HIP library
+and its Python binding) never does.  It shares no code with the HIP path.
+
+The arithmetic lives in ``oracle.c`` (plain C, one thread, double-precision
+accumulation, rows in ascending order); this module builds it with gcc and
+marshals numpy arrays into it.  See the header of ``oracle.c`` for the pages
+and readings each function follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+DTYPES = {"u32": 0, "i32": 1, "f32": 2}
+OPS = {"sum": 0, "min": 1, "max": 2, "mean": 3}
+_NP = {"u32": np.uint32, "i32": np.int32, "f32": np.float32}
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math) into a shared library."""
+    cmd = ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-fPIC", "-shared", src, "-o", out + ".tmp"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def load(path: str | None = None):
+    """Load a compiled oracle library (building the default one if absent)."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+            _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _bind(lib):
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.oracle_reduce.argtypes = [vp, i32, i64, vp, i64, i32, vp, vp, vp, vp]
+    lib.oracle_reduce.restype = ctypes.c_int
+    lib.oracle_rle.argtypes = [vp, i64, vp, vp, vp, vp]
+    lib.oracle_rle.restype = ctypes.c_int
+    lib.oracle_order_key.argtypes = [ctypes.c_uint32, i32]
+    lib.oracle_order_key.restype = ctypes.c_uint32
+    return lib
+
+
+def dtype_name(arr: np.ndarray) -> str:
+    for name, t in _NP.items():
+        if arr.dtype == t:
+            return name
+    raise TypeError(f"unsupported dtype {arr.dtype}")
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+class Reduced:
+    """Result of ``reduce``: out [S, F]; arg [S, F] (min/max);
+    ref and mag [S, F] float64 (float32 sum/mean: the double result and sum|x|)."""
+
+    def __init__(self, out, arg=None, ref=None, mag=None):
+        self.out, self.arg, self.ref, self.mag = out, arg, ref, mag
+
+
+def reduce(values: np.ndarray, offsets: np.ndarray, op: str, lib=None) -> Reduced:
+    """Segmented reduction of ``values`` ([rows] or [rows, F]) over int64 ``offsets``."""
+    lib = lib or load()
+    values = np.ascontiguousarray(values)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int64)
+    dt = dtype_name(values)
+    feat = 1 if values.ndim == 1 else int(np.prod(values.shape[1:]))
+    s = int(offsets.shape[0]) - 1
+    if s < 0:
+        raise ValueError("offsets needs at least one entry")
+    out = np.zeros((s, feat), dtype=np.float32 if op == "mean" else _NP[dt])
+    arg = np.zeros((s, feat), dtype=np.int64) if op in ("min", "max") else None
+    ref = mag = None
+    if dt == "f32" and op in ("sum", "mean"):
+        ref = np.zeros((s, feat), dtype=np.float64)
+        mag = np.zeros((s, feat), dtype=np.float64)
+    rc = lib.oracle_reduce(_ptr(values), DTYPES[dt], feat, _ptr(offsets), s, OPS[op],
+                           _ptr(out), _ptr(arg), _ptr(ref), _ptr(mag))
+    if rc != 0:
+        raise ValueError(f"oracle_reduce rejected dtype={dt} op={op} feat={feat}")
+    return Reduced(out, arg, ref, mag)
+
+
+def rle(keys: np.ndarray, lib=None):
+    """Run-length encode uint32 ``keys``: returns (values, lengths, offsets, count),
+    each array trimmed to its valid prefix (offsets has count + 1 entries)."""
+    lib = lib or load()
+    keys = np.ascontiguousarray(keys, dtype=np.uint32)
+    n = int(keys.shape[0])
+    values = np.zeros(max(n, 1), dtype=np.uint32)
+    lengths = np.zeros(max(n, 1), dtype=np.uint32)
+    offsets = np.zeros(n + 1, dtype=np.int64)
+    count = np.zeros(1, dtype=np.int64)
+    rc = lib.oracle_rle(_ptr(keys), n, _ptr(values), _ptr(lengths), _ptr(offsets), _ptr(count))
+    if rc != 0:
+        raise ValueError("oracle_rle rejected its input")
+    c = int(count[0])
+    return values[:c], lengths[:c], offsets[: c + 1], c
+
+
+def order_key(bits: int, dtype: str, lib=None) -> int:
+    """The monotone uint32 key the oracle orders min/max by."""
+    lib = lib or load()
+    return int(lib.oracle_order_key(ctypes.c_uint32(bits & 0xFFFFFFFF), DTYPES[dtype]))

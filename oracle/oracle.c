@@ -1,0 +1,206 @@
+/*
+ * oracle.c -- the plain, slow CPU oracle for segmented reduction over
+ * offset-delimited segments and for the run-length encoding that produces
+ * such segments.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load or call this code.  The HIP
+ * library never links, loads or calls it, and the two share no code, header,
+ * table or helper.
+ *
+ * Everything here is the plain definition written out, one segment and one
+ * feature at a time, rows in ascending order, in one thread:
+ *
+ *   - luma.gl "GPUSegmentedReduction", sections "What is an offset-delimited
+ *     segment?" and "Contract": segment s owns rows [offsets[s], offsets[s+1]);
+ *     S segments take S+1 offsets; a repeated offset is an empty segment; the
+ *     offsets need not start at 0 (output row i reduces input[o_i..o_{i+1})).
+ *   - same page, "What is segmented reduction?" and "Contract": one sum,
+ *     minimum or maximum per segment over uint32, sint32 or float32 values;
+ *     an empty segment produces zero.
+ *   - phanerozoic/graph-reduce README, "API": mean is sum divided by the
+ *     segment length, empty outputs are 0; min and max also return the row
+ *     that produced them; the input is [N, ...] reduced over dimension 0.
+ *   - same README, "Method" and "Correctness": floats are ordered through a
+ *     monotone map of their bit pattern to an integer; ties go to the lower
+ *     row; an empty min/max segment has arg -1.
+ *   - luma.gl "GPURunLengthEncode and GPUUnique", sections "What is run-length
+ *     encoding?", "Why RLE matters for GPU grouping" and "Contract": each
+ *     adjacent run of equal uint32 values becomes (value, length), first
+ *     occurrence order is kept, lengths [3,2,4] correspond to offsets
+ *     [0,3,5,9], an empty input gives count 0.
+ *
+ * Readings where the pages leave a step open (each one is also listed in the
+ * design notes of the repository):
+ *   - integer sums wrap modulo 2^32 (the pages are silent on overflow);
+ *   - floating-point sums are accumulated in double precision in row order and
+ *     rounded to float32 once; the double sum and the sum of magnitudes are
+ *     returned as well, for the tolerance |gpu - ref| <= 1e-5 * sum|x| + 1e-6;
+ *   - the order used by min/max is the monotone key below for every dtype, so
+ *     -0.0 < +0.0 and NaNs sit at the ends ordered by their bits; a tie means
+ *     identical bits, hence out == values[arg] bit for bit;
+ *   - arg is the absolute row index (int64) per (segment, feature);
+ *   - empty min/max: value 0 (luma.gl contract) with arg -1 (graph-reduce).
+ */
+#include <stdint.h>
+#include <string.h>
+
+#define ORC_U32 0
+#define ORC_I32 1
+#define ORC_F32 2
+
+#define ORC_SUM 0
+#define ORC_MIN 1
+#define ORC_MAX 2
+#define ORC_MEAN 3
+
+/*
+ * Monotone order key (graph-reduce README, "Method": a float's bit pattern
+ * made monotone as an integer).  Keys compare as unsigned 32-bit integers:
+ *   uint32  -> the bits themselves;
+ *   int32   -> bits with the sign bit flipped (signed order);
+ *   float32 -> negative floats: all bits flipped; others: sign bit set.
+ */
+uint32_t oracle_order_key(uint32_t bits, int32_t dtype)
+{
+    if (dtype == ORC_U32)
+        return bits;
+    if (dtype == ORC_I32)
+        return bits ^ 0x80000000u;
+    if (bits & 0x80000000u)
+        return ~bits;
+    return bits | 0x80000000u;
+}
+
+static uint32_t load_bits(const void *values, int64_t index)
+{
+    uint32_t b;
+    memcpy(&b, (const unsigned char *)values + 4 * index, 4);
+    return b;
+}
+
+static float bits_to_float(uint32_t b)
+{
+    float f;
+    memcpy(&f, &b, 4);
+    return f;
+}
+
+static uint32_t float_to_bits(float f)
+{
+    uint32_t b;
+    memcpy(&b, &f, 4);
+    return b;
+}
+
+static void store_bits(void *out, int64_t index, uint32_t b)
+{
+    memcpy((unsigned char *)out + 4 * index, &b, 4);
+}
+
+/*
+ * oracle_reduce: out[s, f] = op over rows r in [offsets[s], offsets[s+1]) of
+ * values[r, f].  values is row-major [rows, feat] of 4-byte elements and
+ * rows are absolute indices (offsets[0] may be above 0).
+ *
+ *   out      [S, feat], same 4-byte type as values (float32 for MEAN);
+ *   arg_out  [S, feat] int64, MIN/MAX only, may be NULL;
+ *   ref_out  [S, feat] double, float32 SUM/MEAN only, may be NULL:
+ *            the double-precision sum (SUM) or sum / length (MEAN);
+ *   abs_out  [S, feat] double, float32 SUM/MEAN only, may be NULL:
+ *            the double-precision sum of |x| over the segment.
+ *
+ * Returns 0, or -1 for an argument it does not accept (MEAN of integers,
+ * feat < 1, unknown dtype or op).
+ */
+int oracle_reduce(const void *values, int32_t dtype, int64_t feat,
+                  const int64_t *offsets, int64_t num_segments, int32_t op,
+                  void *out, int64_t *arg_out, double *ref_out, double *abs_out)
+{
+    if (dtype < ORC_U32 || dtype > ORC_F32 || op < ORC_SUM || op > ORC_MEAN || feat < 1)
+        return -1;
+    if (op == ORC_MEAN && dtype != ORC_F32)
+        return -1;
+
+    for (int64_t s = 0; s < num_segments; ++s) {
+        const int64_t lo = offsets[s];
+        const int64_t hi = offsets[s + 1];
+        for (int64_t f = 0; f < feat; ++f) {
+            const int64_t o = s * feat + f;
+
+            if (op == ORC_SUM || op == ORC_MEAN) {
+                if (dtype == ORC_F32) {
+                    double sum = 0.0, mag = 0.0;
+                    for (int64_t r = lo; r < hi; ++r) {
+                        const double x = (double)bits_to_float(load_bits(values, r * feat + f));
+                        sum += x;
+                        mag += x < 0 ? -x : x;
+                    }
+                    double result = sum;
+                    if (op == ORC_MEAN)
+                        result = (hi > lo) ? sum / (double)(hi - lo) : 0.0;
+                    store_bits(out, o, float_to_bits((float)result));
+                    if (ref_out)
+                        ref_out[o] = result;
+                    if (abs_out)
+                        abs_out[o] = mag;
+                } else {
+                    uint32_t sum = 0u; /* wraps modulo 2^32 for both integer types */
+                    for (int64_t r = lo; r < hi; ++r)
+                        sum += load_bits(values, r * feat + f);
+                    store_bits(out, o, sum);
+                }
+                continue;
+            }
+
+            /* MIN / MAX with the producing row; strict comparison keeps the
+             * first (lowest) row among equal keys. */
+            if (hi <= lo) {
+                store_bits(out, o, 0u);
+                if (arg_out)
+                    arg_out[o] = -1;
+                continue;
+            }
+            int64_t best_row = lo;
+            uint32_t best_key = oracle_order_key(load_bits(values, lo * feat + f), dtype);
+            for (int64_t r = lo + 1; r < hi; ++r) {
+                const uint32_t k = oracle_order_key(load_bits(values, r * feat + f), dtype);
+                const int better = (op == ORC_MIN) ? (k < best_key) : (k > best_key);
+                if (better) {
+                    best_key = k;
+                    best_row = r;
+                }
+            }
+            store_bits(out, o, load_bits(values, best_row * feat + f));
+            if (arg_out)
+                arg_out[o] = best_row;
+        }
+    }
+    return 0;
+}
+
+/*
+ * oracle_rle: run-length encoding of n uint32 keys by adjacency (luma.gl
+ * RLE page).  Writes values[0..count), lengths[0..count), offsets[0..count]
+ * with offsets[count] = n, and *count.  Entries past the valid prefix are not
+ * touched.  Keys are compared bit for bit and need not be sorted.
+ */
+int oracle_rle(const uint32_t *keys, int64_t n, uint32_t *values, uint32_t *lengths,
+               int64_t *offsets, int64_t *count)
+{
+    if (n < 0)
+        return -1;
+    int64_t c = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (i == 0 || keys[i] != keys[i - 1]) {
+            values[c] = keys[i];
+            offsets[c] = i;
+            ++c;
+        }
+    }
+    offsets[c] = n;
+    for (int64_t r = 0; r < c; ++r)
+        lengths[r] = (uint32_t)(offsets[r + 1] - offsets[r]);
+    *count = c;
+    return 0;
+}

@@ -1,0 +1,83 @@
+"""Brute-force reference in pure Python, used only to pin the oracle.
+
+It is written independently of ``oracle/oracle.c``: Python integers and
+``math.fsum`` (the correctly rounded sum) instead of fixed-width arithmetic,
+Python's own float ordering instead of the monotone bit key, and
+``min``/``max`` over (value, row) tuples for the tie rule.  It only accepts
+inputs where Python's float order and the key order agree (finite floats, no
+mix of -0.0 and +0.0), which the callers guarantee.
+
+Semantics followed (luma.gl GPUSegmentedReduction page, "Contract";
+graph-reduce README, "API" and "Correctness"): segment s covers rows
+[offsets[s], offsets[s+1]); sum/min/max/mean per feature; empty segments give
+0 (and arg -1); min/max ties go to the lower row.
+"""
+from __future__ import annotations
+
+import math
+import struct
+
+
+def _f32(bits: int) -> float:
+    return struct.unpack("<f", struct.pack("<I", bits & 0xFFFFFFFF))[0]
+
+
+def _round_f32(x: float) -> float:
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def reduce(rows, offsets, op, kind, feat):
+    """rows: list of lists (rows x feat) of Python ints (u32/i32) or floats (f32).
+
+    Returns (out, arg, exact) as lists of lists [S][F]; ``exact`` holds the
+    correctly rounded float sum (or mean) for float inputs, else None.
+    """
+    out, arg, exact = [], [], []
+    for s in range(len(offsets) - 1):
+        lo, hi = offsets[s], offsets[s + 1]
+        o_row, a_row, e_row = [], [], []
+        for f in range(feat):
+            col = [(rows[r][f], r) for r in range(lo, hi)]
+            if op in ("sum", "mean"):
+                if kind == "f32":
+                    total = math.fsum(v for v, _ in col)
+                    val = total / (hi - lo) if (op == "mean" and hi > lo) else (total if op == "sum" else 0.0)
+                    e_row.append(val)
+                    o_row.append(_round_f32(val))
+                else:
+                    total = sum(v for v, _ in col) % (1 << 32)
+                    if kind == "i32" and total >= (1 << 31):
+                        total -= 1 << 32
+                    o_row.append(total)
+                a_row.append(None)
+            else:
+                if not col:
+                    o_row.append(0)
+                    a_row.append(-1)
+                    continue
+                # (value, row) tuples: the smallest/largest value, then the lowest row.
+                if op == "min":
+                    v, r = min(col)
+                else:
+                    v, r = max(col, key=lambda t: (t[0], -t[1]))
+                o_row.append(v)
+                a_row.append(r)
+        out.append(o_row)
+        arg.append(a_row)
+        exact.append(e_row)
+    return out, arg, (exact if kind == "f32" else None)
+
+
+def rle(keys):
+    """Adjacent runs by definition: a run continues while the next key equals it."""
+    values, lengths = [], []
+    for k in keys:
+        if values and values[-1] == k and lengths:
+            lengths[-1] += 1
+        else:
+            values.append(k)
+            lengths.append(1)
+    offsets = [0]
+    for ln in lengths:
+        offsets.append(offsets[-1] + ln)
+    return values, lengths, offsets

@@ -1,0 +1,336 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each ``pin_*`` function takes a loaded oracle library and raises
+AssertionError on a mismatch.  They are run against the real oracle by
+``test_oracle_pins.py`` and against planted mistakes by
+``test_oracle_mutants.py`` (every planted mistake must fail at least one pin).
+
+What each pin leans on:
+  - printed worked examples (tests/golden/*.json, each with its citation);
+  - brute force in pure Python (tests/brute_ref.py) on tiny random inputs;
+  - library routines for special cases (numpy reduceat / argmin / argmax,
+    itertools.groupby, math.fsum, torch.segment_reduce on the CPU);
+  - closed forms (integer wrap-around, integer-valued floats summed exactly);
+  - invariants of min/max + arg (gathered back, inside the segment, lowest row
+    among ties, nothing better in the segment).
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+import struct
+
+import numpy as np
+
+import oracle
+from tests import brute_ref
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+NP_T = {"u32": np.uint32, "i32": np.int32, "f32": np.float32}
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return json.load(fh)
+
+
+def _col(a):
+    return [x[0] for x in a.tolist()]
+
+
+# ---------------------------------------------------------------- printed examples
+
+def pin_worked_example(lib):
+    """luma.gl GPUSegmentedReduction, 'What is segmented reduction?'."""
+    g = _golden("segmented_reduction_worked_example.json")
+    off = np.array(g["offsets"], dtype=np.int64)
+    for kind in ("u32", "i32", "f32"):
+        vals = np.array(g["values"], dtype=NP_T[kind])
+        for op in ("sum", "min", "max"):
+            r = oracle.reduce(vals, off, op, lib=lib)
+            assert _col(r.out) == g[op], (kind, op, _col(r.out))
+            if op != "sum":
+                assert _col(r.arg) == g["derived"]["arg" + op], (kind, op, _col(r.arg))
+
+
+def pin_empty_segments(lib):
+    """Repeated offsets are empty segments; empty -> 0 (arg -1)."""
+    g = _golden("empty_segments.json")
+    off = np.array(g["offsets"], dtype=np.int64)
+    for kind in ("u32", "i32", "f32"):
+        vals = np.array(g["values"], dtype=NP_T[kind])
+        for op in ("sum", "min", "max"):
+            r = oracle.reduce(vals, off, op, lib=lib)
+            assert _col(r.out) == g[op], (kind, op)
+            if op != "sum":
+                assert _col(r.arg) == g["arg" + op], (kind, op)
+        if kind == "f32":
+            r = oracle.reduce(vals, off, "mean", lib=lib)
+            assert _col(r.out) == [0.0, 6.0, 0.0, 1.0, 0.0]
+            # zero means all-zero bits (+0.0), not -0.0
+            assert not np.signbit(r.out).any()
+
+
+def pin_rle_examples(lib):
+    """luma.gl GPURunLengthEncode, 'What is run-length encoding?' and 'Contract'."""
+    g = _golden("run_length_encode_examples.json")
+    for case in g["cases"]:
+        v, ln, off, c = oracle.rle(np.array(case["input"], dtype=np.uint32), lib=lib)
+        assert v.tolist() == case["values"], case["cite"]
+        assert c == len(case["values"])
+        lengths = case.get("lengths", case.get("derived_lengths"))
+        offsets = case.get("offsets", case.get("derived_offsets"))
+        assert ln.tolist() == lengths, case["cite"]
+        assert off.tolist() == offsets, case["cite"]
+
+
+# ---------------------------------------------------------------- brute force
+
+def _random_case(rng, kind, feat):
+    s = int(rng.integers(0, 9))
+    lengths = rng.integers(0, 7, size=s)
+    lengths[rng.random(s) < 0.25] = 0
+    base = int(rng.integers(0, 4))  # offsets[0] may be above zero
+    offsets = np.concatenate([[base], base + np.cumsum(lengths)]).astype(np.int64)
+    rows = int(offsets[-1]) + int(rng.integers(0, 3))  # rows past the last offset are never read
+    if kind == "f32":
+        # finite, no zeros (so Python's order equals the key order), many ties
+        pool = np.array([-2.5, -1.0, -0.375, 0.125, 0.5, 1.0, 3.0, 1e-3, -7e-4, 6.5e3], dtype=np.float32)
+        vals = pool[rng.integers(0, len(pool), size=(rows, feat))]
+        vals = np.where(rng.random((rows, feat)) < 0.5, vals, rng.uniform(-4, 4, (rows, feat)).astype(np.float32))
+        vals[vals == 0] = 0.25
+    elif kind == "i32":
+        vals = rng.integers(-(2 ** 31), 2 ** 31, size=(rows, feat), dtype=np.int64)
+        vals[rng.random((rows, feat)) < 0.4] = rng.integers(-3, 3)
+        vals = vals.astype(np.int32)
+    else:
+        vals = rng.integers(0, 2 ** 32, size=(rows, feat), dtype=np.uint64)
+        vals[rng.random((rows, feat)) < 0.4] = rng.integers(0, 3)
+        vals = vals.astype(np.uint32)
+    return vals, offsets
+
+
+def pin_brute_random(lib, cases=300, seed=1234):
+    """Oracle == pure-Python brute force on tiny random inputs (F in 1,2,3,5)."""
+    rng = np.random.default_rng(seed)
+    for i in range(cases):
+        kind = ("u32", "i32", "f32")[i % 3]
+        feat = (1, 2, 3, 5)[(i // 3) % 4]
+        vals, off = _random_case(rng, kind, feat)
+        rows = vals.tolist()
+        ops = ("sum", "min", "max") + (("mean",) if kind == "f32" else ())
+        for op in ops:
+            r = oracle.reduce(vals if feat > 1 else vals[:, 0], off, op, lib=lib)
+            b_out, b_arg, b_exact = brute_ref.reduce(rows, off.tolist(), op, kind, feat)
+            s = len(off) - 1
+            if op in ("min", "max"):
+                assert r.out.tolist() == b_out, (i, kind, op)
+                assert r.arg.tolist() == b_arg, (i, kind, op)
+            elif kind == "f32":
+                for si in range(s):
+                    for f in range(feat):
+                        lo, hi = off[si], off[si + 1]
+                        n = int(hi - lo)
+                        ex = b_exact[si][f]
+                        a = math.fsum(abs(float(vals[r, f])) for r in range(lo, hi))
+                        scale = a / n if (op == "mean" and n) else a
+                        assert abs(r.ref[si, f] - ex) <= 1e-13 * scale + 1e-300, (i, op, si, f)
+                        assert abs(r.mag[si, f] - a) <= 1e-13 * a + 1e-300, (i, op, si, f)
+                        # the float32 output is the double result rounded once
+                        assert abs(float(r.out[si, f]) - ex) <= 2.0 ** -23 * abs(ex) + 1e-13 * scale + 1e-300, (i, op, si, f)
+            else:
+                assert r.out.tolist() == b_out, (i, kind, op)
+
+
+# ---------------------------------------------------------------- library special cases
+
+def pin_library_special_cases(lib, seed=7):
+    """S = 1 is a global reduction; nonempty segments match numpy reduceat;
+    F features are F independent columns; float sums match torch.segment_reduce."""
+    rng = np.random.default_rng(seed)
+    x = rng.uniform(-1, 1, 5000).astype(np.float32)
+    xi = rng.integers(-1000, 1001, 5000, dtype=np.int32)
+    off1 = np.array([17, 4321], dtype=np.int64)
+    seg = x[17:4321]
+    r = oracle.reduce(x, off1, "sum", lib=lib)
+    assert abs(r.ref[0, 0] - np.sum(seg, dtype=np.float64)) <= 1e-12 * np.abs(seg).sum()
+    assert abs(r.mag[0, 0] - np.abs(seg).sum(dtype=np.float64)) <= 1e-12 * np.abs(seg).sum()
+    for op, fn, afn in (("min", np.min, np.argmin), ("max", np.max, np.argmax)):
+        for arr in (x, xi):
+            r = oracle.reduce(arr, off1, op, lib=lib)
+            assert r.out[0, 0] == fn(arr[17:4321]) and r.arg[0, 0] == 17 + afn(arr[17:4321]), op
+
+    # many segments, some empty: reduceat on the nonempty ones
+    lengths = rng.integers(0, 40, 300)
+    lengths[rng.random(300) < 0.2] = 0
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    n = int(off[-1])
+    vals = rng.integers(-50, 50, n, dtype=np.int32)
+    ne = lengths > 0
+    starts = off[:-1][ne]
+    for op, ufunc in (("sum", np.add), ("min", np.minimum), ("max", np.maximum)):
+        r = oracle.reduce(vals, off, op, lib=lib)
+        want = ufunc.reduceat(vals.astype(np.int64) if op == "sum" else vals, starts)
+        assert np.array_equal(r.out[ne, 0].astype(np.int64), want.astype(np.int64)), op
+        assert (r.out[~ne, 0] == 0).all(), op
+
+    # F columns are independent 1-D problems
+    feat = 6
+    v2 = rng.standard_normal((n, feat)).astype(np.float32)
+    for op in ("sum", "min", "max", "mean"):
+        r2 = oracle.reduce(v2, off, op, lib=lib)
+        for f in range(feat):
+            r1 = oracle.reduce(np.ascontiguousarray(v2[:, f]), off, op, lib=lib)
+            assert np.array_equal(r2.out[:, f], r1.out[:, 0]), (op, f)
+            if r1.arg is not None:
+                assert np.array_equal(r2.arg[:, f], r1.arg[:, 0]), (op, f)
+
+    # torch.segment_reduce (CPU), the library the graph-reduce README compares against
+    import torch
+    tv = torch.from_numpy(v2.astype(np.float64))
+    tl = torch.from_numpy(lengths.astype(np.int64))
+    r = oracle.reduce(v2, off, "sum", lib=lib)
+    ts = torch.segment_reduce(tv, "sum", lengths=tl, axis=0, unsafe=True).numpy()
+    assert np.allclose(r.ref, ts, rtol=0, atol=1e-12 * max(1.0, np.abs(v2).sum()))
+    tm = torch.segment_reduce(tv, "mean", lengths=tl, axis=0, unsafe=True).numpy()
+    rm = oracle.reduce(v2, off, "mean", lib=lib)
+    tm = np.where(ne[:, None], tm, 0.0)
+    assert np.allclose(rm.ref, tm, rtol=1e-12, atol=1e-12)
+    for op in ("min", "max"):
+        tmx = torch.segment_reduce(torch.from_numpy(v2), op, lengths=tl, axis=0, unsafe=True).numpy()
+        rr = oracle.reduce(v2, off, op, lib=lib)
+        assert np.array_equal(rr.out[ne], tmx[ne]), op
+
+
+def pin_integer_valued_floats(lib, seed=11):
+    """Integer-valued floats with small partial sums add exactly in any order,
+    so the float32 result must equal a float64 numpy sum bit for bit."""
+    rng = np.random.default_rng(seed)
+    lengths = rng.integers(0, 300, 200)
+    off = np.concatenate([[3], 3 + np.cumsum(lengths)]).astype(np.int64)
+    vals = rng.integers(-3, 4, (int(off[-1]) + 5, 3)).astype(np.float32)
+    r = oracle.reduce(vals, off, "sum", lib=lib)
+    for s in range(200):
+        want = vals[off[s]:off[s + 1]].astype(np.float64).sum(axis=0)
+        assert np.array_equal(r.out[s], want.astype(np.float32)), s
+
+
+def pin_wraparound(lib):
+    """Integer sums are taken modulo 2^32 (closed form)."""
+    off = np.array([0, 2, 4, 7], dtype=np.int64)
+    u = np.array([0xFFFFFFFF, 2, 0x80000000, 0x80000000, 1, 2, 3], dtype=np.uint32)
+    assert _col(oracle.reduce(u, off, "sum", lib=lib).out) == [1, 0, 6]
+    i = np.array([2 ** 31 - 1, 1, -(2 ** 31), -1, -5, 2, 3], dtype=np.int32)
+    assert _col(oracle.reduce(i, off, "sum", lib=lib).out) == [-(2 ** 31), 2 ** 31 - 1, 0]
+    # u32 min/max compare unsigned, i32 signed
+    assert _col(oracle.reduce(u, off, "max", lib=lib).out) == [0xFFFFFFFF, 0x80000000, 3]
+    assert _col(oracle.reduce(i, off, "min", lib=lib).out) == [1, -(2 ** 31), -5]
+
+
+def pin_mean(lib, seed=5):
+    """mean = sum / length, empty -> 0 (graph-reduce README, 'API')."""
+    rng = np.random.default_rng(seed)
+    lengths = rng.integers(0, 30, 100)
+    lengths[::7] = 0
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    v = rng.standard_normal((int(off[-1]), 2)).astype(np.float32)
+    r = oracle.reduce(v, off, "mean", lib=lib)
+    for s in range(100):
+        if lengths[s] == 0:
+            assert (r.out[s] == 0).all() and (r.ref[s] == 0).all()
+        else:
+            want = v[off[s]:off[s + 1]].astype(np.float64).mean(axis=0)
+            assert np.allclose(r.ref[s], want, rtol=1e-13, atol=1e-15), s
+
+
+# ---------------------------------------------------------------- order key and invariants
+
+def _fbits(x):
+    return struct.unpack("<I", struct.pack("<f", x))[0]
+
+
+def pin_order_key(lib, seed=3):
+    """The monotone key orders floats as numpy does (finite, distinct, nonzero),
+    int32 as signed integers and uint32 as unsigned; -0.0 sorts just below +0.0
+    and NaNs sit outside +-inf (the reading of the graph-reduce 'Method')."""
+    rng = np.random.default_rng(seed)
+    xs = np.unique(np.concatenate([rng.standard_normal(2000), rng.uniform(-1e30, 1e30, 500),
+                                   [np.inf, -np.inf, 1e-40, -1e-40]]).astype(np.float32))
+    xs = xs[xs != 0]
+    keys = [oracle.order_key(_fbits(float(v)), "f32", lib=lib) for v in xs]
+    assert keys == sorted(keys) and len(set(keys)) == len(keys)
+    kneg0 = oracle.order_key(0x80000000, "f32", lib=lib)
+    kpos0 = oracle.order_key(0x00000000, "f32", lib=lib)
+    kmin = oracle.order_key(_fbits(-1e-40), "f32", lib=lib)
+    kmax = oracle.order_key(_fbits(1e-40), "f32", lib=lib)
+    assert kmin < kneg0 < kpos0 < kmax
+    assert oracle.order_key(0x7FC00000, "f32", lib=lib) > oracle.order_key(_fbits(np.inf), "f32", lib=lib)
+    assert oracle.order_key(0xFFC00000, "f32", lib=lib) < oracle.order_key(_fbits(-np.inf), "f32", lib=lib)
+    ints = np.unique(rng.integers(-(2 ** 31), 2 ** 31, 3000))
+    ik = [oracle.order_key(int(v) & 0xFFFFFFFF, "i32", lib=lib) for v in ints]
+    assert ik == sorted(ik)
+    us = np.unique(rng.integers(0, 2 ** 32, 3000))
+    assert [oracle.order_key(int(v), "u32", lib=lib) for v in us] == [int(v) for v in us]
+
+
+def pin_minmax_invariants(lib, seed=9):
+    """On tie-heavy data, every arg is gathered back, lies in its segment, has no
+    better row in the segment and no earlier row with an equal value
+    (graph-reduce README, 'Correctness')."""
+    rng = np.random.default_rng(seed)
+    lengths = rng.integers(0, 50, 400)
+    off = np.concatenate([[5], 5 + np.cumsum(lengths)]).astype(np.int64)
+    n = int(off[-1]) + 5
+    for kind, vals in (("i32", rng.integers(-3, 3, (n, 2)).astype(np.int32)),
+                       ("u32", rng.integers(0, 4, (n, 2)).astype(np.uint32)),
+                       ("f32", rng.integers(-2, 3, (n, 2)).astype(np.float32) * np.float32(0.5) + np.float32(0.25))):
+        for op in ("min", "max"):
+            r = oracle.reduce(vals, off, op, lib=lib)
+            for s in range(400):
+                lo, hi = int(off[s]), int(off[s + 1])
+                for f in range(2):
+                    a = int(r.arg[s, f])
+                    if lo == hi:
+                        assert a == -1 and r.out[s, f] == 0
+                        continue
+                    assert lo <= a < hi, (kind, op, s)
+                    col = vals[lo:hi, f]
+                    assert r.out[s, f] == vals[a, f]
+                    best = col.min() if op == "min" else col.max()
+                    assert vals[a, f] == best, (kind, op, s)
+                    assert not (col[: a - lo] == best).any(), (kind, op, s)
+
+
+def pin_rle_groupby(lib, seed=13):
+    """RLE equals itertools.groupby (adjacent runs) on random keys, and the
+    offsets are the running sum of the lengths."""
+    rng = np.random.default_rng(seed)
+    for trial in range(40):
+        n = int(rng.integers(0, 400))
+        keys = np.repeat(rng.integers(0, 5, n), rng.integers(1, 6, n))[:n].astype(np.uint32)
+        if trial % 4 == 0:
+            keys = rng.integers(0, 2 ** 32, n, dtype=np.uint64).astype(np.uint32)
+        v, ln, off, c = oracle.rle(keys, lib=lib)
+        groups = [(k, len(list(g))) for k, g in itertools.groupby(keys.tolist())]
+        assert v.tolist() == [k for k, _ in groups]
+        assert ln.tolist() == [m for _, m in groups]
+        assert off.tolist() == list(itertools.accumulate([0] + [m for _, m in groups]))
+        bv, bl, bo = brute_ref.rle(keys.tolist())
+        assert (v.tolist(), ln.tolist(), off.tolist()) == (bv, bl, bo)
+
+
+ALL_PINS = [
+    pin_worked_example,
+    pin_empty_segments,
+    pin_rle_examples,
+    pin_brute_random,
+    pin_library_special_cases,
+    pin_integer_valued_floats,
+    pin_wraparound,
+    pin_mean,
+    pin_order_key,
+    pin_minmax_invariants,
+    pin_rle_groupby,
+]

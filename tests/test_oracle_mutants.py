@@ -1,0 +1,60 @@
+"""Planted mistakes in the oracle must each fail at least one pin.
+
+Each mutant is a copy of oracle/oracle.c with one textual change (a dropped
+term, a wrong sign, a wrong tie rule, a transposed index, ...), compiled with
+gcc into a temporary library on the CPU.  The pins of tests/pins.py are run
+against it; a mutant that passes every pin would show a hole in the pins.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, text to replace, replacement) -- each replacement keeps memory accesses in bounds.
+MUTANTS = [
+    ("drop_first_row_of_sum", "for (int64_t r = lo; r < hi; ++r) {\n                        const double x",
+     "for (int64_t r = lo + 1; r < hi; ++r) {\n                        const double x"),
+    ("drop_first_row_of_int_sum", "for (int64_t r = lo; r < hi; ++r)\n                        sum += load_bits",
+     "for (int64_t r = lo + 1; r < hi; ++r)\n                        sum += load_bits"),
+    ("float_sum_wrong_sign", "sum += x;", "sum -= x;"),
+    ("magnitude_not_absolute", "mag += x < 0 ? -x : x;", "mag += x;"),
+    ("mean_wrong_length", "sum / (double)(hi - lo)", "sum / (double)(hi - lo + 1)"),
+    ("ties_to_higher_row_min", "(k < best_key)", "(k <= best_key)"),
+    ("ties_to_higher_row_max", "(k > best_key)", "(k >= best_key)"),
+    ("min_max_swapped", "(op == ORC_MIN) ? (k < best_key) : (k > best_key)",
+     "(op == ORC_MIN) ? (k > best_key) : (k < best_key)"),
+    ("float_key_negatives_unflipped", "        return ~bits;", "        return bits;"),
+    ("int_key_unsigned", "return bits ^ 0x80000000u;\n    if (bits", "return bits;\n    if (bits"),
+    ("empty_value_nonzero", "store_bits(out, o, 0u);", "store_bits(out, o, 1u);"),
+    ("empty_arg_not_minus_one", "arg_out[o] = -1;", "arg_out[o] = lo;"),
+    ("output_transposed", "const int64_t o = s * feat + f;", "const int64_t o = f * num_segments + s;"),
+    ("feature_stride_dropped", "load_bits(values, r * feat + f));\n                        sum",
+     "load_bits(values, r + f));\n                        sum"),
+    ("arg_relative_to_segment", "arg_out[o] = best_row;", "arg_out[o] = best_row - lo;"),
+    ("rle_only_increasing_boundaries", "keys[i] != keys[i - 1]", "keys[i] > keys[i - 1]"),
+    ("rle_last_offset_short", "offsets[c] = n;", "offsets[c] = n - (n > 0);"),
+    ("rle_length_off_by_one", "(uint32_t)(offsets[r + 1] - offsets[r])", "(uint32_t)(offsets[r + 1] - offsets[r] - 1)"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutant {name}: anchor text not found exactly once"
+    mutant_src = tmp_path / "oracle_mutant.c"
+    mutant_src.write_text(src.replace(old, new))
+    lib_path = str(tmp_path / "liboracle_mutant.so")
+    subprocess.run(["gcc", "-O1", "-std=c99", "-fPIC", "-shared", str(mutant_src), "-o", lib_path], check=True)
+    lib = oracle.load(lib_path)
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(lib)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"planted mistake '{name}' passed every pin"
