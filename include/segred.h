@@ -1,0 +1,150 @@
+/*
+ * segred.h -- C ABI of the segmented-reduction library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Every pointer argument is a DEVICE pointer unless stated otherwise.  Every
+ * call is asynchronous and ordered on the HIP stream it is given (0 is the
+ * null stream): a non-error return means the work was enqueued; faults during
+ * the work surface at the caller's next synchronisation.  Inputs and outputs
+ * are owned by the caller; scratch memory is owned by the library, taken from
+ * a stream-ordered pool and returned on the same stream.  No call throws.
+ * Calls on distinct streams may run concurrently.
+ */
+#ifndef SEGRED_H
+#define SEGRED_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of `values` (4-byte packed scalars). */
+enum segred_dtype { SEGRED_U32 = 0, SEGRED_I32 = 1, SEGRED_F32 = 2 };
+
+/* Reductions.  MEAN is float32 only. */
+enum segred_op { SEGRED_SUM = 0, SEGRED_MIN = 1, SEGRED_MAX = 2, SEGRED_MEAN = 3 };
+
+/* Return codes. */
+enum segred_status {
+    SEGRED_OK = 0,
+    SEGRED_ERR_INVALID_ARGUMENT = 1, /* rejected on the host before any device work */
+    SEGRED_ERR_UNSUPPORTED = 2,      /* a valid request this library does not do (integer MEAN) */
+    SEGRED_ERR_OUT_OF_MEMORY = 3,    /* scratch could not be obtained */
+    SEGRED_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
+};
+
+/*
+ * segred_reduce -- segmented reduction over offset-delimited segments.
+ *
+ * Defined by the luma.gl "GPUSegmentedReduction" page (sections "What is an
+ * offset-delimited segment?", "What is segmented reduction?", "Contract") and
+ * the graph-reduce README ("API": mean and the producing row of min/max;
+ * "Method": ties go to the lower row; "Correctness": the row is an index into
+ * the source, an empty min/max has row -1).
+ *
+ *   values        [rows, feat] row-major, 4-byte elements of type `dtype`.
+ *                 Rows are absolute: segment s covers rows
+ *                 offsets[s] .. offsets[s+1]-1.  Only rows inside
+ *                 [offsets[0], offsets[num_segments]) are read.
+ *   dtype         SEGRED_U32, SEGRED_I32 or SEGRED_F32.
+ *   feat          features per row, >= 1 (each reduced independently).
+ *   offsets       int64 [num_segments + 1], nondecreasing.  offsets[0] may be
+ *                 above 0.  A repeated offset is an empty segment.
+ *   num_segments  S >= 0.  S = 0 enqueues nothing and returns SEGRED_OK.
+ *   op            SEGRED_SUM, SEGRED_MIN, SEGRED_MAX or SEGRED_MEAN.
+ *   out           [S, feat] of the input type (float32 for MEAN).
+ *                 SUM of u32/i32 wraps modulo 2^32.  SUM and MEAN of f32 are
+ *                 accumulated in float64 in a fixed order and rounded to
+ *                 float32 once, so results are bitwise identical run to run
+ *                 on a given device.  MIN/MAX order u32 unsigned, i32 signed,
+ *                 f32 by the monotone bit key (so -0.0 < +0.0 and NaNs sort
+ *                 past +-inf by their bits); `out` holds the element's bits.
+ *                 An empty segment writes 0 (+0.0 for floats).
+ *   arg_out       int64 [S, feat] or NULL.  MIN/MAX only (ignored otherwise):
+ *                 the absolute row of the extremum, the lowest such row on
+ *                 ties, -1 for an empty segment.
+ *   stream        HIP stream the work is ordered on.
+ *
+ * Errors: SEGRED_ERR_INVALID_ARGUMENT for S < 0, feat < 1, an unknown dtype
+ * or op, a NULL values/offsets/out with S > 0, values/out not 4-byte aligned,
+ * offsets/arg_out not 8-byte aligned.  SEGRED_ERR_UNSUPPORTED for MEAN of an
+ * integer type.  SEGRED_ERR_OUT_OF_MEMORY if scratch is unavailable.
+ * SEGRED_ERR_HIP if a launch fails.  The offsets are NOT read back or checked:
+ * offsets that decrease or point outside `values` are undefined behaviour, as
+ * is `out`/`arg_out` overlapping the inputs.  The device never needs the row
+ * count: N = offsets[S] - offsets[0] stays on the device.
+ */
+int segred_reduce(const void *values, int32_t dtype, int64_t feat,
+                  const int64_t *offsets, int64_t num_segments, int32_t op,
+                  void *out, int64_t *arg_out, hipStream_t stream);
+
+/*
+ * segred_offsets_from_rle -- run-length encoding of uint32 keys and the
+ * offsets of the runs, the producer that feeds segred_reduce.
+ *
+ * Defined by the luma.gl "GPURunLengthEncode and GPUUnique" page (sections
+ * "What is run-length encoding?", "Why RLE matters for GPU grouping",
+ * "Contract"): adjacent equal keys form a run; runs keep first-occurrence
+ * order; keys are compared bit for bit and need not be sorted (sorting first
+ * makes equal keys adjacent); run lengths [3,2,4] correspond to offsets
+ * [0,3,5,9]; an empty input gives count 0.
+ *
+ *   sorted_keys  uint32 [n].
+ *   n            0 <= n <= UINT32_MAX.
+ *   values       uint32, capacity n: values[r] = key of run r.
+ *   lengths      uint32, capacity n: lengths[r] = length of run r.
+ *   offsets      int64, capacity n + 1: offsets[r] = first position of run r,
+ *                offsets[count] = n.
+ *   count        one int64 on the device: the number of runs.
+ *   stream       HIP stream the work is ordered on.
+ *
+ * Only values[0..count), lengths[0..count) and offsets[0..count] are written;
+ * the rest of each buffer is left untouched.  To reduce over the runs, read
+ * `count` back (8 bytes) and pass it as num_segments with `offsets`.
+ * Errors: SEGRED_ERR_INVALID_ARGUMENT for n < 0, n > UINT32_MAX, a NULL
+ * output (or NULL keys with n > 0), misalignment (4 bytes for keys, values,
+ * lengths; 8 bytes for offsets and count).  SEGRED_ERR_OUT_OF_MEMORY,
+ * SEGRED_ERR_HIP as for segred_reduce.
+ */
+int segred_offsets_from_rle(const uint32_t *sorted_keys, int64_t n,
+                            uint32_t *values, uint32_t *lengths,
+                            int64_t *offsets, int64_t *count, hipStream_t stream);
+
+/* Static, host-side description of a status code (never NULL). */
+const char *segred_status_string(int status);
+
+/*
+ * Work partition of segred_reduce (a tuning and testing knob, not part of the
+ * method).  The rows and segment ends of a call are split into `shares`
+ * equal parts of the merged (rows + segment ends) sequence, one per wave of
+ * the streaming kernel; segments cut by a part boundary are finished by a
+ * second, fixed-order combine kernel.  0 restores the default.  The float
+ * summation order, and so the last bits of float sums, depend on this value;
+ * integer, min/max and arg results do not.  Applies to calls made after it
+ * returns; process-wide.  The count is rounded up to a multiple of 4 (whole
+ * workgroups).  Returns SEGRED_ERR_INVALID_ARGUMENT unless shares == 0 or
+ * 1 <= shares <= 2^22.
+ */
+int segred_set_shares(int64_t shares);
+
+/* The share count (after rounding) segred_reduce uses for this dtype/op/feat. */
+int64_t segred_get_shares(int32_t dtype, int32_t op, int64_t feat);
+
+/*
+ * Kernel timing (instrumentation for benchmarks).  While enabled, every
+ * segred_reduce call records a pair of HIP events on its stream around its
+ * streaming (first) kernel.  segred_timing_read waits for the recorded
+ * events, returns the summed duration in milliseconds and the number of
+ * timed launches, and clears the record.  Up to 4096 launches are kept;
+ * later ones are not timed.  Host-side state, process-wide, not thread-safe.
+ */
+int segred_timing_enable(int enable);
+int segred_timing_read(double *total_ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEGRED_H */

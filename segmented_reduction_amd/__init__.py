@@ -1,0 +1,180 @@
+"""Segmented reduction over offset-delimited segments on AMD MI355X (gfx950).
+
+A thin ctypes binding over the C ABI in ``include/segred.h`` (libsegred.so,
+built from ``csrc/`` with hipcc).  Every step of the computation runs in the
+library's HIP kernels; this module only checks tensors, allocates outputs
+with PyTorch and passes device pointers and PyTorch's current HIP stream.
+There is no CPU fallback: if the library is missing, calls raise.
+
+    out, arg = reduce(values, offsets, "max")        # values [N] or [N, F] on the GPU
+    values, lengths, offsets, count = offsets_from_rle(sorted_keys)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libsegred.so")
+
+SUM, MIN, MAX, MEAN = 0, 1, 2, 3
+OPS = {"sum": SUM, "min": MIN, "max": MAX, "mean": MEAN}
+DTYPES = {torch.uint32: 0, torch.int32: 1, torch.float32: 2}
+STATUS = {0: "SEGRED_OK", 1: "SEGRED_ERR_INVALID_ARGUMENT", 2: "SEGRED_ERR_UNSUPPORTED",
+          3: "SEGRED_ERR_OUT_OF_MEMORY", 4: "SEGRED_ERR_HIP"}
+
+
+class SegredError(RuntimeError):
+    """A non-zero status returned by the C ABI."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def library(path: str | None = None):
+    """Load libsegred.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            p = path or LIB_PATH
+            if not os.path.exists(p):
+                raise RuntimeError(f"libsegred.so not found at {p}; build it with "
+                                   "`python -m segmented_reduction_amd.build_lib`")
+            lib = ctypes.CDLL(p)
+            vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+            lib.segred_reduce.argtypes = [vp, i32, i64, vp, i64, i32, vp, vp, vp]
+            lib.segred_reduce.restype = ctypes.c_int
+            lib.segred_offsets_from_rle.argtypes = [vp, i64, vp, vp, vp, vp, vp]
+            lib.segred_offsets_from_rle.restype = ctypes.c_int
+            lib.segred_status_string.argtypes = [ctypes.c_int]
+            lib.segred_status_string.restype = ctypes.c_char_p
+            lib.segred_set_shares.argtypes = [i64]
+            lib.segred_set_shares.restype = ctypes.c_int
+            lib.segred_get_shares.argtypes = [i32, i32, i64]
+            lib.segred_get_shares.restype = i64
+            lib.segred_timing_enable.argtypes = [ctypes.c_int]
+            lib.segred_timing_enable.restype = ctypes.c_int
+            lib.segred_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+            lib.segred_timing_read.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return library().segred_status_string(int(status)).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise SegredError(rc, what)
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def reduce(values: torch.Tensor, offsets: torch.Tensor, op: str, *, want_arg: bool = True,
+           out: torch.Tensor | None = None, arg: torch.Tensor | None = None):
+    """Segmented ``op`` ("sum", "min", "max", "mean") of ``values`` over ``offsets``.
+
+    values  [N] or [N, ...] uint32 / int32 / float32 on a GPU, contiguous;
+            trailing dimensions are flattened into F features per row.
+    offsets int64 [S + 1] on the same GPU; segment s is rows offsets[s]..offsets[s+1]-1.
+    Returns (out [S, ...], arg [S, ...] int64 or None).  arg is the row of
+    the extremum for min/max (lowest on ties, -1 for empty segments).
+    """
+    if op not in OPS:
+        raise ValueError(f"op must be one of {sorted(OPS)}")
+    if not (values.is_cuda and offsets.is_cuda):
+        raise ValueError("values and offsets must be GPU tensors")
+    if values.dtype not in DTYPES:
+        raise TypeError(f"values dtype {values.dtype} is not uint32, int32 or float32")
+    if offsets.dtype != torch.int64 or offsets.dim() != 1 or offsets.numel() < 1:
+        raise ValueError("offsets must be a 1-D int64 tensor with S + 1 entries")
+    if values.device != offsets.device:
+        raise ValueError("values and offsets must be on the same device")
+    if not values.is_contiguous() or not offsets.is_contiguous():
+        raise ValueError("values and offsets must be contiguous")
+    if values.dim() == 0:
+        raise ValueError("values needs at least one dimension")
+    s = offsets.numel() - 1
+    feat_shape = tuple(values.shape[1:])
+    feat = 1
+    for d in feat_shape:
+        feat *= d
+    if feat < 1:
+        raise ValueError("values has an empty feature dimension")
+    odt = torch.float32 if op == "mean" else values.dtype
+    if out is None:
+        out = torch.empty((s,) + feat_shape, dtype=odt, device=values.device)
+    want = op in ("min", "max") and want_arg
+    if want and arg is None:
+        arg = torch.empty((s,) + feat_shape, dtype=torch.int64, device=values.device)
+    if not want:
+        arg = None
+    with torch.cuda.device(values.device):
+        rc = library().segred_reduce(values.data_ptr(), DTYPES[values.dtype], feat, offsets.data_ptr(), s,
+                                     OPS[op], out.data_ptr(), arg.data_ptr() if arg is not None else None,
+                                     _stream(values.device))
+    _check(rc, "segred_reduce")
+    return out, arg
+
+
+def offsets_from_rle(keys: torch.Tensor):
+    """Run-length encode uint32 ``keys`` (adjacent runs) on the GPU.
+
+    Returns (values [n], lengths [n], offsets [n + 1], count [1] int64), all on
+    the GPU and written asynchronously; only values[:count], lengths[:count]
+    and offsets[:count + 1] are meaningful.
+    """
+    if not keys.is_cuda or keys.dtype != torch.uint32 or keys.dim() != 1 or not keys.is_contiguous():
+        raise ValueError("keys must be a contiguous 1-D uint32 GPU tensor")
+    n = keys.numel()
+    dev = keys.device
+    values = torch.empty(max(n, 1), dtype=torch.uint32, device=dev)
+    lengths = torch.empty(max(n, 1), dtype=torch.uint32, device=dev)
+    offsets = torch.empty(n + 1, dtype=torch.int64, device=dev)
+    count = torch.empty(1, dtype=torch.int64, device=dev)
+    with torch.cuda.device(dev):
+        rc = library().segred_offsets_from_rle(keys.data_ptr() if n else None, n, values.data_ptr(),
+                                               lengths.data_ptr(), offsets.data_ptr(), count.data_ptr(),
+                                               _stream(dev))
+    _check(rc, "segred_offsets_from_rle")
+    return values, lengths, offsets, count
+
+
+def rle(keys: torch.Tensor):
+    """``offsets_from_rle`` followed by the one 8-byte readback of the count:
+    returns (values[:count], lengths[:count], offsets[:count + 1], count)."""
+    values, lengths, offsets, count = offsets_from_rle(keys)
+    c = int(count.item())
+    return values[:c], lengths[:c], offsets[: c + 1], c
+
+
+def set_shares(shares: int):
+    """Override the work partition (0 = default); see segred_set_shares."""
+    _check(library().segred_set_shares(int(shares)), "segred_set_shares")
+
+
+def get_shares(dtype=torch.float32, op: str = "sum", feat: int = 1) -> int:
+    return int(library().segred_get_shares(DTYPES[dtype], OPS[op], int(feat)))
+
+
+def timing_enable(enable: bool = True):
+    _check(library().segred_timing_enable(1 if enable else 0), "segred_timing_enable")
+
+
+def timing_read():
+    """(total milliseconds, launches) of the streaming kernel since the last read."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int64(0)
+    _check(library().segred_timing_read(ctypes.byref(ms), ctypes.byref(n)), "segred_timing_read")
+    return ms.value, n.value

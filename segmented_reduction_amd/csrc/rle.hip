@@ -1,0 +1,236 @@
+// rle.hip -- run-length encoding of uint32 keys and the offsets of the runs
+// (luma.gl "GPURunLengthEncode and GPUUnique": "What is run-length
+// encoding?", "Why RLE matters for GPU grouping", "Contract").
+//
+// Position i starts a run iff i == 0 or keys[i] != keys[i-1].  Runs are
+// numbered in position order; run r gets values[r] = keys[start],
+// offsets[r] = start, lengths[r] = next start - start, offsets[count] = n.
+//
+// Three launches, no atomics: (1) each tile of 4096 keys counts its run
+// starts and notes its first one; (2) one workgroup scans the tile counts
+// (run index of each tile's first start) and the first starts from the right
+// (the start that follows each tile); (3) each tile ranks its starts in
+// position order through LDS and writes values, offsets and lengths with
+// consecutive lanes on consecutive runs.
+#include "internal.hpp"
+#include "wave.hpp"
+
+namespace segred {
+
+constexpr int kRleThreads = 256;
+constexpr int kRleKeysPerThread = 16;
+constexpr int kRleTile = kRleThreads * kRleKeysPerThread;
+constexpr int kScanThreads = 1024;
+
+// Keys of one tile: thread (wave w, lane l) holds positions
+// tile_start + u * 256 + w * 64 + l, u = 0..15, and whether each starts a run.
+struct TileKeys {
+    uint32_t k[kRleKeysPerThread];
+    bool head[kRleKeysPerThread];
+};
+
+__device__ __forceinline__ void load_tile(const uint32_t *keys, int64_t n, int64_t start, int tid, TileKeys &t) {
+    const int lane = tid & 63;
+#pragma unroll
+    for (int u = 0; u < kRleKeysPerThread; ++u) {
+        const int64_t i = start + u * kRleThreads + tid;
+        t.k[u] = i < n ? keys[i] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kRleKeysPerThread; ++u) {
+        const int64_t i = start + u * kRleThreads + tid;
+        uint32_t prev = lane_get(t.k[u], (lane - 1) & 63);
+        if (lane == 0 && i > 0 && i < n) prev = keys[i - 1];
+        t.head[u] = i < n && (i == 0 || t.k[u] != prev);
+    }
+}
+
+__global__ __launch_bounds__(kRleThreads) void rle_count(const uint32_t *keys, int64_t n, int64_t *tile_count,
+                                                         int64_t *tile_first) {
+    __shared__ int64_t s_cnt[4];
+    __shared__ int64_t s_first[4];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int64_t start = (int64_t)blockIdx.x * kRleTile;
+    TileKeys t;
+    load_tile(keys, n, start, tid, t);
+    int64_t cnt = 0, first = INT64_MAX;
+#pragma unroll
+    for (int u = 0; u < kRleKeysPerThread; ++u) {
+        const uint64_t m = ballot(t.head[u]);
+        cnt += popc64(m);
+        if (m && first == INT64_MAX) first = start + u * kRleThreads + wid * 64 + (int)__builtin_ctzll(m);
+    }
+    if (lane == 0) {
+        s_cnt[wid] = cnt;
+        s_first[wid] = first;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int64_t c = 0, f = INT64_MAX;
+        for (int w = 0; w < 4; ++w) {
+            c += s_cnt[w];
+            f = s_first[w] < f ? s_first[w] : f;
+        }
+        tile_count[blockIdx.x] = c;
+        tile_first[blockIdx.x] = f;
+    }
+}
+
+// Inclusive scan over the 1024 threads of a workgroup; `op` is + or min.
+template <bool MIN>
+__device__ __forceinline__ int64_t block_inclusive_scan(int64_t v, int64_t *s_tmp, int64_t &total) {
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    constexpr int kWaves = kScanThreads / 64;
+    int64_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int64_t y = lane_get(x, (lane - o) & 63);
+        if (lane >= o) x = MIN ? (y < x ? y : x) : x + y;
+    }
+    if (lane == 63) s_tmp[wid] = x;
+    __syncthreads();
+    if (wid == 0) {
+        int64_t w = lane < kWaves ? s_tmp[lane] : (MIN ? INT64_MAX : 0);
+#pragma unroll
+        for (int o = 1; o < kWaves; o <<= 1) {
+            const int64_t y = lane_get(w, (lane - o) & 63);
+            if (lane >= o) w = MIN ? (y < w ? y : w) : w + y;
+        }
+        if (lane < kWaves) s_tmp[kWaves + lane] = w;
+    }
+    __syncthreads();
+    if (wid > 0) {
+        const int64_t p = s_tmp[kWaves + wid - 1];
+        x = MIN ? (p < x ? p : x) : p + x;
+    }
+    total = s_tmp[2 * kWaves - 1];
+    __syncthreads();
+    return x;
+}
+
+// One workgroup: run index of each tile's first start (exclusive scan of the
+// counts), the start following each tile (scan of first starts from the
+// right), the run count and offsets[count] = n.
+__global__ __launch_bounds__(kScanThreads) void rle_scan(int64_t tiles, int64_t n, const int64_t *tile_count,
+                                                         const int64_t *tile_first, int64_t *tile_base,
+                                                         int64_t *tile_next, int64_t *count, int64_t *offsets) {
+    __shared__ int64_t s_tmp[2 * (kScanThreads / 64)];
+    __shared__ int64_t s_incl[kScanThreads];
+    const int tid = threadIdx.x;
+    int64_t running = 0;
+    for (int64_t b = 0; b < tiles; b += kScanThreads) {
+        const int64_t t = b + tid;
+        const int64_t v = t < tiles ? tile_count[t] : 0;
+        int64_t total;
+        const int64_t incl = block_inclusive_scan<false>(v, s_tmp, total);
+        if (t < tiles) tile_base[t] = running + incl - v;
+        running += total;
+    }
+    // Right to left: thread order runs from the last tile down, so the
+    // inclusive min over threads 0..tid is the min over tiles t..(end of this
+    // block of tiles); the exclusive form, joined with the tiles further
+    // right, is the first run start after tile t.
+    int64_t right = n;
+    for (int64_t b = 0; b < tiles; b += kScanThreads) {
+        const int64_t t = tiles - 1 - (b + tid);
+        const int64_t v = t >= 0 ? tile_first[t] : INT64_MAX;
+        int64_t total;
+        const int64_t incl = block_inclusive_scan<true>(v, s_tmp, total);
+        s_incl[tid] = incl;
+        __syncthreads();
+        if (t >= 0) {
+            int64_t ex = tid > 0 ? s_incl[tid - 1] : INT64_MAX;
+            ex = ex < right ? ex : right;
+            tile_next[t] = ex < n ? ex : n;
+        }
+        __syncthreads();
+        right = total < right ? total : right;
+    }
+    if (tid == 0) {
+        *count = running;
+        offsets[running] = n;
+    }
+}
+
+__global__ __launch_bounds__(kRleThreads) void rle_materialize(const uint32_t *keys, int64_t n,
+                                                               const int64_t *tile_base, const int64_t *tile_next,
+                                                               uint32_t *values, uint32_t *lengths,
+                                                               int64_t *offsets) {
+    __shared__ uint32_t s_pos[kRleTile];
+    __shared__ uint32_t s_key[kRleTile];
+    __shared__ int s_wc[kRleKeysPerThread][4];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int64_t start = (int64_t)blockIdx.x * kRleTile;
+    TileKeys t;
+    load_tile(keys, n, start, tid, t);
+    uint64_t m[kRleKeysPerThread];
+#pragma unroll
+    for (int u = 0; u < kRleKeysPerThread; ++u) {
+        m[u] = ballot(t.head[u]);
+        if (lane == 0) s_wc[u][wid] = popc64(m[u]);
+    }
+    __syncthreads();
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int base = 0;
+#pragma unroll
+    for (int u = 0; u < kRleKeysPerThread; ++u) {
+        int before = 0, all = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            before += w < wid ? s_wc[u][w] : 0;
+            all += s_wc[u][w];
+        }
+        if (t.head[u]) {
+            const int rank = base + before + popc64(m[u] & below);
+            s_pos[rank] = (uint32_t)(u * kRleThreads + tid);
+            s_key[rank] = t.k[u];
+        }
+        base += all;
+    }
+    __syncthreads();
+    const int cnt = base;
+    const int64_t rb = tile_base[blockIdx.x];
+    const int64_t next = tile_next[blockIdx.x];
+    for (int q = tid; q < cnt; q += kRleThreads) {
+        const int64_t pos = start + s_pos[q];
+        const int64_t npos = q + 1 < cnt ? start + s_pos[q + 1] : next;
+        values[rb + q] = s_key[q];
+        offsets[rb + q] = pos;
+        lengths[rb + q] = (uint32_t)(npos - pos);
+    }
+}
+
+}  // namespace segred
+
+using namespace segred;
+
+extern "C" int segred_offsets_from_rle(const uint32_t *sorted_keys, int64_t n, uint32_t *values,
+                                       uint32_t *lengths, int64_t *offsets, int64_t *count,
+                                       hipStream_t stream) {
+    if (n < 0 || n > (int64_t)UINT32_MAX) return SEGRED_ERR_INVALID_ARGUMENT;
+    if (!values || !lengths || !offsets || !count || (n > 0 && !sorted_keys)) return SEGRED_ERR_INVALID_ARGUMENT;
+    if ((sorted_keys && !aligned(sorted_keys, 4)) || !aligned(values, 4) || !aligned(lengths, 4) ||
+        !aligned(offsets, 8) || !aligned(count, 8))
+        return SEGRED_ERR_INVALID_ARGUMENT;
+
+    const int64_t tiles = (n + kRleTile - 1) / kRleTile;
+    void *scratch = nullptr;
+    int rc = scratch_alloc(&scratch, (size_t)tiles * 4 * sizeof(int64_t), stream);
+    if (rc != SEGRED_OK) return rc;
+    int64_t *tcount = static_cast<int64_t *>(scratch);
+    int64_t *tfirst = tcount + tiles;
+    int64_t *tbase = tfirst + tiles;
+    int64_t *tnext = tbase + tiles;
+
+    if (tiles > 0)
+        hipLaunchKernelGGL(rle_count, dim3((unsigned)tiles), dim3(kRleThreads), 0, stream, sorted_keys, n, tcount,
+                           tfirst);
+    hipLaunchKernelGGL(rle_scan, dim3(1), dim3(kScanThreads), 0, stream, tiles, n, tcount, tfirst, tbase, tnext,
+                       count, offsets);
+    if (tiles > 0)
+        hipLaunchKernelGGL(rle_materialize, dim3((unsigned)tiles), dim3(kRleThreads), 0, stream, sorted_keys, n,
+                           tbase, tnext, values, lengths, offsets);
+    rc = hipGetLastError() == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
+    scratch_free(scratch, stream);
+    return rc;
+}

@@ -1,0 +1,56 @@
+// wave.hpp -- wave64 helpers for gfx950 (CDNA4): lane queries, ballots and
+// cross-lane moves for 32- and 64-bit values.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace segred {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() {
+    return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
+
+// Value of lane `src` (any lane may ask for any lane).
+__device__ __forceinline__ uint32_t lane_get(uint32_t v, int src) {
+    return (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)v);
+}
+__device__ __forceinline__ uint64_t lane_get(uint64_t v, int src) {
+    uint32_t lo = lane_get((uint32_t)v, src), hi = lane_get((uint32_t)(v >> 32), src);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ int64_t lane_get(int64_t v, int src) {
+    return (int64_t)lane_get((uint64_t)v, src);
+}
+__device__ __forceinline__ double lane_get(double v, int src) {
+    return __longlong_as_double((long long)lane_get((uint64_t)__double_as_longlong(v), src));
+}
+__device__ __forceinline__ bool lane_get(bool v, int src) {
+    return lane_get((uint32_t)v, src) != 0u;
+}
+
+// Make LDS writes of this wave visible to the other lanes of the same wave.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <typename T>
+__device__ __forceinline__ T uniform(T v) {
+    return v;  // values that are wave-uniform by construction
+}
+
+__device__ __forceinline__ int64_t readfirst(int64_t v) {
+    uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+}  // namespace segred

@@ -1,0 +1,140 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, and rejects bad arguments on the host before any device work."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "segred.h")
+CSRC = os.path.join(ROOT, "segmented_reduction_amd", "csrc")
+
+
+def _lib():
+    import segmented_reduction_amd as sr
+    if not os.path.exists(sr.LIB_PATH):
+        from segmented_reduction_amd import build_lib
+        build_lib.build()
+    return sr.library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(segred_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for required in ("segred_reduce", "segred_offsets_from_rle", "segred_status_string"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    import segmented_reduction_amd as sr
+    out = subprocess.run(["nm", "-D", "--defined-only", sr.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(re.findall(r"\bT (segred_\w+)", out.stdout))
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = _lib()
+    for code in range(5):
+        assert lib.segred_status_string(code)
+    assert lib.segred_status_string(99) == b"unknown status"
+
+
+FAKE = 0x10000  # a non-null, aligned host value; never dereferenced (rejected or S == 0)
+
+
+@pytest.mark.parametrize("args,expect", [
+    # (values, dtype, feat, offsets, S, op, out, arg) -> status
+    ((FAKE, 2, 1, FAKE, -1, 0, FAKE, None), 1),        # S < 0
+    ((FAKE, 2, 0, FAKE, 4, 0, FAKE, None), 1),         # feat < 1
+    ((FAKE, 3, 1, FAKE, 4, 0, FAKE, None), 1),         # dtype out of range
+    ((FAKE, -1, 1, FAKE, 4, 0, FAKE, None), 1),
+    ((FAKE, 2, 1, FAKE, 4, 4, FAKE, None), 1),         # op out of range
+    ((FAKE, 0, 1, FAKE, 4, 3, FAKE, None), 2),         # MEAN of u32
+    ((FAKE, 1, 1, FAKE, 4, 3, FAKE, None), 2),         # MEAN of i32
+    ((None, 2, 1, FAKE, 4, 0, FAKE, None), 1),         # null values
+    ((FAKE, 2, 1, None, 4, 0, FAKE, None), 1),         # null offsets
+    ((FAKE, 2, 1, FAKE, 4, 0, None, None), 1),         # null out
+    ((FAKE + 2, 2, 1, FAKE, 4, 0, FAKE, None), 1),     # values not 4-byte aligned
+    ((FAKE, 2, 1, FAKE + 4, 4, 0, FAKE, None), 1),     # offsets not 8-byte aligned
+    ((FAKE, 2, 1, FAKE, 4, 0, FAKE + 1, None), 1),     # out not 4-byte aligned
+    ((FAKE, 2, 1, FAKE, 4, 1, FAKE, FAKE + 4), 1),     # arg not 8-byte aligned
+    ((None, 2, 1, None, 0, 0, None, None), 0),         # S == 0 enqueues nothing
+    ((FAKE, 2, 7, FAKE, 0, 2, FAKE, None), 0),
+])
+def test_reduce_argument_checks(args, expect):
+    lib = _lib()
+    assert lib.segred_reduce(*args, None) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    # (keys, n, values, lengths, offsets, count) -> status
+    ((FAKE, -1, FAKE, FAKE, FAKE, FAKE), 1),
+    ((FAKE, 2 ** 32, FAKE, FAKE, FAKE, FAKE), 1),      # lengths are uint32
+    ((None, 5, FAKE, FAKE, FAKE, FAKE), 1),
+    ((FAKE, 5, None, FAKE, FAKE, FAKE), 1),
+    ((FAKE, 5, FAKE, None, FAKE, FAKE), 1),
+    ((FAKE, 5, FAKE, FAKE, None, FAKE), 1),
+    ((FAKE, 5, FAKE, FAKE, FAKE, None), 1),
+    ((FAKE + 2, 5, FAKE, FAKE, FAKE, FAKE), 1),
+    ((FAKE, 5, FAKE, FAKE, FAKE + 4, FAKE), 1),
+    ((FAKE, 5, FAKE, FAKE, FAKE, FAKE + 4), 1),
+])
+def test_rle_argument_checks(args, expect):
+    lib = _lib()
+    assert lib.segred_offsets_from_rle(*args, None) == expect
+
+
+def test_share_knob_range():
+    lib = _lib()
+    assert lib.segred_set_shares(-1) == 1
+    assert lib.segred_set_shares(2 ** 22 + 1) == 1
+    assert lib.segred_set_shares(37) == 0
+    assert lib.segred_get_shares(2, 0, 1) == 40  # rounded up to whole workgroups of 4 waves
+    assert lib.segred_set_shares(0) == 0
+    assert lib.segred_get_shares(2, 0, 1) > 0
+
+
+def test_timing_read_without_launches():
+    lib = _lib()
+    ms, n = ctypes.c_double(-1.0), ctypes.c_int64(-1)
+    assert lib.segred_timing_read(ctypes.byref(ms), ctypes.byref(n)) == 0
+    assert n.value == 0 and ms.value == 0.0
+    assert lib.segred_timing_read(None, None) == 1
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import segmented_reduction_amd as sr
+    with pytest.raises(ValueError):
+        sr.reduce(torch.zeros(4), torch.zeros(2, dtype=torch.int64), "sum")
+    with pytest.raises(ValueError):
+        sr.reduce(torch.zeros(4), torch.zeros(2, dtype=torch.int64), "median")
+
+
+def test_kernel_sources_have_no_atomics_or_foreign_backends():
+    """No device atomics (results are combined in a fixed order instead) and no
+    CUDA/Triton/dual-platform code in the library sources."""
+    device_atomic = re.compile(r"\batomic[A-Z]\w*\s*\(|__hip_atomic|__atomic_\w+\s*\(|\bunsafeAtomic")
+    for name in os.listdir(CSRC):
+        code = re.sub(r"//[^\n]*", "", open(os.path.join(CSRC, name)).read())
+        assert not device_atomic.search(code), name
+        for bad in ("cuda", "triton", "__hip_platform"):
+            assert bad not in code.lower(), (name, bad)
+
+
+def test_product_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "segmented_reduction_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), os.path.join(dirpath, f)

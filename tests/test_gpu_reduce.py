@@ -1,0 +1,214 @@
+"""Parity of the HIP segmented reduction with the CPU oracle (GPU only).
+
+Every call goes through the C ABI (libsegred.so) via the binding.  Integer
+sums, min/max values and rows must match bit for bit; float32 sums within
+1e-5 * sum|x| + 1e-6 per (segment, feature) (means: that bound / length).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+NP_T = {"u32": np.uint32, "i32": np.int32, "f32": np.float32}
+
+
+@pytest.fixture(autouse=True)
+def _reset_shares():
+    import segmented_reduction_amd as sr
+    sr.set_shares(0)
+    yield
+    sr.set_shares(0)
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return json.load(fh)
+
+
+@pytest.mark.parametrize("kind", ["u32", "i32", "f32"])
+def test_worked_example(kind):
+    """luma.gl GPUSegmentedReduction, 'What is segmented reduction?'."""
+    g = _golden("segmented_reduction_worked_example.json")
+    vals = np.array(g["values"], dtype=NP_T[kind])
+    off = np.array(g["offsets"], dtype=np.int64)
+    for op in ("sum", "min", "max"):
+        gu.say(f"worked example {kind} {op}")
+        out, arg = gu.run_gpu(vals, off, op)
+        assert out[:, 0].tolist() == g[op]
+        if op != "sum":
+            assert arg[:, 0].tolist() == g["derived"]["arg" + op]
+
+
+@pytest.mark.parametrize("kind", ["u32", "i32", "f32"])
+def test_empty_segments_fixture(kind):
+    g = _golden("empty_segments.json")
+    vals = np.array(g["values"], dtype=NP_T[kind])
+    off = np.array(g["offsets"], dtype=np.int64)
+    for op in ("sum", "min", "max"):
+        gu.say(f"empty fixture {kind} {op}")
+        out, arg = gu.run_gpu(vals, off, op)
+        assert out[:, 0].tolist() == g[op]
+        if op != "sum":
+            assert arg[:, 0].tolist() == g["arg" + op]
+
+
+FEATS = [1, 2, 3, 4, 5, 8, 16, 32, 33, 64, 65, 128, 256, 260]
+
+
+@pytest.mark.parametrize("feat", FEATS)
+@pytest.mark.parametrize("kind", ["u32", "i32", "f32"])
+def test_random_ragged(kind, feat):
+    """Ragged segments, 10 % empty, one long segment, offsets[0] > 0, unread
+    rows after the last offset; several work partitions (share counts)."""
+    rows_target = 60_000 if feat <= 8 else 6_000
+    mean_len = 12
+    segs = max(4, rows_target // (mean_len + 1))
+    off, vals = W.ragged(seed=feat * 7 + len(kind), segments=segs, mean_len=mean_len, feat=feat, dtype=kind,
+                         empty_frac=0.1, base=5, tail_rows=3, long_segment=rows_target // 3)
+    ops = ["sum", "min", "max"] + (["mean"] if kind == "f32" else [])
+    for op in ops:
+        orc = oracle.reduce(vals, off, op)
+        for shares in (None, 1, 3, 64, 997):
+            gu.say(f"ragged kind={kind} F={feat} op={op} shares={shares} S={segs}")
+            out, arg = gu.run_gpu(vals, off, op, shares=shares)
+            gu.assert_parity(vals, off, op, out, arg, orc=orc, what=f"ragged F={feat} shares={shares}")
+
+
+@pytest.mark.parametrize("feat", [1, 3, 4, 32, 64])
+@pytest.mark.parametrize("kind", ["u32", "i32", "f32"])
+def test_ties_go_to_lower_row(kind, feat):
+    off, vals = W.ragged(seed=100 + feat, segments=2000, mean_len=15, feat=feat, dtype=kind, values="ties",
+                         long_segment=5000)
+    for op in ("min", "max"):
+        for shares in (None, 7, 333):
+            out, arg = gu.run_gpu(vals, off, op, shares=shares)
+            gu.assert_parity(vals, off, op, out, arg, what=f"ties F={feat} shares={shares}")
+
+
+@pytest.mark.parametrize("feat", [1, 4, 32, 64, 5])
+def test_integer_valued_floats_sum_exactly(feat):
+    """Small integer-valued floats add exactly in any order: the GPU sum must
+    equal the oracle's bit for bit (pins indexing independently of rounding)."""
+    off, vals = W.ragged(seed=200 + feat, segments=3000, mean_len=20, feat=feat, values="intfloat",
+                         long_segment=20000, base=2)
+    for shares in (None, 5, 1024):
+        gu.say(f"intfloat F={feat} shares={shares}")
+        out, _ = gu.run_gpu(vals, off, "sum", shares=shares)
+        orc = oracle.reduce(vals, off, "sum")
+        assert np.array_equal(out.view(np.uint32), orc.out.view(np.uint32))
+
+
+def test_repeat_runs_are_bitwise_identical():
+    off, vals = W.ragged(seed=5, segments=20000, mean_len=40, feat=1, long_segment=300000)
+    v, o = gu.to_gpu(vals), gu.to_gpu(off)
+    import segmented_reduction_amd as sr
+    first = None
+    for rep in range(5):
+        gu.say(f"determinism rep {rep}")
+        out, _ = sr.reduce(v, o, "sum")
+        b = out.cpu().numpy().tobytes()
+        first = first or b
+        assert b == first
+
+
+def test_single_segment_is_a_global_reduction():
+    rng = np.random.default_rng(1)
+    vals = rng.standard_normal(3_000_000).astype(np.float32)
+    off = np.array([123, 2_999_000], dtype=np.int64)
+    for op in ("sum", "min", "max", "mean"):
+        gu.check(vals, off, op, what="S=1")
+    ints = rng.integers(-10, 10, 3_000_000, dtype=np.int32)
+    for op in ("min", "max"):
+        out, arg = gu.run_gpu(ints, off, op)
+        seg = ints[123:2_999_000]
+        want = seg.min() if op == "min" else seg.max()
+        first = 123 + int(np.flatnonzero(seg == want)[0])
+        assert out[0, 0] == want and arg[0, 0] == first
+
+
+def test_all_segments_empty():
+    off = np.full(5001, 7, dtype=np.int64)
+    for kind in ("u32", "i32", "f32"):
+        vals = np.ones((10, 4), dtype=NP_T[kind])
+        for op in ("sum", "min", "max") + (("mean",) if kind == "f32" else ()):
+            out, arg = gu.run_gpu(vals, off, op)
+            assert (out == 0).all()
+            if arg is not None:
+                assert (arg == -1).all()
+
+
+def test_every_segment_one_row():
+    vals = np.arange(100_000, dtype=np.int32)[::-1].copy()
+    off = np.arange(100_001, dtype=np.int64)
+    for op in ("sum", "min", "max"):
+        out, arg = gu.run_gpu(vals, off, op)
+        assert np.array_equal(out[:, 0], vals)
+        if arg is not None:
+            assert np.array_equal(arg[:, 0], np.arange(100_000))
+
+
+def test_zero_segments_is_a_no_op():
+    import segmented_reduction_amd as sr
+    v = torch.ones(10, device="cuda")
+    o = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out, arg = sr.reduce(v, o, "max")
+    torch.cuda.synchronize()
+    assert out.shape == (0,) and arg.shape == (0,)
+
+
+def test_unaligned_rows_use_the_scalar_path():
+    """values starting 4 bytes past an allocation (F = 4): 16-byte loads do not
+    apply and the 4-byte path must give the same results."""
+    off, vals = W.ragged(seed=9, segments=3000, mean_len=10, feat=4, dtype="f32")
+    big = torch.zeros(vals.size + 1, dtype=torch.float32, device="cuda")
+    big[1:] = gu.to_gpu(vals.reshape(-1))
+    v = big[1:].view(vals.shape)
+    assert v.data_ptr() % 16 != 0
+    for op in ("sum", "max"):
+        out, arg = gu.run_gpu(vals, off, op, values_t=v)
+        gu.assert_parity(vals, off, op, out, arg, what="unaligned")
+
+
+def test_value_only_min_max():
+    off, vals = W.ragged(seed=10, segments=500, mean_len=30, feat=32, dtype="i32")
+    for op in ("min", "max"):
+        out, arg = gu.run_gpu(vals, off, op, want_arg=False)
+        assert arg is None
+        gu.assert_parity(vals, off, op, out, None, what="value-only")
+
+
+def test_guard_bands_are_untouched():
+    """Outputs written into the middle of larger buffers: the bytes around
+    them keep their canary values."""
+    import segmented_reduction_amd as sr
+    off, vals = W.ragged(seed=11, segments=777, mean_len=9, feat=8, dtype="u32")
+    s = off.size - 1
+    pad = 64
+    out_big = torch.full((s * 8 + 2 * pad,), -1515870811, dtype=torch.int32, device="cuda")
+    arg_big = torch.full((s * 8 + 2 * pad,), -12345, dtype=torch.int64, device="cuda")
+    out_view = out_big[pad:pad + s * 8].view(torch.uint32).view(s, 8)
+    arg_view = arg_big[pad:pad + s * 8].view(s, 8)
+    sr.reduce(gu.to_gpu(vals), gu.to_gpu(off), "max", out=out_view, arg=arg_view)
+    torch.cuda.synchronize()
+    ob, ab = out_big.cpu().numpy(), arg_big.cpu().numpy()
+    assert (ob[:pad] == np.int32(-1515870811)).all() and (ob[-pad:] == np.int32(-1515870811)).all()
+    assert (ab[:pad] == -12345).all() and (ab[-pad:] == -12345).all()
+    gu.assert_parity(vals, off, "max", out_view.cpu().numpy().reshape(s, 8), arg_view.cpu().numpy(), what="guard")
+
+
+def test_three_dimensional_values_flatten_features():
+    off, vals = W.ragged(seed=12, segments=400, mean_len=7, feat=12, dtype="f32")
+    v3 = vals.reshape(-1, 3, 4)
+    import segmented_reduction_amd as sr
+    out, arg = sr.reduce(gu.to_gpu(v3), gu.to_gpu(off), "min")
+    assert out.shape == (400, 3, 4) and arg.shape == (400, 3, 4)
+    gu.assert_parity(vals, off, "min", out.cpu().numpy().reshape(400, 12), arg.cpu().numpy().reshape(400, 12))
