@@ -70,7 +70,8 @@ enum segred_status {
  * Errors: SEGRED_ERR_INVALID_ARGUMENT for S < 0, feat < 1, an unknown dtype
  * or op, a NULL values/offsets/out with S > 0, values/out not 4-byte aligned,
  * offsets/arg_out not 8-byte aligned.  SEGRED_ERR_UNSUPPORTED for MEAN of an
- * integer type.  SEGRED_ERR_OUT_OF_MEMORY if scratch is unavailable.
+ * integer type or for feat > 2^24 (rows are addressed with 32-bit offsets
+ * inside a chunk).  SEGRED_ERR_OUT_OF_MEMORY if scratch is unavailable.
  * SEGRED_ERR_HIP if a launch fails.  The offsets are NOT read back or checked:
  * offsets that decrease or point outside `values` are undefined behaviour, as
  * is `out`/`arg_out` overlapping the inputs.  The device never needs the row
@@ -137,11 +138,13 @@ int64_t segred_get_shares(int32_t dtype, int32_t op, int64_t feat);
  * segred_reduce call records a pair of HIP events on its stream around its
  * streaming (first) kernel.  segred_timing_read waits for the recorded
  * events, returns the summed duration in milliseconds and the number of
- * timed launches, and clears the record.  Up to 4096 launches are kept;
- * later ones are not timed.  Host-side state, process-wide, not thread-safe.
+ * timed launches, writes the first `capacity` per-launch durations (ms, in
+ * launch order) to the host array `each_ms` (may be NULL when capacity is
+ * 0), and clears the record.  Up to 4096 launches are kept; later ones are
+ * not timed.  Host-side state, process-wide, not thread-safe.
  */
 int segred_timing_enable(int enable);
-int segred_timing_read(double *total_ms, int64_t *launches);
+int segred_timing_read(double *total_ms, int64_t *launches, float *each_ms, int64_t capacity);
 
 #ifdef __cplusplus
 }

@@ -62,7 +62,8 @@ def library(path: str | None = None):
             lib.segred_get_shares.restype = i64
             lib.segred_timing_enable.argtypes = [ctypes.c_int]
             lib.segred_timing_enable.restype = ctypes.c_int
-            lib.segred_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+            lib.segred_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64),
+                                              ctypes.POINTER(ctypes.c_float), i64]
             lib.segred_timing_read.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -172,9 +173,10 @@ def timing_enable(enable: bool = True):
     _check(library().segred_timing_enable(1 if enable else 0), "segred_timing_enable")
 
 
-def timing_read():
-    """(total milliseconds, launches) of the streaming kernel since the last read."""
+def timing_read(capacity: int = 4096):
+    """(total ms, launches, per-launch ms list) of the streaming kernel since the last read."""
     ms = ctypes.c_double(0.0)
     n = ctypes.c_int64(0)
-    _check(library().segred_timing_read(ctypes.byref(ms), ctypes.byref(n)), "segred_timing_read")
-    return ms.value, n.value
+    each = (ctypes.c_float * max(capacity, 1))()
+    _check(library().segred_timing_read(ctypes.byref(ms), ctypes.byref(n), each, capacity), "segred_timing_read")
+    return ms.value, n.value, [each[i] for i in range(min(n.value, capacity))]

@@ -27,7 +27,7 @@ hipMemPool_t pool_for_current_device() {
         hipMemPool_t pool = nullptr;
         if (hipMemPoolCreate(&pool, &props) != hipSuccess) return nullptr;
         uint64_t keep = UINT64_MAX;
-        hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
         g_pools[dev] = pool;
     }
     return g_pools[dev];
@@ -110,13 +110,14 @@ extern "C" int segred_timing_enable(int enable) {
     return SEGRED_OK;
 }
 
-extern "C" int segred_timing_read(double *total_ms, int64_t *launches) {
-    if (!total_ms || !launches) return SEGRED_ERR_INVALID_ARGUMENT;
+extern "C" int segred_timing_read(double *total_ms, int64_t *launches, float *each_ms, int64_t capacity) {
+    if (!total_ms || !launches || capacity < 0 || (capacity > 0 && !each_ms)) return SEGRED_ERR_INVALID_ARGUMENT;
     double sum = 0.0;
     for (int i = 0; i < g_timing.used; ++i) {
         if (hipEventSynchronize(g_timing.ev[2 * i + 1]) != hipSuccess) return SEGRED_ERR_HIP;
         float ms = 0.f;
         if (hipEventElapsedTime(&ms, g_timing.ev[2 * i], g_timing.ev[2 * i + 1]) != hipSuccess) return SEGRED_ERR_HIP;
+        if (i < capacity) each_ms[i] = ms;
         sum += ms;
     }
     *total_ms = sum;

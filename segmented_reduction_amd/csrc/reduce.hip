@@ -9,26 +9,37 @@
 // Work partition.  The rows and the segment ends are merged into one
 // sequence (a segment's rows, then its end), the merge-path view of
 // Merrill & Garland's merge-based SpMV that the graph-reduce README cites.
-// The sequence is cut into NW equal shares, one per wave; a wave finds its
-// share's (segment, row) coordinates with a 64-way search over the offsets.
-// Long or skewed segments are therefore spread over many waves instead of
-// serialising on one.
+// The sequence is cut into NW equal shares, one per resident wave; a wave
+// finds its share's (segment, row) coordinates with a search over the
+// offsets (a shared first round in LDS, then 256-way rounds).  Long or skewed
+// segments are therefore spread over many waves instead of serialising on
+// one.
 //
-// Inside a share the wave walks chunks of CH items.  A chunk's rows are
-// split into G groups of V consecutive rows; each group is L lanes wide and
-// each lane holds VEC features of a row.  A group walks its rows in order,
-// finishing every segment that ends inside it; a segmented scan over the G
-// groups (cross-lane moves) completes segments cut by group and chunk
-// boundaries.  Segments cut by a share boundary leave one partial per share
-// in scratch; a second kernel combines them in share order.  No atomics are
-// used anywhere, and every summation order is a fixed function of the
-// offsets and NW, so results repeat bit for bit.
+// Inside a share the wave walks chunks of CH items.  For rows of F >= 2
+// features each lane owns one feature; a chunk's rows are split into G
+// groups of V consecutive rows (G = 1 for F >= 64, where segment control is
+// wave-uniform).  For 1-D values each lane owns 16 consecutive elements,
+// staged through LDS.  A group walks its rows in order, finishing every
+// segment that ends inside it; a segmented scan over the groups (cross-lane
+// moves) completes segments cut by group and chunk boundaries.  Segments cut
+// by a share boundary leave one partial per share in scratch; a second kernel
+// combines them in share order.  No atomics are used anywhere, and every
+// summation order is a fixed function of the offsets and NW, so results
+// repeat bit for bit.
+//
+// Memory: rows are read through buffer descriptors that cover exactly the
+// valid part of a chunk (reads past it return 0, so no clamping), and the
+// next chunk streams into each register as soon as the current chunk has
+// consumed it.
 //
 // Accumulators: float sums in float64 (rounded to float32 once), integer sums
 // in wrapping uint32, min/max as a 64-bit word (order key << 32 | row code)
 // whose integer max/min picks the extremum and, on equal keys, the lowest row
 // (the packed value/row word of the graph-reduce README's "Method").
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "internal.hpp"
 #include "wave.hpp"
@@ -44,7 +55,7 @@ struct KArgs {
     int64_t S, F, NW;
     uint32_t *out;           // [S, F]
     int64_t *arg;            // [S, F] or null
-    int64_t *hdr;            // [NW][3]: head segment, tail segment, first row of the share
+    int64_t *hdr;            // [NW][4]: see write_header
     uint64_t *hval;          // [NW][F]: partial of the share's first segment when it began earlier
     uint64_t *tval;          // [NW][F]: partial of the share's last segment when it continues
 };
@@ -163,32 +174,133 @@ __device__ __forceinline__ int count_le(const uint32_t *arr, int n, uint32_t x) 
     return lo;
 }
 
-// Pass 1: streaming reduction of every share.
-//   VEC   features per lane (4: 16-byte loads, F % 4 == 0; 1: 4-byte loads)
-//   L     lanes per row (power of two); G = 64 / L row groups per wave
-//   V     consecutive rows per group per chunk; CH = G * V items per chunk
-//   STAGE rows staged through LDS (F == 1: a lane's V consecutive elements)
-template <int DT, int OP, int VEC, int L, int V, bool STAGE>
-__global__ __launch_bounds__(256) void seg_reduce_pass1(const KArgs a) {
+// Item d is preceded by i(d) = max{ i in [0, S] : offsets[i] - o0 + i <= d }
+// segment ends (offsets[i] - o0 + i increases strictly with i).  The first
+// round of the search does not depend on d: the workgroup reads 256 evenly
+// spaced offsets (offsets[0] and offsets[S] among them) into LDS once, which
+// also gives o0 and the total item count T.  Each wave then narrows both ends
+// of its share with 256-way rounds (4 probes per lane): 2 memory round trips
+// in all for S < 65K segments, 3 for S < 16M.  Every probe is clamped into
+// the array and loaded unconditionally (a load under a branch would be
+// waited for inside the branch).
+
+// A wave's share of the merged (rows + segment ends) sequence: items
+// [d0, d1), i.e. segment ends [i0, i1) and rows [j0, j1) (rows relative to
+// offsets[0]).
+struct Share {
+    int64_t o0, D, d0, d1, i0, j0, i1, j1;
+    int64_t first_row; // first row of segment i0 (relative to offsets[0])
+    bool split_head;   // segment i0 ends in the share but began in an earlier one
+    bool has_tail;     // segment i1 has rows in the share and continues past it
+};
+
+__device__ __forceinline__ Share find_share(const int64_t *off, int64_t S, int64_t NW, int64_t wave, int lane,
+                                            int64_t *s_probe /* LDS [256], workgroup-wide */) {
+    const int tid = threadIdx.x;
+    const int64_t step1 = (S + 254) / 255;  // probes k * step1, k < 255, and S
+    const int64_t p = tid == 255 ? S : min((int64_t)tid * step1, S);
+    s_probe[tid] = off[p];
+    __syncthreads();
+
+    const int64_t o0 = s_probe[0];
+    const int64_t T = (s_probe[255] - o0) + S;
+    const int64_t D = (T + NW - 1) / NW;
+    const int64_t d0 = min(wave * D, T), d1 = min(d0 + D, T);
+
+    // round 1 from LDS: the last probe with key <= d bounds i(d) from below,
+    // the next one from above (the count is >= 1 since key(0) = 0 <= d)
+    int c0 = 0, c1 = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int k = u * 64 + lane;
+        const int64_t pk = k == 255 ? S : min((int64_t)k * step1, S);
+        const int64_t key = s_probe[k] - o0 + pk;
+        c0 += popc64(ballot(key <= d0));
+        c1 += popc64(ballot(key <= d1));
+    }
+    auto bound = [&](int cnt, int64_t &lo, int64_t &hi) __attribute__((always_inline)) {
+        lo = (cnt - 1) == 255 ? S : min((int64_t)(cnt - 1) * step1, S);
+        hi = cnt >= 256 ? S : ((cnt == 255 ? S : min((int64_t)cnt * step1, S)) - 1);
+        if (hi < lo) hi = lo;
+    };
+    int64_t lo0, hi0, lo1, hi1;
+    bound(c0, lo0, hi0);
+    bound(c1, lo1, hi1);
+    while (lo0 < hi0 || lo1 < hi1) {
+        const int64_t st0 = (hi0 - lo0 + 255) >> 8, st1 = (hi1 - lo1 + 255) >> 8;
+        int64_t k0[4], k1[4];
+        bool ok0[4], ok1[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t j = (int64_t)(u * 64 + lane + 1);
+            const int64_t p0 = lo0 + j * st0, p1 = lo1 + j * st1;
+            ok0[u] = lo0 < hi0 && p0 <= hi0;
+            ok1[u] = lo1 < hi1 && p1 <= hi1;
+            const int64_t q0 = min(p0, S), q1 = min(p1, S);
+            k0[u] = off[q0] - o0 + q0;
+            k1[u] = off[q1] - o0 + q1;
+        }
+        int n0 = 0, n1 = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            n0 += popc64(ballot(ok0[u] && k0[u] <= d0));
+            n1 += popc64(ballot(ok1[u] && k1[u] <= d1));
+        }
+        if (lo0 < hi0) {
+            hi0 = min(hi0, lo0 + (int64_t)(n0 + 1) * st0 - 1);
+            lo0 += (int64_t)n0 * st0;
+        }
+        if (lo1 < hi1) {
+            hi1 = min(hi1, lo1 + (int64_t)(n1 + 1) * st1 - 1);
+            lo1 += (int64_t)n1 * st1;
+        }
+    }
+    // Everything here is the same in every lane; saying so lets the compiler
+    // keep it in scalar registers (and build uniform buffer descriptors).
+    Share sh;
+    sh.o0 = readfirst(o0);
+    sh.D = readfirst(D);
+    sh.d0 = readfirst(d0);
+    sh.d1 = readfirst(d1);
+    sh.i0 = readfirst(lo0);
+    sh.j0 = sh.d0 - sh.i0;
+    sh.i1 = readfirst(lo1);
+    sh.j1 = sh.d1 - sh.i1;
+    sh.first_row = readfirst(off[min(sh.i0, S)] - sh.o0);
+    sh.split_head = sh.i0 < sh.i1 && sh.first_row < sh.j0;
+    const int64_t tail_row = readfirst(off[min(sh.i1, S)] - sh.o0);
+    sh.has_tail = sh.i1 < S && tail_row < sh.j1;
+    return sh;
+}
+
+// Header of a share for the combine kernel: [split head segment or -1,
+// continuing tail segment or -1, first row of the share, share holding the
+// split head segment's first row].
+__device__ __forceinline__ void write_header(const KArgs &a, int64_t wave, const Share &sh) {
+    a.hdr[wave * 4 + 0] = sh.split_head ? sh.i0 : -1;
+    a.hdr[wave * 4 + 1] = sh.has_tail ? sh.i1 : -1;
+    a.hdr[wave * 4 + 2] = sh.o0 + sh.j0;
+    a.hdr[wave * 4 + 3] = sh.split_head ? (sh.first_row + sh.i0) / sh.D : wave;
+}
+
+// Pass 1 for rows of F >= 2 features: each lane owns one feature of a row.
+//   L   lanes per row (next power of two >= F, at most 64; wider rows are
+//       done in blocks of 64 features); G = 64 / L row groups per wave
+//   V   consecutive rows per group per chunk; CH = G * V items per chunk
+// With F >= 64 a row is the whole wave: segment control is wave-uniform and
+// no cross-lane step is needed at all.  A chunk's rows are fetched together
+// with its first 64 segment ends before its row count is known (up to CH
+// rows; rows past the chunk are fetched again by the next chunk), and the
+// next chunk is fetched while the current one is processed.
+template <int DT, int OP, int L, int V>
+__global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
     using R = Red<DT, OP>;
     using acc_t = typename R::acc_t;
     constexpr int G = 64 / L;
     constexpr int CH = G * V;
-    constexpr int FB = L * VEC;
     constexpr uint32_t kInf = 0xFFFFFFFFu;
-    static_assert(!STAGE || (VEC == 1 && L == 1), "staging is for one-feature rows");
-    struct AccV {
-        acc_t v[VEC];
-        __device__ static __forceinline__ AccV identity() {
-            AccV r;
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) r.v[i] = R::id();
-            return r;
-        }
-    };
 
     __shared__ __attribute__((aligned(16))) uint32_t s_ends[4][CH];
-    __shared__ __attribute__((aligned(16))) uint32_t s_vals[4][STAGE ? CH : 1];
 
     const int wid = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -196,131 +308,119 @@ __global__ __launch_bounds__(256) void seg_reduce_pass1(const KArgs a) {
     const int c = lane % L;
     const int64_t wave = (int64_t)blockIdx.x * 4 + wid;
     const int64_t *off = a.offsets;
-    const int64_t S = a.S;
+    __shared__ int64_t s_probe[256];
+    const Share sh = find_share(off, a.S, a.NW, wave, lane, s_probe);
+    const int64_t o0 = sh.o0, base = sh.o0 + sh.j0;
+    uint32_t *se = s_ends[wid];
+    const uint32_t gv = (uint32_t)(g * V);
 
-    const int64_t o0 = off[0];
-    const int64_t T = (off[S] - o0) + S;
-    const int64_t D = (T + a.NW - 1) / a.NW;
-    const int64_t d0 = min(wave * D, T);
-    const int64_t d1 = min(d0 + D, T);
+    for (int64_t fbase = 0; fbase < a.F; fbase += L) {
+        const int64_t f = fbase + c;
+        const bool fvalid = f < a.F;
 
-    // 64-way search for i(d) = max{ i in [0, S] : offsets[i] - o0 + i <= d }
-    // at both ends of the share.
-    int64_t lo0 = 0, hi0 = S, lo1 = 0, hi1 = S;
-    while (lo0 < hi0 || lo1 < hi1) {
-        const int64_t st0 = (hi0 - lo0 + 63) >> 6, st1 = (hi1 - lo1 + 63) >> 6;
-        const int64_t p0 = lo0 + (int64_t)(lane + 1) * st0, p1 = lo1 + (int64_t)(lane + 1) * st1;
-        const bool ok0 = lo0 < hi0 && p0 <= hi0, ok1 = lo1 < hi1 && p1 <= hi1;
-        const int64_t k0 = ok0 ? off[p0] - o0 + p0 : 0;
-        const int64_t k1 = ok1 ? off[p1] - o0 + p1 : 0;
-        const int c0 = popc64(ballot(ok0 && k0 <= d0));
-        const int c1 = popc64(ballot(ok1 && k1 <= d1));
-        if (lo0 < hi0) {
-            hi0 = min(hi0, lo0 + (int64_t)(c0 + 1) * st0 - 1);
-            lo0 += (int64_t)c0 * st0;
-        }
-        if (lo1 < hi1) {
-            hi1 = min(hi1, lo1 + (int64_t)(c1 + 1) * st1 - 1);
-            lo1 += (int64_t)c1 * st1;
-        }
-    }
-    const int64_t i0 = lo0, j0 = d0 - lo0, i1 = lo1, j1 = d1 - lo1;
-    const bool split_head = i0 < i1 && off[i0] - o0 < j0;  // first segment began in an earlier share
-    const bool has_tail = i1 < S && off[i1] - o0 < j1;      // last segment continues past the share
-    const int64_t base = o0 + j0;
+        // Partial of the open segment (the one the next chunk starts in),
+        // kept per lane; summed over the groups only when a chunk finishes
+        // the segment, so chunks without a segment end need no cross-lane
+        // work.
+        acc_t open = R::id();
+        bool open_spread = false;  // open partials are in several groups
 
-    for (int64_t fbase = 0; fbase < a.F; fbase += FB) {
-        const int64_t f0 = fbase + (int64_t)c * VEC;
-        const bool fvalid = f0 < a.F;
-        acc_t carry[VEC];
+        // Fetch: a chunk's first 64 segment ends (index clamped into the
+        // array, loaded unconditionally: a load under a branch would be
+        // waited for inside the branch) and its rows through a buffer
+        // descriptor that covers only the rows inside the share, so rows past
+        // it read as 0 without touching memory (a chunk that does not exist
+        // gets an empty descriptor).  One lane offset serves all rows; the row
+        // step is a scalar offset.  Register x[t] is refilled with row t of
+        // the next chunk as soon as row t of the current chunk is consumed, so
+        // the next chunk streams in while this one is processed without a
+        // second register set.
+        const uint32_t row_bytes = (uint32_t)(a.F * 4);
+        const uint32_t voff = (uint32_t)((gv * a.F + c) * 4);
+        auto rows_of = [&](int64_t ic_, int64_t jc_) __attribute__((always_inline)) {
+            const int64_t rmax = ic_ + jc_ < sh.d1 ? min((int64_t)CH, sh.j1 - jc_) : 0;
+            return make_rsrc(a.values + (o0 + jc_) * a.F + fbase, (uint32_t)(rmax * row_bytes));
+        };
+        uint32_t x[V];
+        int64_t ic = sh.i0, jc = sh.j0;
+        int64_t en = off[min(ic + 1 + lane, a.S)];
+        {
+            const auto rs = rows_of(ic, jc);
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) carry[v] = R::id();
-
-        int64_t ic = i0, jc = j0;
-        while (ic + jc < d1) {
-            const int64_t items = min((int64_t)CH, d1 - ic - jc);
-            const int64_t ends_left = min((int64_t)CH, i1 - ic);
-
-            // Rows of a staged chunk are fetched before its length is known
-            // (at most CH rows; the ones past the chunk are fetched again by
-            // the next chunk).
-            uint32_t sv[STAGE ? CH / 64 : 1];
-            if constexpr (STAGE) {
-                const int64_t rmax = min((int64_t)CH, j1 - jc);
-                const uint32_t *src = a.values + (o0 + jc);
-#pragma unroll
-                for (int u = 0; u < CH / 64; ++u) {
-                    const int r = u * 64 + lane;
-                    sv[u] = r < rmax ? src[r] : 0u;
-                }
-            }
+            for (int t = 0; t < V; ++t) x[t] = ld32(rs, voff, t * row_bytes);
+        }
+        while (ic + jc < sh.d1) {
+            const int64_t items = min((int64_t)CH, sh.d1 - ic - jc);
+            const int64_t ends_left = min((int64_t)CH, sh.i1 - ic);
 
             // Segment ends inside this chunk: end k (row position e relative
             // to jc) is one of the first `items` items iff e + k + 1 <= items.
-            int ne = 0;
-            for (int b = 0; b < CH; b += 64) {
+            const int64_t e0 = en - o0 - jc;
+            const bool c0 = lane < ends_left && e0 + lane + 1 <= items;
+            int cnt = popc64(ballot(c0));
+            if (c0) se[lane] = (uint32_t)e0;
+            int ne = cnt;
+            for (int b = 64; cnt == 64 && b < CH; b += 64) {
                 const int k = b + lane;
                 const bool valid = k < ends_left;
-                const int64_t e = valid ? off[ic + 1 + k] - o0 - jc : 0;
+                const int64_t e = off[min(ic + 1 + k, a.S)] - o0 - jc;
                 const bool cond = valid && e + k + 1 <= items;
-                const int cnt = popc64(ballot(cond));
-                if (cond) s_ends[wid][k] = (uint32_t)e;
+                cnt = popc64(ballot(cond));
+                if (cond) se[k] = (uint32_t)e;
                 ne += cnt;
-                if (cnt < 64) break;
             }
             const int rows = (int)(items - ne);
-            if constexpr (STAGE) {
+            const int64_t icn = ic + ne, jcn = jc + rows;
+            en = off[min(icn + 1 + lane, a.S)];
+            const auto rsn = rows_of(icn, jcn);
+            const uint32_t relbase = (uint32_t)(jc - sh.j0);
+
+            if (ne == 0) {
+                // No segment ends here: every row continues the open segment.
 #pragma unroll
-                for (int u = 0; u < CH / 64; ++u) s_vals[wid][u * 64 + lane] = sv[u];
+                for (int t = 0; t < V; ++t) {
+                    const uint32_t r = gv + t;
+                    if ((int)r < rows) open = R::comb(open, R::lift(x[t], relbase + r));
+                    x[t] = ld32(rsn, voff, t * row_bytes);
+                }
+                open_spread = G > 1;
+                ic = icn;
+                jc = jcn;
+                continue;
+            }
+
+            // The open segment's partial so far, needed by group 0 only: the
+            // groups' parts in group order when they are spread.
+            acc_t carry = open;
+            if (G > 1 && open_spread) {
+#pragma unroll
+                for (int m = L; m < 64; m <<= 1) {
+                    const acc_t o = lane_get(carry, lane ^ m);
+                    carry = (lane & m) ? R::comb(o, carry) : R::comb(carry, o);
+                }
             }
             wave_lds_sync();
 
             // Group g owns rows [gV, gV + V) and the ends at positions
             // (gV, gV + V] (group 0 also those at 0).
-            const uint32_t gv = (uint32_t)(g * V);
-            const int a_lo = g == 0 ? 0 : count_le(s_ends[wid], ne, gv);
-            const int a_hi = count_le(s_ends[wid], ne, gv + V);
-
-            uint32_t x[V][VEC];
-            if constexpr (STAGE) {
-#pragma unroll
-                for (int t = 0; t < V; t += 4) {
-                    const uint4 q = *reinterpret_cast<const uint4 *>(&s_vals[wid][gv + t]);
-                    x[t][0] = q.x;
-                    x[t + 1][0] = q.y;
-                    x[t + 2][0] = q.z;
-                    x[t + 3][0] = q.w;
-                }
-            } else {
-#pragma unroll
-                for (int t = 0; t < V; ++t) {
-                    const int r = (int)gv + t;
-                    const int64_t idx = (o0 + jc + r) * a.F + f0;
-                    if (r < rows && fvalid) {
-                        if constexpr (VEC == 4) {
-                            const uint4 q = *reinterpret_cast<const uint4 *>(a.values + idx);
-                            x[t][0] = q.x;
-                            x[t][1] = q.y;
-                            x[t][2] = q.z;
-                            x[t][3] = q.w;
-                        } else {
-                            x[t][0] = a.values[idx];
-                        }
-                    } else {
-#pragma unroll
-                        for (int v = 0; v < VEC; ++v) x[t][v] = 0u;
-                    }
-                }
+            int a_lo = 0, a_hi = ne;
+            if constexpr (G > 1) {
+                a_lo = g == 0 ? 0 : count_le(se, ne, gv);
+                a_hi = count_le(se, ne, gv + V);
             }
 
-            // Walk the group's rows in order.
-            AccV acc = AccV::identity(), hacc = AccV::identity();
+            // Walk the group's rows in order (wave-uniform control for G = 1).
+            acc_t acc = R::id(), hacc = R::id();
             bool hh = false;  // this group finished at least one segment
             int64_t hseg = 0;
             int k = a_lo;
             int64_t seg = ic + a_lo;
-            uint32_t next_end = k < a_hi ? s_ends[wid][k] : kInf;
-            const uint32_t relbase = (uint32_t)(jc - j0);
+            auto end_at = [&](int kk) __attribute__((always_inline)) -> uint32_t {
+                if (kk >= a_hi) return kInf;
+                const uint32_t e = se[kk];
+                return G == 1 ? __builtin_amdgcn_readfirstlane(e) : e;
+            };
+            uint32_t next_end = end_at(k);
 
             auto finish = [&]() __attribute__((always_inline)) {
                 if (!hh) {
@@ -328,79 +428,284 @@ __global__ __launch_bounds__(256) void seg_reduce_pass1(const KArgs a) {
                     hseg = seg;
                     hacc = acc;
                 } else if (fvalid) {
-                    store_final<DT, OP, VEC>(a, seg, f0, acc.v, base);
+                    store_final<DT, OP, 1>(a, seg, f, &acc, base);
                 }
-                acc = AccV::identity();
+                acc = R::id();
                 ++seg;
                 ++k;
-                next_end = k < a_hi ? s_ends[wid][k] : kInf;
+                next_end = end_at(k);
             };
 
 #pragma unroll
             for (int t = 0; t < V; ++t) {
                 const uint32_t r = gv + t;
                 while (next_end <= r) finish();
-                if ((int)r < rows) {
-#pragma unroll
-                    for (int v = 0; v < VEC; ++v) acc.v[v] = R::comb(acc.v[v], R::lift(x[t][v], relbase + r));
-                }
+                if ((int)r < rows) acc = R::comb(acc, R::lift(x[t], relbase + r));
+                x[t] = ld32(rsn, voff, t * row_bytes);
             }
             while (k < a_hi) finish();
 
-            // Segmented inclusive scan over the groups; the chunk carry enters
-            // at group 0.  A group that finished a segment restarts the scan.
-            bool flag = hh;
-            acc_t xs[VEC];
+            // Segmented inclusive scan over the groups; the carry enters at
+            // group 0.  A group that finished a segment restarts the scan.
+            acc_t xs = (g == 0 && !hh) ? R::comb(carry, acc) : acc;
+            acc_t ex = carry;
+            if constexpr (G > 1) {
+                bool flag = hh;
 #pragma unroll
-            for (int v = 0; v < VEC; ++v) xs[v] = (g == 0 && !flag) ? R::comb(carry[v], acc.v[v]) : acc.v[v];
-#pragma unroll
-            for (int o = L; o < 64; o <<= 1) {
-                const int src = (lane - o) & 63;
-                const bool pf = lane_get(flag, src);
-                acc_t px[VEC];
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) px[v] = lane_get(xs[v], src);
-                if (lane >= o) {
-                    if (!flag) {
-#pragma unroll
-                        for (int v = 0; v < VEC; ++v) xs[v] = R::comb(px[v], xs[v]);
+                for (int o = L; o < 64; o <<= 1) {
+                    const int src = (lane - o) & 63;
+                    const bool pf = lane_get(flag, src);
+                    const acc_t px = lane_get(xs, src);
+                    if (lane >= o) {
+                        if (!flag) xs = R::comb(px, xs);
+                        flag = flag || pf;
                     }
-                    flag = flag || pf;
                 }
-            }
-            acc_t ex[VEC];
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) {
-                const acc_t prev = lane_get(xs[v], (lane - L) & 63);
-                ex[v] = g == 0 ? carry[v] : prev;
+                const acc_t prev = lane_get(xs, (lane - L) & 63);
+                if (g != 0) ex = prev;
             }
             if (hh && fvalid) {
-                acc_t hv[VEC];
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) hv[v] = R::comb(ex[v], hacc.v[v]);
-                if (split_head && hseg == i0) {
-#pragma unroll
-                    for (int v = 0; v < VEC; ++v) a.hval[wave * a.F + f0 + v] = R::to_slot(hv[v]);
-                } else {
-                    store_final<DT, OP, VEC>(a, hseg, f0, hv, base);
-                }
+                const acc_t hv = R::comb(ex, hacc);
+                if (sh.split_head && hseg == sh.i0) a.hval[wave * a.F + f] = R::to_slot(hv);
+                else store_final<DT, OP, 1>(a, hseg, f, &hv, base);
             }
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) carry[v] = lane_get(xs[v], (G - 1) * L + c);
+            // The open segment after this chunk: group G-1's inclusive value,
+            // parked in group 0.
+            if constexpr (G > 1) {
+                const acc_t last = lane_get(xs, (G - 1) * L + c);
+                open = g == 0 ? last : R::id();
+            } else {
+                open = xs;
+            }
+            open_spread = false;
 
-            ic += ne;
-            jc += rows;
+            ic = icn;
+            jc = jcn;
             wave_lds_sync();
         }
-        if (has_tail && fvalid) {
+        if (sh.has_tail) {
+            acc_t t = open;
+            if (G > 1 && open_spread) {
 #pragma unroll
-            for (int v = 0; v < VEC; ++v) a.tval[wave * a.F + f0 + v] = R::to_slot(carry[v]);
+                for (int m = L; m < 64; m <<= 1) {
+                    const acc_t o = lane_get(t, lane ^ m);
+                    t = (lane & m) ? R::comb(o, t) : R::comb(t, o);
+                }
+            }
+            if (g == 0 && fvalid) a.tval[wave * a.F + f] = R::to_slot(t);
         }
     }
+    if (lane == 0) write_header(a, wave, sh);
+}
+
+// Pass 1 for one feature per row (1-D values).  A chunk is 1024 items; its
+// elements are fetched with coalesced loads and staged in LDS, lane l then
+// walks elements [16 l, 16 l + 16) in order.  The next chunk's elements and
+// first 128 ends are fetched while the current chunk is processed.  Finished
+// segments park their result in LDS (slot = end index in the chunk, the
+// element and end arrays are reused for the low and high words) and are
+// stored by one coalesced pass at the end of the chunk.
+template <int DT, int OP>
+__global__ __launch_bounds__(256) void seg_reduce_flat(const KArgs a) {
+    using R = Red<DT, OP>;
+    using acc_t = typename R::acc_t;
+    constexpr int V = 16;    // elements per lane per chunk
+    constexpr int CH = 64 * V;
+    constexpr int EC = 512;  // segment ends per chunk at most
+    constexpr int NB = 2;    // batches of 64 ends fetched ahead
+    constexpr uint32_t kInf = 0xFFFFFFFFu;
+    constexpr bool kWide = sizeof(acc_t) == 8;
+    constexpr bool kSum = R::kSumF || R::kSumI;
+
+    __shared__ __attribute__((aligned(16))) uint32_t s_vals[4][CH];  // elements, then result low words
+    __shared__ __attribute__((aligned(16))) uint32_t s_ends[4][EC];  // end positions, then result high words
+    __shared__ int s_first[4][64];                                   // first end owned by each lane
+
+    const int wid = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + wid;
+    const int64_t *off = a.offsets;
+    __shared__ int64_t s_probe[256];
+    const Share sh = find_share(off, a.S, a.NW, wave, lane, s_probe);
+    const int64_t o0 = sh.o0, base = sh.o0 + sh.j0;
+    uint32_t *sv = s_vals[wid];
+    uint32_t *se = s_ends[wid];
+    int *sf = s_first[wid];
+
+    uint32_t X[V];
+    int64_t E[NB];
+    auto fetch = [&](int64_t ic_, int64_t jc_) __attribute__((always_inline)) {
+        // Ends: clamped index, unconditional load (see the row kernel).
+        // Elements: a buffer descriptor over the share's remaining elements
+        // of this chunk, so positions past it read as 0.
+#pragma unroll
+        for (int b = 0; b < NB; ++b) E[b] = off[min(ic_ + 1 + b * 64 + lane, a.S)];
+        const int64_t rmax = min((int64_t)CH, sh.j1 - jc_);
+        const auto rs = make_rsrc(a.values + (o0 + jc_), (uint32_t)(rmax * 4));
+#pragma unroll
+        for (int u = 0; u < V; ++u) X[u] = ld32(rs, (uint32_t)(lane * 4), (uint32_t)(u * 256));
+    };
+
+    acc_t carry = R::id();
+    int64_t ic = sh.i0, jc = sh.j0;
+    if (ic + jc < sh.d1) fetch(ic, jc);
+    while (ic + jc < sh.d1) {
+        int64_t items = min((int64_t)CH, sh.d1 - ic - jc);
+        const int64_t el = min((int64_t)EC, sh.i1 - ic);
+
+        // Ends inside the chunk (end k at row position e: e + k + 1 <= items).
+        int ne = 0;
+        bool more = true;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if (more) {
+                const int k = b * 64 + lane;
+                const bool valid = k < el;
+                const int64_t e = E[b] - o0 - jc;
+                const bool cond = valid && e + k + 1 <= items;
+                const int cnt = popc64(ballot(cond));
+                if (cond) se[k] = (uint32_t)e;
+                ne += cnt;
+                more = cnt == 64;
+            }
+        }
+        for (int b = NB; more && b < EC / 64; ++b) {
+            const int k = b * 64 + lane;
+            const bool valid = k < el;
+            const int64_t e = off[min(ic + 1 + k, a.S)] - o0 - jc;
+            const bool cond = valid && e + k + 1 <= items;
+            const int cnt = popc64(ballot(cond));
+            if (cond) se[k] = (uint32_t)e;
+            ne += cnt;
+            more = cnt == 64;
+        }
+        if (ne == EC) {
+            // At most EC ends per chunk: stop the chunk right after end EC-1.
+            wave_lds_sync();
+            items = (int64_t)se[EC - 1] + EC;
+        }
+        const int rows = (int)(items - ne);
+
+        // Stage the chunk's elements (sums: zero past the chunk's rows).
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+            const int r = u * 64 + lane;
+            sv[r] = (kSum && r >= rows) ? 0u : X[u];
+        }
+        const int64_t icn = ic + ne, jcn = jc + rows;
+        if (icn + jcn < sh.d1) fetch(icn, jcn);
+
+        // Lane l owns the ends at positions (16 l, 16 l + 16] (lane 0 also
+        // those at 0): its first end is the first end whose owner is >= l.
+        sf[lane] = ne;
+        wave_lds_sync();
+        for (int k = lane; k < ne; k += 64) {
+            const uint32_t e = se[k];
+            const int o = e == 0 ? 0 : (int)((e - 1) / V);
+            int po = -1;
+            if (k > 0) {
+                const uint32_t pe = se[k - 1];
+                po = pe == 0 ? 0 : (int)((pe - 1) / V);
+            }
+            if (o != po) sf[o] = k;
+        }
+        wave_lds_sync();
+        int a_lo = sf[lane];
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = (int)lane_get((uint32_t)a_lo, (lane + o) & 63);
+            if (lane + o < 64) a_lo = y < a_lo ? y : a_lo;
+        }
+        int a_hi = (int)lane_get((uint32_t)a_lo, (lane + 1) & 63);
+        if (lane == 63) a_hi = ne;
+
+        uint32_t x[V];
+#pragma unroll
+        for (int t = 0; t < V; t += 4) {
+            const uint4 q = *reinterpret_cast<const uint4 *>(&sv[lane * V + t]);
+            x[t] = q.x;
+            x[t + 1] = q.y;
+            x[t + 2] = q.z;
+            x[t + 3] = q.w;
+        }
+
+        // Walk the lane's elements in order.
+        acc_t acc = R::id(), hacc = R::id();
+        bool hh = false;
+        int k = a_lo;
+        uint32_t next_end = k < a_hi ? se[k] : kInf;
+        const uint32_t relbase = (uint32_t)(jc - sh.j0);
+        const uint32_t r0 = (uint32_t)(lane * V);
+
+        auto finish = [&]() __attribute__((always_inline)) {
+            if (!hh) {
+                hh = true;
+                hacc = acc;
+            } else {
+                const uint64_t bits = R::to_slot(acc);
+                sv[k] = (uint32_t)bits;
+                if (kWide) se[k] = (uint32_t)(bits >> 32);
+            }
+            acc = R::id();
+            ++k;
+            next_end = k < a_hi ? se[k] : kInf;
+        };
+
+#pragma unroll
+        for (int t = 0; t < V; ++t) {
+            const uint32_t r = r0 + t;
+            while (next_end <= r) finish();
+            if constexpr (kSum) {
+                acc = R::comb(acc, R::lift(x[t], 0u));
+            } else {
+                if ((int)r < rows) acc = R::comb(acc, R::lift(x[t], relbase + r));
+            }
+        }
+        while (k < a_hi) finish();
+
+        // Segmented scan over the lanes; the chunk carry enters at lane 0.
+        bool flag = hh;
+        acc_t xs = (lane == 0 && !flag) ? R::comb(carry, acc) : acc;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int src = (lane - o) & 63;
+            const bool pf = lane_get(flag, src);
+            const acc_t px = lane_get(xs, src);
+            if (lane >= o) {
+                if (!flag) xs = R::comb(px, xs);
+                flag = flag || pf;
+            }
+        }
+        acc_t ex = lane_get(xs, (lane - 1) & 63);
+        if (lane == 0) ex = carry;
+        if (hh) {
+            const acc_t hv = R::comb(ex, hacc);
+            if (sh.split_head && ic + a_lo == sh.i0) {
+                a.hval[wave] = R::to_slot(hv);
+            } else {
+                const uint64_t bits = R::to_slot(hv);
+                sv[a_lo] = (uint32_t)bits;
+                if (kWide) se[a_lo] = (uint32_t)(bits >> 32);
+            }
+        }
+        carry = lane_get(xs, 63);
+        wave_lds_sync();
+
+        // Coalesced stores of every segment finished in this chunk.
+        for (int q = lane; q < ne; q += 64) {
+            const int64_t seg = ic + q;
+            if (sh.split_head && seg == sh.i0) continue;
+            const uint64_t bits = (uint64_t)sv[q] | (kWide ? (uint64_t)se[q] << 32 : 0ull);
+            const acc_t v = R::from_slot(bits);
+            store_final<DT, OP, 1>(a, seg, 0, &v, base);
+        }
+        ic = icn;
+        jc = jcn;
+        wave_lds_sync();
+    }
     if (lane == 0) {
-        a.hdr[wave * 3 + 0] = split_head ? i0 : -1;
-        a.hdr[wave * 3 + 1] = has_tail ? i1 : -1;
-        a.hdr[wave * 3 + 2] = base;
+        if (sh.has_tail) a.tval[wave] = R::to_slot(carry);
+        write_header(a, wave, sh);
     }
 }
 
@@ -453,16 +758,11 @@ __global__ __launch_bounds__(256) void seg_reduce_pass2(const KArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t w = (int64_t)blockIdx.x * 4 + wid;
     if (w >= a.NW) return;
-    const int64_t s = a.hdr[w * 3 + 0];
+    const int64_t s = a.hdr[w * 4 + 0];
+    const int64_t first = a.hdr[w * 4 + 3];  // share holding the segment's first row
     if (s < 0) return;
-
-    const int64_t *off = a.offsets;
-    const int64_t o0 = off[0];
-    const int64_t T = (off[a.S] - o0) + a.S;
-    const int64_t D = (T + a.NW - 1) / a.NW;
-    const int64_t first = (off[s] - o0 + s) / D;  // share holding the segment's first row
     int64_t len = 0;
-    if constexpr (OP == OP_MEAN) len = off[s + 1] - off[s];
+    if constexpr (OP == OP_MEAN) len = a.offsets[s + 1] - a.offsets[s];
 
     int fp = 1;
     while (fp < a.F && fp < 64) fp <<= 1;
@@ -481,19 +781,19 @@ __global__ __launch_bounds__(256) void seg_reduce_pass2(const KArgs a) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     q[u] = a.tval[(t + u * cols) * a.F + f];
-                    bs[u] = a.hdr[(t + u * cols) * 3 + 2];
+                    bs[u] = a.hdr[(t + u * cols) * 4 + 2];
                 }
 #pragma unroll
                 for (int u = 0; u < 4; ++u) acc = P::comb(acc, P::from(q[u], bs[u]));
             }
-            for (; t < w; t += cols) acc = P::comb(acc, P::from(a.tval[t * a.F + f], a.hdr[t * 3 + 2]));
+            for (; t < w; t += cols) acc = P::comb(acc, P::from(a.tval[t * a.F + f], a.hdr[t * 4 + 2]));
         }
         for (int m = fp; m < 64; m <<= 1) {
             const P o = acc.get(lane ^ m);
             acc = (lane & m) ? P::comb(o, acc) : P::comb(acc, o);
         }
         if (cc == 0 && valid) {
-            acc = P::comb(acc, P::from(a.hval[w * a.F + f], a.hdr[w * 3 + 2]));
+            acc = P::comb(acc, P::from(a.hval[w * a.F + f], a.hdr[w * 4 + 2]));
             uint32_t ob;
             int64_t ab;
             acc.bits(len, ob, ab);
@@ -505,84 +805,104 @@ __global__ __launch_bounds__(256) void seg_reduce_pass2(const KArgs a) {
 
 // ------------------------------------------------------------------ host side
 
-enum Variant { VAR_FLAT, VAR_VEC4, VAR_VEC1 };
+constexpr int64_t kFallbackShares = 8192;
+constexpr int64_t kMaxFeat = int64_t(1) << 24;
 
-struct Plan {
-    Variant var;
-    int lanes;  // lanes per row (VEC4)
-    int64_t shares;
-};
 
-constexpr int64_t kDefaultShares = 8192;
+// Waves of `kernel` that fit on the device at once (CUs x resident
+// workgroups x 4): one share per resident wave, so every wave streams its
+// share from start to end without a second generation of workgroups.
+static int64_t resident_waves(const void *kernel) {
+    static std::mutex mu;
+    static std::map<std::pair<int, const void *>, int64_t> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return kFallbackShares;
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find({dev, kernel});
+    if (it != cache.end()) return it->second;
+    int cus = 0, blocks = 0;
+    int64_t w = kFallbackShares;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, 256, 0) == hipSuccess && cus > 0 &&
+        blocks > 0)
+        w = (int64_t)cus * blocks * 4;
+    (void)hipGetLastError();
+    cache[{dev, kernel}] = w;
+    return w;
+}
 
-static int lanes_for_vec4(int64_t feat) {
-    int64_t q = feat / 4, l = 1;
-    while (l < q && l < 64) l <<= 1;
+static int lanes_for(int64_t feat) {
+    int64_t l = 2;
+    while (l < feat && l < 64) l <<= 1;
     return (int)l;
 }
 
-static Plan make_plan(const void *values, int64_t feat, const void *out, const int64_t *arg) {
-    Plan p;
-    if (feat == 1) {
-        p.var = VAR_FLAT;
-        p.lanes = 1;
-    } else if (feat % 4 == 0 && aligned(values, 16) && aligned(out, 16) && (!arg || aligned(arg, 16))) {
-        p.var = VAR_VEC4;
-        p.lanes = lanes_for_vec4(feat);
-    } else {
-        p.var = VAR_VEC1;
-        p.lanes = 64;
+template <int DT, int OP>
+static const void *pick_kernel(int64_t feat) {
+    if (feat == 1) return reinterpret_cast<const void *>(&seg_reduce_flat<DT, OP>);
+    switch (lanes_for(feat)) {
+    case 2: return reinterpret_cast<const void *>(&seg_reduce_rows<DT, OP, 2, 16>);
+    case 4: return reinterpret_cast<const void *>(&seg_reduce_rows<DT, OP, 4, 16>);
+    case 8: return reinterpret_cast<const void *>(&seg_reduce_rows<DT, OP, 8, 16>);
+    case 16: return reinterpret_cast<const void *>(&seg_reduce_rows<DT, OP, 16, 16>);
+    case 32: return reinterpret_cast<const void *>(&seg_reduce_rows<DT, OP, 32, 32>);
+    default: return reinterpret_cast<const void *>(&seg_reduce_rows<DT, OP, 64, 32>);
     }
-    const int64_t o = shares_override();
-    p.shares = ((o > 0 ? o : kDefaultShares) + 3) / 4 * 4;  // whole workgroups of 4 waves
-    return p;
 }
 
-template <int DT, int OP, int VEC, int L, int V, bool STAGE>
-static void launch_pass1(const KArgs &k, int64_t blocks, hipStream_t st) {
-    hipLaunchKernelGGL((seg_reduce_pass1<DT, OP, VEC, L, V, STAGE>), dim3((unsigned)blocks), dim3(256), 0, st, k);
+// Shares per call: one per wave that fits on the device at once.
+static int64_t shares_for(const void *kernel) {
+    const int64_t o = shares_override();
+    return ((o > 0 ? o : resident_waves(kernel)) + 3) / 4 * 4;  // whole workgroups of 4 waves
 }
 
 template <int DT, int OP>
-static int run(const Plan &p, const KArgs &k, hipStream_t st) {
-    const int64_t blocks = p.shares / 4;
+static int run(KArgs k, hipStream_t st) {
+    const void *kernel = pick_kernel<DT, OP>(k.F);
+    const int64_t nw = shares_for(kernel);
+    const size_t hdr_bytes = (size_t)nw * 4 * sizeof(int64_t);
+    const size_t val_bytes = (size_t)nw * (size_t)k.F * sizeof(uint64_t);
+    void *scratch = nullptr;
+    int rc = scratch_alloc(&scratch, hdr_bytes + 2 * val_bytes, st);
+    if (rc != SEGRED_OK) return rc;
+    char *p = static_cast<char *>(scratch);
+    k.NW = nw;
+    k.hdr = reinterpret_cast<int64_t *>(p);
+    k.hval = reinterpret_cast<uint64_t *>(p + hdr_bytes);
+    k.tval = k.hval + (size_t)nw * (size_t)k.F;
+
+    const dim3 grid((unsigned)(nw / 4)), block(256);
     const int slot = timing_begin(st);
-    switch (p.var) {
-    case VAR_FLAT: launch_pass1<DT, OP, 1, 1, 16, true>(k, blocks, st); break;
-    case VAR_VEC1: launch_pass1<DT, OP, 1, 64, 32, false>(k, blocks, st); break;
-    case VAR_VEC4:
-        switch (p.lanes) {
-        case 1: launch_pass1<DT, OP, 4, 1, 8, false>(k, blocks, st); break;
-        case 2: launch_pass1<DT, OP, 4, 2, 8, false>(k, blocks, st); break;
-        case 4: launch_pass1<DT, OP, 4, 4, 8, false>(k, blocks, st); break;
-        case 8: launch_pass1<DT, OP, 4, 8, 8, false>(k, blocks, st); break;
-        case 16: launch_pass1<DT, OP, 4, 16, 8, false>(k, blocks, st); break;
-        case 32: launch_pass1<DT, OP, 4, 32, 8, false>(k, blocks, st); break;
-        default: launch_pass1<DT, OP, 4, 64, 8, false>(k, blocks, st); break;
-        }
-        break;
-    }
+    void *params[] = {&k};
+    hipError_t e = hipLaunchKernel(kernel, grid, block, params, 0, st);
     timing_end(slot, st);
-    if (hipGetLastError() != hipSuccess) return SEGRED_ERR_HIP;
-    hipLaunchKernelGGL((seg_reduce_pass2<DT, OP>), dim3((unsigned)blocks), dim3(256), 0, st, k);
-    if (hipGetLastError() != hipSuccess) return SEGRED_ERR_HIP;
-    return SEGRED_OK;
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL((seg_reduce_pass2<DT, OP>), grid, block, 0, st, k);
+        e = hipGetLastError();
+    }
+    scratch_free(scratch, st);
+    return e == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
 }
 
-static int dispatch(int32_t dtype, int32_t op, const Plan &p, const KArgs &k, hipStream_t st) {
+static int dispatch(int32_t dtype, int32_t op, const KArgs &k, hipStream_t st) {
     switch (dtype * 4 + op) {
-    case DT_U32 * 4 + OP_SUM: return run<DT_U32, OP_SUM>(p, k, st);
-    case DT_U32 * 4 + OP_MIN: return run<DT_U32, OP_MIN>(p, k, st);
-    case DT_U32 * 4 + OP_MAX: return run<DT_U32, OP_MAX>(p, k, st);
-    case DT_I32 * 4 + OP_SUM: return run<DT_I32, OP_SUM>(p, k, st);
-    case DT_I32 * 4 + OP_MIN: return run<DT_I32, OP_MIN>(p, k, st);
-    case DT_I32 * 4 + OP_MAX: return run<DT_I32, OP_MAX>(p, k, st);
-    case DT_F32 * 4 + OP_SUM: return run<DT_F32, OP_SUM>(p, k, st);
-    case DT_F32 * 4 + OP_MIN: return run<DT_F32, OP_MIN>(p, k, st);
-    case DT_F32 * 4 + OP_MAX: return run<DT_F32, OP_MAX>(p, k, st);
-    case DT_F32 * 4 + OP_MEAN: return run<DT_F32, OP_MEAN>(p, k, st);
+    case DT_U32 * 4 + OP_SUM: return run<DT_U32, OP_SUM>(k, st);
+    case DT_U32 * 4 + OP_MIN: return run<DT_U32, OP_MIN>(k, st);
+    case DT_U32 * 4 + OP_MAX: return run<DT_U32, OP_MAX>(k, st);
+    case DT_I32 * 4 + OP_SUM: return run<DT_I32, OP_SUM>(k, st);
+    case DT_I32 * 4 + OP_MIN: return run<DT_I32, OP_MIN>(k, st);
+    case DT_I32 * 4 + OP_MAX: return run<DT_I32, OP_MAX>(k, st);
+    case DT_F32 * 4 + OP_SUM: return run<DT_F32, OP_SUM>(k, st);
+    case DT_F32 * 4 + OP_MIN: return run<DT_F32, OP_MIN>(k, st);
+    case DT_F32 * 4 + OP_MAX: return run<DT_F32, OP_MAX>(k, st);
+    case DT_F32 * 4 + OP_MEAN: return run<DT_F32, OP_MEAN>(k, st);
     default: return SEGRED_ERR_UNSUPPORTED;
     }
+}
+
+template <int DT, int OP>
+static int64_t shares_of(int64_t feat) {
+    return shares_for(pick_kernel<DT, OP>(feat));
 }
 
 }  // namespace segred
@@ -590,11 +910,20 @@ static int dispatch(int32_t dtype, int32_t op, const Plan &p, const KArgs &k, hi
 using namespace segred;
 
 extern "C" int64_t segred_get_shares(int32_t dtype, int32_t op, int64_t feat) {
-    (void)dtype;
-    (void)op;
-    (void)feat;
-    const int64_t o = shares_override();
-    return ((o > 0 ? o : kDefaultShares) + 3) / 4 * 4;
+    if (feat < 1) return -1;
+    switch (dtype * 4 + op) {
+    case DT_U32 * 4 + OP_SUM: return shares_of<DT_U32, OP_SUM>(feat);
+    case DT_U32 * 4 + OP_MIN: return shares_of<DT_U32, OP_MIN>(feat);
+    case DT_U32 * 4 + OP_MAX: return shares_of<DT_U32, OP_MAX>(feat);
+    case DT_I32 * 4 + OP_SUM: return shares_of<DT_I32, OP_SUM>(feat);
+    case DT_I32 * 4 + OP_MIN: return shares_of<DT_I32, OP_MIN>(feat);
+    case DT_I32 * 4 + OP_MAX: return shares_of<DT_I32, OP_MAX>(feat);
+    case DT_F32 * 4 + OP_SUM: return shares_of<DT_F32, OP_SUM>(feat);
+    case DT_F32 * 4 + OP_MIN: return shares_of<DT_F32, OP_MIN>(feat);
+    case DT_F32 * 4 + OP_MAX: return shares_of<DT_F32, OP_MAX>(feat);
+    case DT_F32 * 4 + OP_MEAN: return shares_of<DT_F32, OP_MEAN>(feat);
+    default: return -1;
+    }
 }
 
 extern "C" int segred_reduce(const void *values, int32_t dtype, int64_t feat, const int64_t *offsets,
@@ -604,33 +933,19 @@ extern "C" int segred_reduce(const void *values, int32_t dtype, int64_t feat, co
         op > SEGRED_MEAN)
         return SEGRED_ERR_INVALID_ARGUMENT;
     if (op == SEGRED_MEAN && dtype != SEGRED_F32) return SEGRED_ERR_UNSUPPORTED;
+    if (feat > kMaxFeat) return SEGRED_ERR_UNSUPPORTED;  // 32-bit in-chunk byte offsets
     if (num_segments == 0) return SEGRED_OK;
     if (!values || !offsets || !out) return SEGRED_ERR_INVALID_ARGUMENT;
     if (!aligned(values, 4) || !aligned(out, 4) || !aligned(offsets, 8) || (arg_out && !aligned(arg_out, 8)))
         return SEGRED_ERR_INVALID_ARGUMENT;
     if (op == SEGRED_SUM || op == SEGRED_MEAN) arg_out = nullptr;
 
-    const Plan plan = make_plan(values, feat, out, arg_out);
-    const int64_t nw = plan.shares;
-    const size_t hdr_bytes = (size_t)nw * 3 * sizeof(int64_t);
-    const size_t val_bytes = (size_t)nw * (size_t)feat * sizeof(uint64_t);
-    void *scratch = nullptr;
-    int rc = scratch_alloc(&scratch, hdr_bytes + 2 * val_bytes, stream);
-    if (rc != SEGRED_OK) return rc;
-
-    KArgs k;
+    KArgs k{};
     k.values = static_cast<const uint32_t *>(values);
     k.offsets = offsets;
     k.S = num_segments;
     k.F = feat;
-    k.NW = nw;
     k.out = static_cast<uint32_t *>(out);
     k.arg = arg_out;
-    k.hdr = static_cast<int64_t *>(scratch);
-    k.hval = reinterpret_cast<uint64_t *>(static_cast<char *>(scratch) + hdr_bytes);
-    k.tval = k.hval + (size_t)nw * (size_t)feat;
-
-    rc = dispatch(dtype, op, plan, k, stream);
-    scratch_free(scratch, stream);
-    return rc;
+    return dispatch(dtype, op, k, stream);
 }

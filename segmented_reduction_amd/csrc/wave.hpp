@@ -53,4 +53,16 @@ __device__ __forceinline__ int64_t readfirst(int64_t v) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Raw buffer access: a descriptor over [base, base + bytes); a load whose
+// byte offset (lane offset + scalar offset) is at or past `bytes` returns 0
+// without touching memory, so a descriptor limited to the valid part of an
+// array makes clamping unnecessary.  Descriptor word 3 is the gfx9-family
+// raw 32-bit layout.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint32_t ld32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+
 }  // namespace segred

@@ -60,6 +60,7 @@ FAKE = 0x10000  # a non-null, aligned host value; never dereferenced (rejected o
     ((FAKE, 2, 1, FAKE, 4, 4, FAKE, None), 1),         # op out of range
     ((FAKE, 0, 1, FAKE, 4, 3, FAKE, None), 2),         # MEAN of u32
     ((FAKE, 1, 1, FAKE, 4, 3, FAKE, None), 2),         # MEAN of i32
+    ((FAKE, 2, 2 ** 24 + 1, FAKE, 4, 0, FAKE, None), 2),  # more features than the 32-bit chunk offsets allow
     ((None, 2, 1, FAKE, 4, 0, FAKE, None), 1),         # null values
     ((FAKE, 2, 1, None, 4, 0, FAKE, None), 1),         # null offsets
     ((FAKE, 2, 1, FAKE, 4, 0, None, None), 1),         # null out
@@ -106,9 +107,10 @@ def test_share_knob_range():
 def test_timing_read_without_launches():
     lib = _lib()
     ms, n = ctypes.c_double(-1.0), ctypes.c_int64(-1)
-    assert lib.segred_timing_read(ctypes.byref(ms), ctypes.byref(n)) == 0
+    assert lib.segred_timing_read(ctypes.byref(ms), ctypes.byref(n), None, 0) == 0
     assert n.value == 0 and ms.value == 0.0
-    assert lib.segred_timing_read(None, None) == 1
+    assert lib.segred_timing_read(None, None, None, 0) == 1
+    assert lib.segred_timing_read(ctypes.byref(ms), ctypes.byref(n), None, 4) == 1
 
 
 def test_binding_refuses_cpu_tensors():
