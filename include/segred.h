@@ -6,9 +6,13 @@
  * call is asynchronous and ordered on the HIP stream it is given (0 is the
  * null stream): a non-error return means the work was enqueued; faults during
  * the work surface at the caller's next synchronisation.  Inputs and outputs
- * are owned by the caller; scratch memory is owned by the library, taken from
- * a stream-ordered pool and returned on the same stream.  No call throws.
- * Calls on distinct streams may run concurrently.
+ * are owned by the caller; scratch memory is owned by the library: each
+ * (device, stream) keeps one cached scratch buffer of up to 256 MiB that
+ * later calls on that stream reuse (larger needs, and streams past the 64th,
+ * take a stream-ordered pool allocation freed on the same stream).  The
+ * cached buffers are held until the process ends.  No call throws.  Calls on
+ * distinct streams may run concurrently.  A stream must have no call of this
+ * library in flight when it is destroyed (synchronise it first).
  */
 #ifndef SEGRED_H
 #define SEGRED_H
@@ -135,8 +139,9 @@ int64_t segred_get_shares(int32_t dtype, int32_t op, int64_t feat);
 
 /*
  * Kernel timing (instrumentation for benchmarks).  While enabled, every
- * segred_reduce call records a pair of HIP events on its stream around its
- * streaming (first) kernel.  segred_timing_read waits for the recorded
+ * segred_reduce call launches its streaming (first) kernel with a pair of
+ * HIP events that the runtime stamps with that kernel's own start and end
+ * (hipExtLaunchKernel), so a duration is the kernel's execution time.  segred_timing_read waits for the recorded
  * events, returns the summed duration in milliseconds and the number of
  * timed launches, writes the first `capacity` per-launch durations (ms, in
  * launch order) to the host array `each_ms` (may be NULL when capacity is

@@ -1,6 +1,9 @@
 // api.hip -- status strings, the scratch pool, launch timing and the share
 // knob of the segmented-reduction library.
+#include <algorithm>
 #include <atomic>
+#include <map>
+#include <memory>
 #include <mutex>
 #include <vector>
 
@@ -44,11 +47,16 @@ Timing g_timing;
 
 std::atomic<int64_t> g_shares{0};
 
-}  // namespace
+struct CacheEntry {
+    std::mutex mu;
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+// keyed by (device, stream handle); entries live until the process ends
+std::map<std::pair<int, uintptr_t>, std::unique_ptr<CacheEntry>> g_cache;
 
-int scratch_alloc(void **ptr, size_t bytes, hipStream_t stream) {
+int pool_alloc(void **ptr, size_t bytes, hipStream_t stream) {
     *ptr = nullptr;
-    if (bytes == 0) return SEGRED_OK;
     hipMemPool_t pool = pool_for_current_device();
     if (!pool) return SEGRED_ERR_HIP;
     hipError_t e = hipMallocFromPoolAsync(ptr, bytes, pool, stream);
@@ -59,21 +67,61 @@ int scratch_alloc(void **ptr, size_t bytes, hipStream_t stream) {
     return e == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
 }
 
-void scratch_free(void *ptr, hipStream_t stream) {
-    if (ptr) (void)hipFreeAsync(ptr, stream);
+CacheEntry *cache_entry(hipStream_t stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    const uintptr_t key = reinterpret_cast<uintptr_t>(stream);
+    std::lock_guard<std::mutex> lk(g_pool_mu);
+    auto it = g_cache.find({dev, key});
+    if (it != g_cache.end()) return it->second.get();
+    if ((int)g_cache.size() >= kScratchCacheEntries) return nullptr;
+    auto &slot = g_cache[{dev, key}];
+    slot = std::make_unique<CacheEntry>();
+    return slot.get();
+}
+
+}  // namespace
+
+ScratchLease::~ScratchLease() {
+    if (owned_) (void)hipFreeAsync(owned_, stream_);
+}
+
+int scratch_acquire(ScratchLease &lease, size_t bytes, hipStream_t stream) {
+    lease.stream_ = stream;
+    if (bytes == 0) return SEGRED_OK;
+    CacheEntry *e = bytes <= kScratchCacheBytes ? cache_entry(stream) : nullptr;
+    if (!e) {
+        int rc = pool_alloc(&lease.owned_, bytes, stream);
+        lease.ptr = lease.owned_;
+        return rc;
+    }
+    lease.lock_ = std::unique_lock<std::mutex>(e->mu);
+    if (e->bytes < bytes) {
+        // grow geometrically (1 MiB granules) so a ramp of sizes reallocates rarely
+        size_t want = std::max(bytes, std::min(2 * e->bytes, kScratchCacheBytes));
+        want = (want + (size_t(1) << 20) - 1) & ~((size_t(1) << 20) - 1);
+        void *p = nullptr;
+        int rc = pool_alloc(&p, want, stream);
+        if (rc != SEGRED_OK) return rc;
+        if (e->ptr) (void)hipFreeAsync(e->ptr, stream);
+        e->ptr = p;
+        e->bytes = want;
+    }
+    lease.ptr = e->ptr;
+    return SEGRED_OK;
 }
 
 bool timing_on() { return g_timing.on; }
 
-int timing_begin(hipStream_t stream) {
-    if (!g_timing.on || g_timing.used >= kMaxTimed) return -1;
-    int slot = g_timing.used++;
-    if (hipEventRecord(g_timing.ev[2 * slot], stream) != hipSuccess) return -1;
-    return slot;
-}
-
-void timing_end(int slot, hipStream_t stream) {
-    if (slot >= 0) (void)hipEventRecord(g_timing.ev[2 * slot + 1], stream);
+void timing_events(hipEvent_t *start, hipEvent_t *stop) {
+    *start = *stop = nullptr;
+    if (!g_timing.on || g_timing.used >= kMaxTimed) return;
+    const int slot = g_timing.used++;
+    *start = g_timing.ev[2 * slot];
+    *stop = g_timing.ev[2 * slot + 1];
 }
 
 int64_t shares_override() { return g_shares.load(std::memory_order_relaxed); }

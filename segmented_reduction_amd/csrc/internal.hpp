@@ -3,21 +3,50 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
+
+#include <mutex>
 
 #include "segred.h"
 
 namespace segred {
 
-// Stream-ordered scratch from a per-device pool that keeps its memory
-// (release threshold = max), so steady-state calls do not hit the driver.
-int scratch_alloc(void **ptr, size_t bytes, hipStream_t stream);
-void scratch_free(void *ptr, hipStream_t stream);
+// Scratch for one call, owned by the library.  Each (device, stream) pair
+// keeps one cached buffer that later calls on the same stream reuse: calls
+// on one stream run in order, so the reuse is safe, and a cached call costs
+// neither an allocation nor a free (each stream-ordered pool operation adds
+// tens of microseconds of host time and an idle gap on the GPU).  The buffer
+// grows stream-ordered on demand.  Requests above kScratchCacheBytes, or
+// beyond kScratchCacheEntries streams per process, take a stream-ordered
+// allocation from a per-device pool that keeps its memory (release
+// threshold = max) and free it after the call.  The lease holds the
+// entry's lock until it is destroyed, after the call's launches are queued,
+// so two host threads sharing a stream cannot swap the buffer under each
+// other.  Entries are keyed by the stream handle: a stream must have no call
+// in flight when it is destroyed, or a new stream that receives the same
+// handle could reuse the buffer while the old calls still run.
+constexpr size_t kScratchCacheBytes = size_t(256) << 20;
+constexpr int kScratchCacheEntries = 64;
 
-// Launch timing around the streaming kernel (segred_timing_enable).
+struct ScratchLease {
+    void *ptr = nullptr;
+    ScratchLease() = default;
+    ScratchLease(const ScratchLease &) = delete;
+    ScratchLease &operator=(const ScratchLease &) = delete;
+    ~ScratchLease();
+
+    void *owned_ = nullptr;  // per-call pool allocation, freed on `stream_`
+    hipStream_t stream_ = nullptr;
+    std::unique_lock<std::mutex> lock_;
+};
+int scratch_acquire(ScratchLease &lease, size_t bytes, hipStream_t stream);
+
+// Launch timing of the streaming kernel (segred_timing_enable): the next
+// pair of events to hand to hipExtLaunchKernel, which stamps them with the
+// kernel's own start and end; both null when timing is off or the ring is full.
 bool timing_on();
-int timing_begin(hipStream_t stream);  // returns a slot id or -1
-void timing_end(int slot, hipStream_t stream);
+void timing_events(hipEvent_t *start, hipEvent_t *stop);
 
 // Process-wide share override (0 = default).
 int64_t shares_override();

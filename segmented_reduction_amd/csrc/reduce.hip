@@ -862,25 +862,24 @@ static int run(KArgs k, hipStream_t st) {
     const int64_t nw = shares_for(kernel);
     const size_t hdr_bytes = (size_t)nw * 4 * sizeof(int64_t);
     const size_t val_bytes = (size_t)nw * (size_t)k.F * sizeof(uint64_t);
-    void *scratch = nullptr;
-    int rc = scratch_alloc(&scratch, hdr_bytes + 2 * val_bytes, st);
+    ScratchLease scratch;
+    int rc = scratch_acquire(scratch, hdr_bytes + 2 * val_bytes, st);
     if (rc != SEGRED_OK) return rc;
-    char *p = static_cast<char *>(scratch);
+    char *p = static_cast<char *>(scratch.ptr);
     k.NW = nw;
     k.hdr = reinterpret_cast<int64_t *>(p);
     k.hval = reinterpret_cast<uint64_t *>(p + hdr_bytes);
     k.tval = k.hval + (size_t)nw * (size_t)k.F;
 
     const dim3 grid((unsigned)(nw / 4)), block(256);
-    const int slot = timing_begin(st);
+    hipEvent_t t0, t1;
+    timing_events(&t0, &t1);
     void *params[] = {&k};
-    hipError_t e = hipLaunchKernel(kernel, grid, block, params, 0, st);
-    timing_end(slot, st);
+    hipError_t e = hipExtLaunchKernel(kernel, grid, block, params, 0, st, t0, t1, 0);
     if (e == hipSuccess) {
         hipLaunchKernelGGL((seg_reduce_pass2<DT, OP>), grid, block, 0, st, k);
         e = hipGetLastError();
     }
-    scratch_free(scratch, st);
     return e == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
 }
 

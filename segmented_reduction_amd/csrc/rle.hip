@@ -214,10 +214,10 @@ extern "C" int segred_offsets_from_rle(const uint32_t *sorted_keys, int64_t n, u
         return SEGRED_ERR_INVALID_ARGUMENT;
 
     const int64_t tiles = (n + kRleTile - 1) / kRleTile;
-    void *scratch = nullptr;
-    int rc = scratch_alloc(&scratch, (size_t)tiles * 4 * sizeof(int64_t), stream);
+    ScratchLease scratch;
+    int rc = scratch_acquire(scratch, (size_t)tiles * 4 * sizeof(int64_t), stream);
     if (rc != SEGRED_OK) return rc;
-    int64_t *tcount = static_cast<int64_t *>(scratch);
+    int64_t *tcount = static_cast<int64_t *>(scratch.ptr);
     int64_t *tfirst = tcount + tiles;
     int64_t *tbase = tfirst + tiles;
     int64_t *tnext = tbase + tiles;
@@ -230,7 +230,5 @@ extern "C" int segred_offsets_from_rle(const uint32_t *sorted_keys, int64_t n, u
     if (tiles > 0)
         hipLaunchKernelGGL(rle_materialize, dim3((unsigned)tiles), dim3(kRleThreads), 0, stream, sorted_keys, n,
                            tbase, tnext, values, lengths, offsets);
-    rc = hipGetLastError() == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
-    scratch_free(scratch, stream);
-    return rc;
+    return hipGetLastError() == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
 }
