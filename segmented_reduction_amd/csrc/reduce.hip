@@ -143,9 +143,8 @@ __device__ __forceinline__ void final_bits(typename Red<DT, OP>::acc_t acc, int6
 
 template <int DT, int OP, int VEC>
 __device__ __forceinline__ void store_final(const KArgs &a, int64_t seg, int64_t f0,
-                                            const typename Red<DT, OP>::acc_t *acc, int64_t base) {
-    int64_t len = 0;
-    if constexpr (OP == OP_MEAN) len = a.offsets[seg + 1] - a.offsets[seg];
+                                            const typename Red<DT, OP>::acc_t *acc, int64_t base,
+                                            int64_t len /* rows of the segment, used by MEAN */) {
     uint32_t ob[VEC];
     int64_t ab[VEC];
 #pragma unroll
@@ -324,6 +323,9 @@ __global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
         // work.
         acc_t open = R::id();
         bool open_spread = false;  // open partials are in several groups
+        // MEAN: first row (relative to offsets[0]) of the open segment, so a
+        // finished segment's length comes from the ends already in LDS.
+        int64_t open_start = sh.first_row;
 
         // Fetch: a chunk's first 64 segment ends (index clamped into the
         // array, loaded unconditionally: a load under a branch would be
@@ -412,9 +414,13 @@ __global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
             // Walk the group's rows in order (wave-uniform control for G = 1).
             acc_t acc = R::id(), hacc = R::id();
             bool hh = false;  // this group finished at least one segment
-            int64_t hseg = 0;
+            int64_t hseg = 0, hlen = 0;
             int k = a_lo;
             int64_t seg = ic + a_lo;
+            int64_t seg_start = open_start;  // MEAN only
+            if constexpr (OP == OP_MEAN && G > 1) {
+                if (a_lo > 0) seg_start = jc + (int64_t)se[a_lo - 1];
+            }
             auto end_at = [&](int kk) __attribute__((always_inline)) -> uint32_t {
                 if (kk >= a_hi) return kInf;
                 const uint32_t e = se[kk];
@@ -423,12 +429,19 @@ __global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
             uint32_t next_end = end_at(k);
 
             auto finish = [&]() __attribute__((always_inline)) {
+                int64_t len = 0;
+                if constexpr (OP == OP_MEAN) {
+                    const int64_t e_abs = jc + (int64_t)next_end;
+                    len = e_abs - seg_start;
+                    seg_start = e_abs;
+                }
                 if (!hh) {
                     hh = true;
                     hseg = seg;
                     hacc = acc;
+                    hlen = len;
                 } else if (fvalid) {
-                    store_final<DT, OP, 1>(a, seg, f, &acc, base);
+                    store_final<DT, OP, 1>(a, seg, f, &acc, base, len);
                 }
                 acc = R::id();
                 ++seg;
@@ -467,7 +480,7 @@ __global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
             if (hh && fvalid) {
                 const acc_t hv = R::comb(ex, hacc);
                 if (sh.split_head && hseg == sh.i0) a.hval[wave * a.F + f] = R::to_slot(hv);
-                else store_final<DT, OP, 1>(a, hseg, f, &hv, base);
+                else store_final<DT, OP, 1>(a, hseg, f, &hv, base, hlen);
             }
             // The open segment after this chunk: group G-1's inclusive value,
             // parked in group 0.
@@ -478,6 +491,7 @@ __global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
                 open = xs;
             }
             open_spread = false;
+            if constexpr (OP == OP_MEAN) open_start = jc + (int64_t)__builtin_amdgcn_readfirstlane(se[ne - 1]);
 
             ic = icn;
             jc = jcn;
@@ -697,7 +711,9 @@ __global__ __launch_bounds__(256) void seg_reduce_flat(const KArgs a) {
             if (sh.split_head && seg == sh.i0) continue;
             const uint64_t bits = (uint64_t)sv[q] | (kWide ? (uint64_t)se[q] << 32 : 0ull);
             const acc_t v = R::from_slot(bits);
-            store_final<DT, OP, 1>(a, seg, 0, &v, base);
+            int64_t len = 0;
+            if constexpr (OP == OP_MEAN) len = off[seg + 1] - off[seg];
+            store_final<DT, OP, 1>(a, seg, 0, &v, base, len);
         }
         ic = icn;
         jc = jcn;
