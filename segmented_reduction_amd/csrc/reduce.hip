@@ -66,7 +66,7 @@ template <int DT>
 __device__ __forceinline__ uint32_t okey(uint32_t b) {
     if constexpr (DT == DT_U32) return b;
     else if constexpr (DT == DT_I32) return b ^ 0x80000000u;
-    else return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    else return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);  // ~b if negative, else b | sign
 }
 template <int DT>
 __device__ __forceinline__ uint32_t okey_inv(uint32_t k) {
@@ -194,7 +194,8 @@ struct Share {
 };
 
 __device__ __forceinline__ Share find_share(const int64_t *off, int64_t S, int64_t NW, int64_t wave, int lane,
-                                            int64_t *s_probe /* LDS [256], workgroup-wide */) {
+                                            int64_t *s_probe /* LDS [256], workgroup-wide */,
+                                            int64_t min_share = 1) {
     const int tid = threadIdx.x;
     const int64_t step1 = (S + 254) / 255;  // probes k * step1, k < 255, and S
     const int64_t p = tid == 255 ? S : min((int64_t)tid * step1, S);
@@ -203,7 +204,9 @@ __device__ __forceinline__ Share find_share(const int64_t *off, int64_t S, int64
 
     const int64_t o0 = s_probe[0];
     const int64_t T = (s_probe[255] - o0) + S;
-    const int64_t D = (T + NW - 1) / NW;
+    // Shares of at least min_share items: small inputs use fewer waves (the
+    // rest get empty shares and only write their header).
+    const int64_t D = max((T + NW - 1) / NW, min_share);
     const int64_t d0 = min(wave * D, T), d1 = min(d0 + D, T);
 
     // round 1 from LDS: the last probe with key <= d bounds i(d) from below,
@@ -512,208 +515,255 @@ __global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
     if (lane == 0) write_header(a, wave, sh);
 }
 
-// Pass 1 for one feature per row (1-D values).  A chunk is 1024 items; its
-// elements are fetched with coalesced loads and staged in LDS, lane l then
-// walks elements [16 l, 16 l + 16) in order.  The next chunk's elements and
-// first 128 ends are fetched while the current chunk is processed.  Finished
-// segments park their result in LDS (slot = end index in the chunk, the
-// element and end arrays are reused for the low and high words) and are
-// stored by one coalesced pass at the end of the chunk.
+// Pass 1 for one feature per row (1-D values).
+//
+// A chunk is up to 2048 elements and up to 256 segment ends.  Its elements
+// arrive with coalesced 16-byte loads and are staged through LDS (an XOR
+// swizzle of 16-byte units keeps both the fill and the per-lane reads free of
+// bank conflicts), so that lane l holds elements [32 l, 32 l + 32).  The
+// chunk's ends become a reset mask per lane (bit t: a segment ends right
+// before element 32 l + t).  Each lane then runs one pass over its 32
+// elements that restarts its accumulator at every reset (a bitwise AND with
+// the sign-extended mask bit, no branches) and leaves the running value at
+// every element in LDS; a segmented scan across the lanes (cross-lane moves)
+// gives every lane the part of its open segment that lies before it.  The
+// result of a segment ending before element p is then the running value at
+// p - 1, plus the carried-in part when the segment began before that lane:
+// one lane per end looks both up and stores the result, so the stores are
+// coalesced.  The next chunk streams into registers while this one is
+// processed.
+//
+// Float sums: a lane's 32 elements and the scan across a chunk's 64 lanes add
+// in float32 (a tree of depth 6 over lane sums of at most 32 terms, so the
+// error stays below 38 * 2^-24 of the sum of magnitudes, well inside
+// 1e-5 * sum|x|); everything that crosses a chunk or share boundary adds in
+// float64.  Min/max work on the packed (key, row code) word; for MIN the word
+// is complemented inside the chunk so that both are a maximum.
+__device__ __forceinline__ int flat_unit(int owner, int c) {
+    return owner * 8 + (c ^ ((owner & 7) ^ ((owner >> 3) & 1)));
+}
+
 template <int DT, int OP>
 __global__ __launch_bounds__(256) void seg_reduce_flat(const KArgs a) {
     using R = Red<DT, OP>;
     using acc_t = typename R::acc_t;
-    constexpr int V = 16;    // elements per lane per chunk
-    constexpr int CH = 64 * V;
-    constexpr int EC = 512;  // segment ends per chunk at most
-    constexpr int NB = 2;    // batches of 64 ends fetched ahead
-    constexpr uint32_t kInf = 0xFFFFFFFFu;
-    constexpr bool kWide = sizeof(acc_t) == 8;
-    constexpr bool kSum = R::kSumF || R::kSumI;
+    constexpr bool kSumF = R::kSumF, kMM = R::kMinMax;
+    constexpr int V = 32, CH = 64 * V, EC = 256, NB = 2;
+    constexpr uint32_t kNone = 0xFFFFFFFFu;
+    // in-chunk value: float for float sums, else the accumulator itself
+    // (min/max in the "maximum" domain)
+    using lacc_t = std::conditional_t<kSumF, float, acc_t>;
+    auto to_max = [](acc_t v) __attribute__((always_inline)) -> acc_t {
+        if constexpr (OP == OP_MIN) return ~v;
+        else return v;
+    };
+    auto widen = [](lacc_t v) __attribute__((always_inline)) -> acc_t {
+        if constexpr (kSumF) return (double)v;
+        else return v;
+    };
+    auto lcomb = [](lacc_t e, lacc_t l) __attribute__((always_inline)) -> lacc_t {
+        if constexpr (kMM) return l > e ? l : e;
+        else return e + l;
+    };
+    auto acomb = [](acc_t e, acc_t l) __attribute__((always_inline)) -> acc_t {
+        if constexpr (kMM) return l > e ? l : e;
+        else return e + l;
+    };
 
-    __shared__ __attribute__((aligned(16))) uint32_t s_vals[4][CH];  // elements, then result low words
-    __shared__ __attribute__((aligned(16))) uint32_t s_ends[4][EC];  // end positions, then result high words
-    __shared__ int s_first[4][64];                                   // first end owned by each lane
+    __shared__ __attribute__((aligned(16))) uint32_t s_x[4][CH];             // elements, then running values (min/max: keys)
+    __shared__ __attribute__((aligned(16))) uint32_t s_y[4][kMM ? CH : 4];   // min/max: running row codes
+    __shared__ uint32_t s_e[4][EC];                                          // end positions in the chunk
+    __shared__ uint32_t s_m[4][64];                                          // reset masks
+    __shared__ uint64_t s_c[4][64];                                          // carried-in part per lane
+    __shared__ int64_t s_probe[256];
 
     const int wid = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * 4 + wid;
     const int64_t *off = a.offsets;
-    __shared__ int64_t s_probe[256];
-    const Share sh = find_share(off, a.S, a.NW, wave, lane, s_probe);
+    const Share sh = find_share(off, a.S, a.NW, wave, lane, s_probe, (int64_t)CH);
     const int64_t o0 = sh.o0, base = sh.o0 + sh.j0;
-    uint32_t *sv = s_vals[wid];
-    uint32_t *se = s_ends[wid];
-    int *sf = s_first[wid];
+    uint32_t *sx = s_x[wid];
+    uint32_t *sy = s_y[wid];
+    uint32_t *se = s_e[wid];
+    uint32_t *sm = s_m[wid];
+    uint64_t *sc = s_c[wid];
 
-    uint32_t X[V];
+    // Fetch a chunk: its first NB * 64 ends (indices clamped, loads
+    // unconditional) and its elements through a descriptor limited to the
+    // share's remaining rows (reads past them return 0).
+    uint4 X[V / 4];
     int64_t E[NB];
     auto fetch = [&](int64_t ic_, int64_t jc_) __attribute__((always_inline)) {
-        // Ends: clamped index, unconditional load (see the row kernel).
-        // Elements: a buffer descriptor over the share's remaining elements
-        // of this chunk, so positions past it read as 0.
 #pragma unroll
         for (int b = 0; b < NB; ++b) E[b] = off[min(ic_ + 1 + b * 64 + lane, a.S)];
-        const int64_t rmax = min((int64_t)CH, sh.j1 - jc_);
+        const int64_t rmax = ic_ + jc_ < sh.d1 ? min((int64_t)CH, sh.j1 - jc_) : 0;
         const auto rs = make_rsrc(a.values + (o0 + jc_), (uint32_t)(rmax * 4));
 #pragma unroll
-        for (int u = 0; u < V; ++u) X[u] = ld32(rs, (uint32_t)(lane * 4), (uint32_t)(u * 256));
+        for (int u = 0; u < V / 4; ++u) X[u] = ld128(rs, (uint32_t)(lane * 16), (uint32_t)(u * 1024));
     };
 
     acc_t carry = R::id();
     int64_t ic = sh.i0, jc = sh.j0;
-    if (ic + jc < sh.d1) fetch(ic, jc);
+    fetch(ic, jc);
     while (ic + jc < sh.d1) {
-        int64_t items = min((int64_t)CH, sh.d1 - ic - jc);
-        const int64_t el = min((int64_t)EC, sh.i1 - ic);
+        const int64_t rows_avail = min((int64_t)CH, sh.j1 - jc);
+        const int64_t ends_avail = min((int64_t)EC, sh.i1 - ic);
 
-        // Ends inside the chunk (end k at row position e: e + k + 1 <= items).
+        // The chunk's ends: end k (position e relative to jc) belongs to it
+        // iff e <= rows_avail; at most EC of them.  Each sets its reset bit.
+        sm[lane] = 0u;
+        wave_lds_sync();
         int ne = 0;
         bool more = true;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            if (more) {
-                const int k = b * 64 + lane;
-                const bool valid = k < el;
-                const int64_t e = E[b] - o0 - jc;
-                const bool cond = valid && e + k + 1 <= items;
-                const int cnt = popc64(ballot(cond));
-                if (cond) se[k] = (uint32_t)e;
-                ne += cnt;
-                more = cnt == 64;
-            }
-        }
-        for (int b = NB; more && b < EC / 64; ++b) {
+        auto take_ends = [&](int b, int64_t eabs) __attribute__((always_inline)) {
             const int k = b * 64 + lane;
-            const bool valid = k < el;
-            const int64_t e = off[min(ic + 1 + k, a.S)] - o0 - jc;
-            const bool cond = valid && e + k + 1 <= items;
+            const int64_t e = eabs - o0 - jc;
+            const bool cond = k < ends_avail && e <= rows_avail;
             const int cnt = popc64(ballot(cond));
-            if (cond) se[k] = (uint32_t)e;
+            if (cond) {
+                se[k] = (uint32_t)e;
+                if (e < CH) lds_or(&sm[e >> 5], 1u << (e & 31));
+            }
             ne += cnt;
             more = cnt == 64;
-        }
-        if (ne == EC) {
-            // At most EC ends per chunk: stop the chunk right after end EC-1.
-            wave_lds_sync();
-            items = (int64_t)se[EC - 1] + EC;
-        }
-        const int rows = (int)(items - ne);
-
-        // Stage the chunk's elements (sums: zero past the chunk's rows).
+        };
 #pragma unroll
-        for (int u = 0; u < V; ++u) {
-            const int r = u * 64 + lane;
-            sv[r] = (kSum && r >= rows) ? 0u : X[u];
-        }
+        for (int b = 0; b < NB; ++b)
+            if (more) take_ends(b, E[b]);
+        for (int b = NB; more && b < EC / 64; ++b) take_ends(b, off[min(ic + 1 + b * 64 + lane, a.S)]);
+        wave_lds_sync();
+        // With EC ends the chunk stops at the last of them.
+        const int rows = ne == EC ? (int)__builtin_amdgcn_readfirstlane(se[EC - 1]) : (int)rows_avail;
+
+        // Stage the elements (lane l of load u holds elements 256 u + 4 l ..).
+#pragma unroll
+        for (int u = 0; u < V / 4; ++u)
+            *reinterpret_cast<uint4 *>(&sx[flat_unit(8 * u + (lane >> 3), lane & 7) * 4]) = X[u];
         const int64_t icn = ic + ne, jcn = jc + rows;
-        if (icn + jcn < sh.d1) fetch(icn, jcn);
-
-        // Lane l owns the ends at positions (16 l, 16 l + 16] (lane 0 also
-        // those at 0): its first end is the first end whose owner is >= l.
-        sf[lane] = ne;
+        fetch(icn, jcn);
         wave_lds_sync();
-        for (int k = lane; k < ne; k += 64) {
-            const uint32_t e = se[k];
-            const int o = e == 0 ? 0 : (int)((e - 1) / V);
-            int po = -1;
-            if (k > 0) {
-                const uint32_t pe = se[k - 1];
-                po = pe == 0 ? 0 : (int)((pe - 1) / V);
-            }
-            if (o != po) sf[o] = k;
-        }
-        wave_lds_sync();
-        int a_lo = sf[lane];
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = (int)lane_get((uint32_t)a_lo, (lane + o) & 63);
-            if (lane + o < 64) a_lo = y < a_lo ? y : a_lo;
-        }
-        int a_hi = (int)lane_get((uint32_t)a_lo, (lane + 1) & 63);
-        if (lane == 63) a_hi = ne;
 
         uint32_t x[V];
 #pragma unroll
-        for (int t = 0; t < V; t += 4) {
-            const uint4 q = *reinterpret_cast<const uint4 *>(&sv[lane * V + t]);
-            x[t] = q.x;
-            x[t + 1] = q.y;
-            x[t + 2] = q.z;
-            x[t + 3] = q.w;
+        for (int c = 0; c < V / 4; ++c) {
+            const uint4 q = *reinterpret_cast<const uint4 *>(&sx[flat_unit(lane, c) * 4]);
+            x[4 * c] = q.x;
+            x[4 * c + 1] = q.y;
+            x[4 * c + 2] = q.z;
+            x[4 * c + 3] = q.w;
         }
+        const uint32_t keep = ~sm[lane];
 
-        // Walk the lane's elements in order.
-        acc_t acc = R::id(), hacc = R::id();
-        bool hh = false;
-        int k = a_lo;
-        uint32_t next_end = k < a_hi ? se[k] : kInf;
-        const uint32_t relbase = (uint32_t)(jc - sh.j0);
-        const uint32_t r0 = (uint32_t)(lane * V);
-
-        auto finish = [&]() __attribute__((always_inline)) {
-            if (!hh) {
-                hh = true;
-                hacc = acc;
-            } else {
-                const uint64_t bits = R::to_slot(acc);
-                sv[k] = (uint32_t)bits;
-                if (kWide) se[k] = (uint32_t)(bits >> 32);
+        // One pass over the lane's elements, restarting at every reset.
+        lacc_t acc{};
+        uint32_t y[kMM ? V : 1];
+        // Elements at or past `rows` (a partial chunk) take no part: sums
+        // zero them, min/max mask their candidate words.
+        const int nv = rows - lane * V;
+        const uint32_t vmask = nv >= V ? 0xFFFFFFFFu : (nv <= 0 ? 0u : (1u << nv) - 1u);
+        if constexpr (!kMM) {
+            if (rows < CH) {
+#pragma unroll
+                for (int t = 0; t < V; ++t) x[t] &= sbit(vmask, t);
             }
-            acc = R::id();
-            ++k;
-            next_end = k < a_hi ? se[k] : kInf;
+        }
+        auto lane_pass = [&](auto partial) __attribute__((always_inline)) {
+            constexpr bool kPartial = decltype(partial)::value;
+            const uint32_t ncode0 = ~(uint32_t)(jc - sh.j0 + lane * V);  // ~row code of element 0
+#pragma unroll
+            for (int t = 0; t < V; ++t) {
+                const uint32_t km = sbit(keep, t);
+                if constexpr (kMM) {
+                    acc &= ((uint64_t)km << 32) | km;
+                    uint32_t key = okey<DT>(x[t]);
+                    if constexpr (OP == OP_MIN) key = ~key;
+                    uint64_t cand = ((uint64_t)key << 32) | (ncode0 - (uint32_t)t);
+                    if constexpr (kPartial) {
+                        const uint32_t vm = sbit(vmask, t);
+                        cand &= ((uint64_t)vm << 32) | vm;
+                    }
+                    acc = cand > acc ? cand : acc;
+                    x[t] = (uint32_t)(acc >> 32);
+                    y[t] = (uint32_t)acc;
+                } else {
+                    if constexpr (kSumF) acc = __uint_as_float(__float_as_uint(acc) & km) + __uint_as_float(x[t]);
+                    else acc = (acc & km) + x[t];
+                    x[t] = kSumF ? __float_as_uint(acc) : (uint32_t)acc;
+                }
+            }
         };
+        if (kMM && rows < CH) lane_pass(std::true_type{});
+        else lane_pass(std::false_type{});
 
 #pragma unroll
-        for (int t = 0; t < V; ++t) {
-            const uint32_t r = r0 + t;
-            while (next_end <= r) finish();
-            if constexpr (kSum) {
-                acc = R::comb(acc, R::lift(x[t], 0u));
-            } else {
-                if ((int)r < rows) acc = R::comb(acc, R::lift(x[t], relbase + r));
-            }
+        for (int c = 0; c < V / 4; ++c) {
+            *reinterpret_cast<uint4 *>(&sx[flat_unit(lane, c) * 4]) =
+                make_uint4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
+            if constexpr (kMM)
+                *reinterpret_cast<uint4 *>(&sy[flat_unit(lane, c) * 4]) =
+                    make_uint4(y[4 * c], y[4 * c + 1], y[4 * c + 2], y[4 * c + 3]);
         }
-        while (k < a_hi) finish();
 
-        // Segmented scan over the lanes; the chunk carry enters at lane 0.
-        bool flag = hh;
-        acc_t xs = (lane == 0 && !flag) ? R::comb(carry, acc) : acc;
+        // Segmented scan across the lanes of the lanes' open parts.
+        bool fl = keep != 0xFFFFFFFFu;
+        lacc_t xs = acc;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             const int src = (lane - o) & 63;
-            const bool pf = lane_get(flag, src);
-            const acc_t px = lane_get(xs, src);
+            const bool pf = lane_get(fl, src);
+            const lacc_t px = lane_get(xs, src);
             if (lane >= o) {
-                if (!flag) xs = R::comb(px, xs);
-                flag = flag || pf;
+                if (!fl) xs = lcomb(px, xs);
+                fl = fl || pf;
             }
         }
-        acc_t ex = lane_get(xs, (lane - 1) & 63);
-        if (lane == 0) ex = carry;
-        if (hh) {
-            const acc_t hv = R::comb(ex, hacc);
-            if (sh.split_head && ic + a_lo == sh.i0) {
-                a.hval[wave] = R::to_slot(hv);
-            } else {
-                const uint64_t bits = R::to_slot(hv);
-                sv[a_lo] = (uint32_t)bits;
-                if (kWide) se[a_lo] = (uint32_t)(bits >> 32);
-            }
+        const acc_t cm = to_max(carry);
+        lacc_t ex = lane_get(xs, (lane - 1) & 63);
+        bool fx = lane_get(fl, (lane - 1) & 63);
+        if (lane == 0) {
+            ex = lacc_t{};
+            fx = false;
         }
-        carry = lane_get(xs, 63);
+        const acc_t cin = fx ? widen(ex) : acomb(cm, widen(ex));
+        sc[lane] = R::to_slot(cin);
+        {
+            // The part of the open segment after the chunk; none when the
+            // chunk's last end closes its last row (an end at position CH
+            // has no reset bit inside the chunk).
+            const lacc_t x63 = lane_get(xs, 63);
+            const bool f63 = lane_get(fl, 63);
+            carry = to_max(f63 ? widen(x63) : acomb(cm, widen(x63)));
+            if (ne > 0 && __builtin_amdgcn_readfirstlane(se[ne - 1]) == (uint32_t)rows) carry = R::id();
+        }
         wave_lds_sync();
 
-        // Coalesced stores of every segment finished in this chunk.
+        // One lane per end: look up the segment's value and store it.
         for (int q = lane; q < ne; q += 64) {
+            const uint32_t p = se[q];
+            const uint32_t pp = q > 0 ? se[q - 1] : kNone;
             const int64_t seg = ic + q;
-            if (sh.split_head && seg == sh.i0) continue;
-            const uint64_t bits = (uint64_t)sv[q] | (kWide ? (uint64_t)se[q] << 32 : 0ull);
-            const acc_t v = R::from_slot(bits);
-            int64_t len = 0;
-            if constexpr (OP == OP_MEAN) len = off[seg + 1] - off[seg];
-            store_final<DT, OP, 1>(a, seg, 0, &v, base, len);
+            acc_t v;
+            if (p == pp) {
+                v = to_max(R::id());  // empty
+            } else if (p == 0) {
+                v = R::from_slot(sc[0]);  // ends where the chunk starts
+            } else {
+                const uint32_t l2 = (p - 1) >> 5, t2 = (p - 1) & 31;
+                const int u = flat_unit((int)l2, (int)(t2 >> 2)) * 4 + (int)(t2 & 3);
+                if constexpr (kMM) v = ((uint64_t)sx[u] << 32) | sy[u];
+                else if constexpr (kSumF) v = (double)__uint_as_float(sx[u]);
+                else v = sx[u];
+                if (pp == kNone || pp < (l2 << 5)) v = acomb(R::from_slot(sc[l2]), v);
+            }
+            v = to_max(v);
+            if (sh.split_head && seg == sh.i0) {
+                a.hval[wave] = R::to_slot(v);
+            } else {
+                int64_t len = 0;
+                if constexpr (OP == OP_MEAN) len = off[seg + 1] - off[seg];
+                store_final<DT, OP, 1>(a, seg, 0, &v, base, len);
+            }
         }
         ic = icn;
         jc = jcn;

@@ -31,6 +31,9 @@ __device__ __forceinline__ int64_t lane_get(int64_t v, int src) {
 __device__ __forceinline__ double lane_get(double v, int src) {
     return __longlong_as_double((long long)lane_get((uint64_t)__double_as_longlong(v), src));
 }
+__device__ __forceinline__ float lane_get(float v, int src) {
+    return __uint_as_float(lane_get(__float_as_uint(v), src));
+}
 __device__ __forceinline__ bool lane_get(bool v, int src) {
     return lane_get((uint32_t)v, src) != 0u;
 }
@@ -63,6 +66,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 }
 __device__ __forceinline__ uint32_t ld32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+
+__device__ __forceinline__ uint4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    // Range checking is per dword: a 16-byte unit cut by the limit returns its
+    // in-range dwords and zeros for the rest.
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+}
+
+// Bit t of m, sign-extended (all ones when set, else 0), as one v_bfe_i32.
+// Written as an instruction so that the compiler keeps the AND with it
+// instead of turning every use into a compare and a select (which costs an
+// extra instruction and a 64-bit mask register per bit).
+__device__ __forceinline__ uint32_t sbit(uint32_t m, int t) {
+    uint32_t r;
+    asm volatile("v_bfe_i32 %0, %1, %2, 1" : "=v"(r) : "v"(m), "n"(t));
+    return r;
+}
+
+// Bitwise OR into a word of this wave's LDS (ds_or_b32).  The only atomic
+// operation in the library: it sets flag bits, so the result does not depend
+// on the order in which lanes arrive.
+__device__ __forceinline__ void lds_or(uint32_t *p, uint32_t v) {
+    __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
 }
 
 }  // namespace segred

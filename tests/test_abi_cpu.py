@@ -123,14 +123,24 @@ def test_binding_refuses_cpu_tensors():
 
 
 def test_kernel_sources_have_no_atomics_or_foreign_backends():
-    """No device atomics (results are combined in a fixed order instead) and no
-    CUDA/Triton/dual-platform code in the library sources."""
+    """No atomics on global memory (results are combined in a fixed order
+    instead) and no CUDA/Triton/dual-platform code in the library sources.
+    The one atomic allowed is the wave-scope LDS bit-OR helper `lds_or`
+    (it sets flag bits, so arrival order cannot change a result)."""
     device_atomic = re.compile(r"\batomic[A-Z]\w*\s*\(|__hip_atomic|__atomic_\w+\s*\(|\bunsafeAtomic")
+    allowed = "__hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT)"
+    seen_allowed = 0
     for name in os.listdir(CSRC):
         code = re.sub(r"//[^\n]*", "", open(os.path.join(CSRC, name)).read())
+        if name == "wave.hpp":
+            seen_allowed = code.count(allowed)
+            code = code.replace(allowed, "")
         assert not device_atomic.search(code), name
         for bad in ("cuda", "triton", "__hip_platform"):
             assert bad not in code.lower(), (name, bad)
+        for m in re.finditer(r"\blds_or\(&(\w+)\[", code):
+            assert m.group(1) == "sm", (name, m.group(0))  # only the per-wave LDS mask array
+    assert seen_allowed == 1
 
 
 def test_product_never_touches_the_oracle():

@@ -212,3 +212,32 @@ def test_three_dimensional_values_flatten_features():
     out, arg = sr.reduce(gu.to_gpu(v3), gu.to_gpu(off), "min")
     assert out.shape == (400, 3, 4) and arg.shape == (400, 3, 4)
     gu.assert_parity(vals, off, "min", out.cpu().numpy().reshape(400, 12), arg.cpu().numpy().reshape(400, 12))
+
+
+def _edge_offsets(chunk=2048):
+    """1-D lengths that put segment ends on chunk edges for a single share
+    starting at row 0: ends exactly at multiples of the chunk, a run of 300
+    empty segments inside one chunk and another right on a chunk edge (more
+    ends than one chunk takes), a segment spanning several chunks, and a
+    last segment ending inside a partial chunk."""
+    lengths = [chunk, chunk, 5, chunk - 5, 2 * chunk, 1, chunk - 1]
+    lengths += [0] * 300 + [7, 100] + [0] * 300 + [chunk - 107]
+    lengths += [3 * chunk + 17, chunk - 17] + [0] * 5 + [11, 0, 0, 29]
+    return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+
+
+@pytest.mark.parametrize("kind", ["u32", "i32", "f32"])
+def test_one_dimensional_chunk_edges(kind):
+    off = _edge_offsets()
+    rows = int(off[-1])
+    rng = np.random.default_rng(77)
+    vals = {"f32": rng.standard_normal(rows, dtype=np.float32),
+            "i32": rng.integers(-(2 ** 31), 2 ** 31, rows, dtype=np.int32),
+            "u32": rng.integers(0, 2 ** 32, rows, dtype=np.uint32)}[kind]
+    ops = ["sum", "min", "max"] + (["mean"] if kind == "f32" else [])
+    for op in ops:
+        orc = oracle.reduce(vals, off, op)
+        for shares in (1, 2, 3, None):
+            gu.say(f"chunk edges kind={kind} op={op} shares={shares}")
+            out, arg = gu.run_gpu(vals, off, op, shares=shares)
+            gu.assert_parity(vals, off, op, out, arg, orc=orc, what=f"chunk edges shares={shares}")
