@@ -103,9 +103,9 @@ class ReduceWorkload(Workload):
 
 
 class RleWorkload(Workload):
-    """sort -> RLE -> offsets -> reduce: encode 16M sorted keys, read the run
-    count back (8 bytes), then sum the uint32 payload and take the min (+row)
-    of the int32 payload over the runs."""
+    """sort -> RLE -> offsets -> reduce: encode 16M sorted keys, then sum the
+    uint32 payload and take the min (+row) of the int32 payload over the runs,
+    with the run count read on the device (no readback inside a step)."""
 
     def __init__(self, cfg, copies, sr, torch):
         self.sr, self.torch = sr, torch
@@ -116,18 +116,22 @@ class RleWorkload(Workload):
         self.sets = [(k, pu, pi)] + [(k.clone(), pu.clone(), pi.clone()) for _ in range(copies - 1)]
         self.n = int(cfg["keys"].size)
         self.calls = [("sum_u32", "sum"), ("min_i32", "min")]
-        self.count = None
+        # the run count of this input (fixed by the seed), for the byte count
+        _, _, _, cnt = sr.offsets_from_rle(k)
+        self.count = int(cnt.item())
+        dev = k.device
+        self.out_sum = torch.empty(self.n, dtype=torch.uint32, device=dev)
+        self.out_min = torch.empty(self.n, dtype=torch.int32, device=dev)
+        self.arg_min = torch.empty(self.n, dtype=torch.int64, device=dev)
         self.outs = {}
 
     def step(self, i):
         k, pu, pi = self.sets[i % len(self.sets)]
         values, lengths, offsets, count = self.sr.offsets_from_rle(k)
-        c = int(count.item())
-        self.count = c
-        off = offsets[: c + 1]
-        self.outs["sum_u32"] = self.sr.reduce(pu, off, "sum")
-        self.outs["min_i32"] = self.sr.reduce(pi, off, "min")
-        self.outs["rle"] = (values[:c], lengths[:c], off)
+        self.outs["sum_u32"] = self.sr.reduce(pu, offsets, "sum", out=self.out_sum, num_segments=count)
+        self.outs["min_i32"] = self.sr.reduce(pi, offsets, "min", out=self.out_min, arg=self.arg_min,
+                                              num_segments=count)
+        self.outs["rle"] = (values, lengths, offsets, count)
 
     def rle_bytes(self):
         return self.n * 4 + self.count * (4 + 4 + 8) + 8 + 8
@@ -147,7 +151,7 @@ DESCRIPTIONS = {
     "message": "graph message passing: 1,000,000 destination-sorted rows x F=64 f32 normal(0,1) into "
                "10,000 segments (multinomial lengths, mean 100), int64 indptr; sum and max+argmax",
     "rle": "sort->RLE->reduce: 16M uint32 Zipf(1.1) keys over 2^20 values sorted, RLE to values/lengths/"
-           "offsets, count readback, segmented sum of u32 payload and min+arg of i32 payload",
+           "offsets/count, segmented sum of u32 payload and min+arg of i32 payload over the device-side count",
     "skew": "heavy skew 1-D: 50M f32 uniform[0,1) over 1M segments (Pareto 1.5 lengths, one 5M-row "
             "segment, 10% empty); sum and min+argmin",
     "powerlaw": "power-law graph: 2M nodes, 32M destination-sorted edges (in-degree Lomax alpha=2, hub of "
@@ -208,15 +212,17 @@ def check_parity(wl, results):
     verdict = {}
     if isinstance(wl, RleWorkload):
         v, ln, off, c = results["rle"]
-        gv, gl, go = (x.cpu().numpy() for x in wl.outs["rle"])
-        verdict["rle"] = bool(c == wl.count and np.array_equal(gv, v) and np.array_equal(gl, ln)
-                              and np.array_equal(go, off))
+        gv, gl, go, gc = wl.outs["rle"]
+        gc = int(gc.item())
+        verdict["rle"] = bool(gc == c == wl.count and np.array_equal(gv[:c].cpu().numpy(), v)
+                              and np.array_equal(gl[:c].cpu().numpy(), ln)
+                              and np.array_equal(go[: c + 1].cpu().numpy(), off))
         for label in ("sum_u32", "min_i32"):
             out, arg = wl.outs[label]
             ref = results[label]
-            ok = np.array_equal(out.cpu().numpy().view(np.uint32), ref.out[:, 0].view(np.uint32))
+            ok = np.array_equal(out[:c].cpu().numpy().view(np.uint32), ref.out[:, 0].view(np.uint32))
             if arg is not None:
-                ok = ok and np.array_equal(arg.cpu().numpy(), ref.arg[:, 0])
+                ok = ok and np.array_equal(arg[:c].cpu().numpy(), ref.arg[:, 0])
             verdict[label] = bool(ok)
         return verdict
     for op in wl.ops:

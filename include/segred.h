@@ -60,9 +60,12 @@ enum segred_status {
  *   op            SEGRED_SUM, SEGRED_MIN, SEGRED_MAX or SEGRED_MEAN.
  *   out           [S, feat] of the input type (float32 for MEAN).
  *                 SUM of u32/i32 wraps modulo 2^32.  SUM and MEAN of f32 are
- *                 accumulated in float64 in a fixed order and rounded to
- *                 float32 once, so results are bitwise identical run to run
- *                 on a given device.  MIN/MAX order u32 unsigned, i32 signed,
+ *                 accumulated in a fixed order, so results are bitwise
+ *                 identical run to run on a given device: in float64 and
+ *                 rounded to float32 once, except that 1-D inputs (feat = 1)
+ *                 add runs of at most 32 consecutive elements and a 64-way
+ *                 tree of such runs in float32 first (error below
+ *                 38 * 2^-24 * sum|x| in all).  MIN/MAX order u32 unsigned, i32 signed,
  *                 f32 by the monotone bit key (so -0.0 < +0.0 and NaNs sort
  *                 past +-inf by their bits); `out` holds the element's bits.
  *                 An empty segment writes 0 (+0.0 for floats).
@@ -107,7 +110,8 @@ int segred_reduce(const void *values, int32_t dtype, int64_t feat,
  *
  * Only values[0..count), lengths[0..count) and offsets[0..count] are written;
  * the rest of each buffer is left untouched.  To reduce over the runs, read
- * `count` back (8 bytes) and pass it as num_segments with `offsets`.
+ * `count` back (8 bytes) and pass it as num_segments with `offsets`, or pass
+ * `count` itself to segred_reduce_device_count (no readback).
  * Errors: SEGRED_ERR_INVALID_ARGUMENT for n < 0, n > UINT32_MAX, a NULL
  * output (or NULL keys with n > 0), misalignment (4 bytes for keys, values,
  * lengths; 8 bytes for offsets and count).  SEGRED_ERR_OUT_OF_MEMORY,
@@ -116,6 +120,29 @@ int segred_reduce(const void *values, int32_t dtype, int64_t feat,
 int segred_offsets_from_rle(const uint32_t *sorted_keys, int64_t n,
                             uint32_t *values, uint32_t *lengths,
                             int64_t *offsets, int64_t *count, hipStream_t stream);
+
+/*
+ * segred_reduce_device_count -- segred_reduce with the segment count read on
+ * the device, for the sort -> RLE -> offsets -> reduce composition that the
+ * "GPURunLengthEncode and GPUUnique" page draws ("Composition": run lengths
+ * become offsets that feed the segmented reduction) without reading the run
+ * count back to the host.
+ *
+ *   num_segments  one int64 on the device (e.g. the `count` written by
+ *                 segred_offsets_from_rle), read when the call runs; the
+ *                 call reduces S = min(max(*num_segments, 0), max_segments)
+ *                 segments.
+ *   max_segments  host bound >= 0: `offsets` must hold max_segments + 1
+ *                 entries and `out`/`arg_out` max_segments * feat; rows of
+ *                 `out`/`arg_out` at or past S are left untouched.
+ *   all other arguments and every error: as segred_reduce (plus
+ *   SEGRED_ERR_INVALID_ARGUMENT for a NULL or misaligned num_segments).
+ *   Only offsets[0..S] are read.
+ */
+int segred_reduce_device_count(const void *values, int32_t dtype, int64_t feat,
+                               const int64_t *offsets, const int64_t *num_segments,
+                               int64_t max_segments, int32_t op, void *out,
+                               int64_t *arg_out, hipStream_t stream);
 
 /* Static, host-side description of a status code (never NULL). */
 const char *segred_status_string(int status);

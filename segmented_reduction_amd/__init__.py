@@ -52,6 +52,8 @@ def library(path: str | None = None):
             vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
             lib.segred_reduce.argtypes = [vp, i32, i64, vp, i64, i32, vp, vp, vp]
             lib.segred_reduce.restype = ctypes.c_int
+            lib.segred_reduce_device_count.argtypes = [vp, i32, i64, vp, vp, i64, i32, vp, vp, vp]
+            lib.segred_reduce_device_count.restype = ctypes.c_int
             lib.segred_offsets_from_rle.argtypes = [vp, i64, vp, vp, vp, vp, vp]
             lib.segred_offsets_from_rle.restype = ctypes.c_int
             lib.segred_status_string.argtypes = [ctypes.c_int]
@@ -83,12 +85,17 @@ def _stream(device: torch.device) -> int:
 
 
 def reduce(values: torch.Tensor, offsets: torch.Tensor, op: str, *, want_arg: bool = True,
-           out: torch.Tensor | None = None, arg: torch.Tensor | None = None):
+           out: torch.Tensor | None = None, arg: torch.Tensor | None = None,
+           num_segments: torch.Tensor | None = None):
     """Segmented ``op`` ("sum", "min", "max", "mean") of ``values`` over ``offsets``.
 
     values  [N] or [N, ...] uint32 / int32 / float32 on a GPU, contiguous;
             trailing dimensions are flattened into F features per row.
     offsets int64 [S + 1] on the same GPU; segment s is rows offsets[s]..offsets[s+1]-1.
+    num_segments  optional one-element int64 GPU tensor: the segment count is
+            then read on the device (segred_reduce_device_count); offsets
+            and the outputs are its capacity and rows past the count are
+            left as they were.
     Returns (out [S, ...], arg [S, ...] int64 or None).  arg is the row of
     the extremum for min/max (lowest on ties, -1 for empty segments).
     """
@@ -121,6 +128,16 @@ def reduce(values: torch.Tensor, offsets: torch.Tensor, op: str, *, want_arg: bo
         arg = torch.empty((s,) + feat_shape, dtype=torch.int64, device=values.device)
     if not want:
         arg = None
+    if num_segments is not None:
+        if (not num_segments.is_cuda or num_segments.dtype != torch.int64 or num_segments.numel() != 1
+                or num_segments.device != values.device):
+            raise ValueError("num_segments must be a one-element int64 tensor on the values' device")
+        with torch.cuda.device(values.device):
+            rc = library().segred_reduce_device_count(
+                values.data_ptr(), DTYPES[values.dtype], feat, offsets.data_ptr(), num_segments.data_ptr(), s,
+                OPS[op], out.data_ptr(), arg.data_ptr() if arg is not None else None, _stream(values.device))
+        _check(rc, "segred_reduce_device_count")
+        return out, arg
     with torch.cuda.device(values.device):
         rc = library().segred_reduce(values.data_ptr(), DTYPES[values.dtype], feat, offsets.data_ptr(), s,
                                      OPS[op], out.data_ptr(), arg.data_ptr() if arg is not None else None,

@@ -52,13 +52,21 @@ enum { OP_SUM = 0, OP_MIN = 1, OP_MAX = 2, OP_MEAN = 3 };
 struct KArgs {
     const uint32_t *values;  // element bits, row-major [rows, F]
     const int64_t *offsets;  // [S + 1]
-    int64_t S, F, NW;
+    int64_t S, F, NW;        // S: segment count, or the capacity when S_dev is set
+    const int64_t *S_dev;    // segment count on the device (min(*S_dev, S) is used), or null
     uint32_t *out;           // [S, F]
     int64_t *arg;            // [S, F] or null
     int64_t *hdr;            // [NW][4]: see write_header
     uint64_t *hval;          // [NW][F]: partial of the share's first segment when it began earlier
     uint64_t *tval;          // [NW][F]: partial of the share's last segment when it continues
 };
+
+// The call's segment count: the host value, or the device one clamped to it.
+__device__ __forceinline__ int64_t seg_count(const KArgs &a) {
+    if (!a.S_dev) return a.S;
+    const int64_t s = *a.S_dev;
+    return s < 0 ? 0 : (s < a.S ? s : a.S);
+}
 
 // Monotone order key: u32 as is, i32 with the sign flipped, f32 with all bits
 // flipped when negative and the sign set otherwise (graph-reduce, "Method").
@@ -173,15 +181,21 @@ __device__ __forceinline__ int count_le(const uint32_t *arr, int n, uint32_t x) 
     return lo;
 }
 
-// Item d is preceded by i(d) = max{ i in [0, S] : offsets[i] - o0 + i <= d }
-// segment ends (offsets[i] - o0 + i increases strictly with i).  The first
-// round of the search does not depend on d: the workgroup reads 256 evenly
-// spaced offsets (offsets[0] and offsets[S] among them) into LDS once, which
-// also gives o0 and the total item count T.  Each wave then narrows both ends
-// of its share with 256-way rounds (4 probes per lane): 2 memory round trips
-// in all for S < 65K segments, 3 for S < 16M.  Every probe is clamped into
-// the array and loaded unconditionally (a load under a branch would be
-// waited for inside the branch).
+// Item d is preceded by i(d) = max{ i in [0, S] : key(i) <= d } segment ends,
+// key(i) = offsets[i] - o0 + i (strictly increasing in i).  The four waves
+// of a workgroup own four consecutive shares, so their five boundary
+// diagonals lie close together and the workgroup searches for them jointly:
+//   round A: 256 evenly spaced offsets (the same for every workgroup, so they
+//            stay cached), which also give o0 and the item count T;
+//   round B: 256 evenly spaced offsets over the range round A leaves for the
+//            workgroup's first and last diagonal;
+//   round C: each wave narrows its own two diagonals with 256-way rounds (one
+//            round unless the workgroup's range is wider than 65K ends).
+// Rounds A and B are one load per thread; round C reads a few consecutive
+// cache lines.  Every probe is clamped into the array and loaded
+// unconditionally (a load under a branch would be waited for inside the
+// branch).  The key of the last probe at or below a diagonal is kept, which
+// gives offsets[i(d)] without another load.
 
 // A wave's share of the merged (rows + segment ends) sequence: items
 // [d0, d1), i.e. segment ends [i0, i1) and rows [j0, j1) (rows relative to
@@ -193,41 +207,70 @@ struct Share {
     bool has_tail;     // segment i1 has rows in the share and continues past it
 };
 
+// Where d falls among 256 probes p_k = lo + k * step (k < 255) and p_255 = hi
+// whose raw offsets are in s[]: the last probe with key <= d (there is one)
+// and its key; i(d) then lies in [lo', hi'].
+struct Bracket {
+    int64_t lo, hi, klo;
+};
+__device__ __forceinline__ int64_t probe_pos(int k, int64_t lo, int64_t step, int64_t hi) {
+    return k == 255 ? hi : min(lo + (int64_t)k * step, hi);
+}
+__device__ __forceinline__ Bracket bracket(const int64_t *s, int64_t lo, int64_t step, int64_t hi, int64_t o0,
+                                           int64_t d, int lane) {
+    int cnt = 0;
+    int64_t kk[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int k = u * 64 + lane;
+        kk[u] = s[k] - o0 + probe_pos(k, lo, step, hi);
+        cnt += popc64(ballot(kk[u] <= d));
+    }
+    // cnt >= 1: probe 0 has key <= d
+    const int last = cnt - 1, ul = last >> 6;
+    const int64_t klast = ul == 0 ? kk[0] : ul == 1 ? kk[1] : ul == 2 ? kk[2] : kk[3];
+    Bracket b;
+    b.klo = (int64_t)__builtin_amdgcn_readlane((uint32_t)klast, last & 63) |
+            ((int64_t)__builtin_amdgcn_readlane((uint32_t)((uint64_t)klast >> 32), last & 63) << 32);
+    b.lo = probe_pos(last, lo, step, hi);
+    b.hi = cnt >= 256 ? hi : probe_pos(cnt, lo, step, hi) - 1;
+    if (b.hi < b.lo) b.hi = b.lo;
+    return b;
+}
+
 __device__ __forceinline__ Share find_share(const int64_t *off, int64_t S, int64_t NW, int64_t wave, int lane,
                                             int64_t *s_probe /* LDS [256], workgroup-wide */,
                                             int64_t min_share = 1) {
     const int tid = threadIdx.x;
-    const int64_t step1 = (S + 254) / 255;  // probes k * step1, k < 255, and S
-    const int64_t p = tid == 255 ? S : min((int64_t)tid * step1, S);
-    s_probe[tid] = off[p];
-    __syncthreads();
+    const int wid = tid >> 6;
+    const int64_t blk = (int64_t)blockIdx.x;
 
+    // Round A.
+    const int64_t stepA = (S + 254) / 255;
+    s_probe[tid] = off[probe_pos(tid, 0, stepA, S)];
+    __syncthreads();
     const int64_t o0 = s_probe[0];
     const int64_t T = (s_probe[255] - o0) + S;
     // Shares of at least min_share items: small inputs use fewer waves (the
     // rest get empty shares and only write their header).
     const int64_t D = max((T + NW - 1) / NW, min_share);
-    const int64_t d0 = min(wave * D, T), d1 = min(d0 + D, T);
+    const int64_t g0 = min(blk * 4 * D, T), g4 = min((blk * 4 + 4) * D, T);
+    const int64_t d0 = min((blk * 4 + wid) * D, T), d1 = min(d0 + D, T);
+    const Bracket a0 = bracket(s_probe, 0, stepA, S, o0, g0, lane);
+    const Bracket a4 = bracket(s_probe, 0, stepA, S, o0, g4, lane);
+    __syncthreads();  // every wave is done with round A
 
-    // round 1 from LDS: the last probe with key <= d bounds i(d) from below,
-    // the next one from above (the count is >= 1 since key(0) = 0 <= d)
-    int c0 = 0, c1 = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int k = u * 64 + lane;
-        const int64_t pk = k == 255 ? S : min((int64_t)k * step1, S);
-        const int64_t key = s_probe[k] - o0 + pk;
-        c0 += popc64(ballot(key <= d0));
-        c1 += popc64(ballot(key <= d1));
-    }
-    auto bound = [&](int cnt, int64_t &lo, int64_t &hi) __attribute__((always_inline)) {
-        lo = (cnt - 1) == 255 ? S : min((int64_t)(cnt - 1) * step1, S);
-        hi = cnt >= 256 ? S : ((cnt == 255 ? S : min((int64_t)cnt * step1, S)) - 1);
-        if (hi < lo) hi = lo;
-    };
-    int64_t lo0, hi0, lo1, hi1;
-    bound(c0, lo0, hi0);
-    bound(c1, lo1, hi1);
+    // Round B over [L, H], which holds i(d) for every diagonal of the group.
+    const int64_t L = a0.lo, H = a4.hi;
+    const int64_t stepB = max((H - L + 254) / 255, (int64_t)1);
+    s_probe[tid] = off[probe_pos(tid, L, stepB, H)];
+    __syncthreads();
+    Bracket b0 = bracket(s_probe, L, stepB, H, o0, d0, lane);
+    Bracket b1 = bracket(s_probe, L, stepB, H, o0, d1, lane);
+
+    // Round C: 256-way rounds on both diagonals of this wave.
+    int64_t lo0 = b0.lo, hi0 = b0.hi, k0lo = b0.klo;
+    int64_t lo1 = b1.lo, hi1 = b1.hi, k1lo = b1.klo;
     while (lo0 < hi0 || lo1 < hi1) {
         const int64_t st0 = (hi0 - lo0 + 255) >> 8, st1 = (hi1 - lo1 + 255) >> 8;
         int64_t k0[4], k1[4];
@@ -248,11 +291,21 @@ __device__ __forceinline__ Share find_share(const int64_t *off, int64_t S, int64
             n0 += popc64(ballot(ok0[u] && k0[u] <= d0));
             n1 += popc64(ballot(ok1[u] && k1[u] <= d1));
         }
+        // key of probe n (1-based), held by lane (n - 1) % 64 in slot (n - 1) / 64
+        auto key_of = [&](int64_t v0, int64_t v1, int64_t v2, int64_t v3, int n)
+            __attribute__((always_inline)) -> int64_t {
+            const int m = n - 1, u = m >> 6;
+            const int64_t v = u == 0 ? v0 : u == 1 ? v1 : u == 2 ? v2 : v3;
+            return (int64_t)__builtin_amdgcn_readlane((uint32_t)v, m & 63) |
+                   ((int64_t)__builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), m & 63) << 32);
+        };
         if (lo0 < hi0) {
+            if (n0 > 0) k0lo = key_of(k0[0], k0[1], k0[2], k0[3], n0);
             hi0 = min(hi0, lo0 + (int64_t)(n0 + 1) * st0 - 1);
             lo0 += (int64_t)n0 * st0;
         }
         if (lo1 < hi1) {
+            if (n1 > 0) k1lo = key_of(k1[0], k1[1], k1[2], k1[3], n1);
             hi1 = min(hi1, lo1 + (int64_t)(n1 + 1) * st1 - 1);
             lo1 += (int64_t)n1 * st1;
         }
@@ -268,9 +321,9 @@ __device__ __forceinline__ Share find_share(const int64_t *off, int64_t S, int64
     sh.j0 = sh.d0 - sh.i0;
     sh.i1 = readfirst(lo1);
     sh.j1 = sh.d1 - sh.i1;
-    sh.first_row = readfirst(off[min(sh.i0, S)] - sh.o0);
+    sh.first_row = readfirst(k0lo) - sh.i0;  // offsets[i0] - o0
     sh.split_head = sh.i0 < sh.i1 && sh.first_row < sh.j0;
-    const int64_t tail_row = readfirst(off[min(sh.i1, S)] - sh.o0);
+    const int64_t tail_row = readfirst(k1lo) - sh.i1;  // offsets[i1] - o0
     sh.has_tail = sh.i1 < S && tail_row < sh.j1;
     return sh;
 }
@@ -311,7 +364,8 @@ __global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
     const int64_t wave = (int64_t)blockIdx.x * 4 + wid;
     const int64_t *off = a.offsets;
     __shared__ int64_t s_probe[256];
-    const Share sh = find_share(off, a.S, a.NW, wave, lane, s_probe);
+    const int64_t S = seg_count(a);
+    const Share sh = find_share(off, S, a.NW, wave, lane, s_probe);
     const int64_t o0 = sh.o0, base = sh.o0 + sh.j0;
     uint32_t *se = s_ends[wid];
     const uint32_t gv = (uint32_t)(g * V);
@@ -348,7 +402,7 @@ __global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
         };
         uint32_t x[V];
         int64_t ic = sh.i0, jc = sh.j0;
-        int64_t en = off[min(ic + 1 + lane, a.S)];
+        int64_t en = off[min(ic + 1 + lane, S)];
         {
             const auto rs = rows_of(ic, jc);
 #pragma unroll
@@ -368,7 +422,7 @@ __global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
             for (int b = 64; cnt == 64 && b < CH; b += 64) {
                 const int k = b + lane;
                 const bool valid = k < ends_left;
-                const int64_t e = off[min(ic + 1 + k, a.S)] - o0 - jc;
+                const int64_t e = off[min(ic + 1 + k, S)] - o0 - jc;
                 const bool cond = valid && e + k + 1 <= items;
                 cnt = popc64(ballot(cond));
                 if (cond) se[k] = (uint32_t)e;
@@ -376,7 +430,7 @@ __global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
             }
             const int rows = (int)(items - ne);
             const int64_t icn = ic + ne, jcn = jc + rows;
-            en = off[min(icn + 1 + lane, a.S)];
+            en = off[min(icn + 1 + lane, S)];
             const auto rsn = rows_of(icn, jcn);
             const uint32_t relbase = (uint32_t)(jc - sh.j0);
 
@@ -517,38 +571,40 @@ __global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
 
 // Pass 1 for one feature per row (1-D values).
 //
-// A chunk is up to 2048 elements and up to 256 segment ends.  Its elements
+// A chunk is up to 2048 elements and up to 128 segment ends.  Its elements
 // arrive with coalesced 16-byte loads and are staged through LDS (an XOR
 // swizzle of 16-byte units keeps both the fill and the per-lane reads free of
 // bank conflicts), so that lane l holds elements [32 l, 32 l + 32).  The
 // chunk's ends become a reset mask per lane (bit t: a segment ends right
-// before element 32 l + t).  Each lane then runs one pass over its 32
-// elements that restarts its accumulator at every reset (a bitwise AND with
-// the sign-extended mask bit, no branches) and leaves the running value at
-// every element in LDS; a segmented scan across the lanes (cross-lane moves)
-// gives every lane the part of its open segment that lies before it.  The
-// result of a segment ending before element p is then the running value at
-// p - 1, plus the carried-in part when the segment began before that lane:
-// one lane per end looks both up and stores the result, so the stores are
-// coalesced.  The next chunk streams into registers while this one is
-// processed.
+// before element 32 l + t).  Each lane then makes one pass over its 32
+// elements that restarts its accumulator at every reset (an AND with the
+// sign-extended mask bit, no branches) and leaves its running value at every
+// element in LDS; a segmented scan across the lanes (cross-lane moves) gives
+// every lane the part of its open segment that lies before it.  The result of
+// a segment ending before element p is then the running value at p - 1, plus
+// the carried-in part when the segment began before that lane: one lane per
+// end looks both up and stores the result, so the stores are coalesced.  The
+// next chunk streams into registers while this one is processed.
 //
 // Float sums: a lane's 32 elements and the scan across a chunk's 64 lanes add
 // in float32 (a tree of depth 6 over lane sums of at most 32 terms, so the
 // error stays below 38 * 2^-24 of the sum of magnitudes, well inside
 // 1e-5 * sum|x|); everything that crosses a chunk or share boundary adds in
-// float64.  Min/max work on the packed (key, row code) word; for MIN the word
-// is complemented inside the chunk so that both are a maximum.
+// float64.  Min/max: the running value is the packed (key, 32 - t) word of
+// the best element so far (MIN complements the key, so both are a maximum);
+// only its position byte is kept in LDS and the store looks the element up
+// again in the staged chunk.
 __device__ __forceinline__ int flat_unit(int owner, int c) {
     return owner * 8 + (c ^ ((owner & 7) ^ ((owner >> 3) & 1)));
 }
 
 template <int DT, int OP>
-__global__ __launch_bounds__(256) void seg_reduce_flat(const KArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Red<DT, OP>::kMinMax ? 2 : 4)))
+void seg_reduce_flat(const KArgs a) {
     using R = Red<DT, OP>;
     using acc_t = typename R::acc_t;
     constexpr bool kSumF = R::kSumF, kMM = R::kMinMax;
-    constexpr int V = 32, CH = 64 * V, EC = 256, NB = 2;
+    constexpr int V = 32, CH = 64 * V, EC = 128, NB = EC / 64;
     constexpr uint32_t kNone = 0xFFFFFFFFu;
     // in-chunk value: float for float sums, else the accumulator itself
     // (min/max in the "maximum" domain)
@@ -569,34 +625,41 @@ __global__ __launch_bounds__(256) void seg_reduce_flat(const KArgs a) {
         if constexpr (kMM) return l > e ? l : e;
         else return e + l;
     };
+    // packed word of element t of lane l (row code relative to the share)
+    auto mm_word = [&](uint32_t bits, uint32_t rel) __attribute__((always_inline)) -> uint64_t {
+        uint32_t key = okey<DT>(bits);
+        if constexpr (OP == OP_MIN) key = ~key;
+        return ((uint64_t)key << 32) | ~rel;
+    };
 
-    __shared__ __attribute__((aligned(16))) uint32_t s_x[4][CH];             // elements, then running values (min/max: keys)
-    __shared__ __attribute__((aligned(16))) uint32_t s_y[4][kMM ? CH : 4];   // min/max: running row codes
-    __shared__ uint32_t s_e[4][EC];                                          // end positions in the chunk
-    __shared__ uint32_t s_m[4][64];                                          // reset masks
-    __shared__ uint64_t s_c[4][64];                                          // carried-in part per lane
+    __shared__ __attribute__((aligned(16))) uint32_t s_x[4][CH];            // elements (sums: then running values)
+    __shared__ __attribute__((aligned(16))) uint32_t s_p[4][kMM ? CH / 4 : 4];  // min/max: position bytes
+    __shared__ uint32_t s_e[4][EC];                                         // end positions in the chunk
+    __shared__ uint32_t s_m[4][64];                                         // reset masks
+    __shared__ uint64_t s_c[4][64];                                         // carried-in part per lane
     __shared__ int64_t s_probe[256];
 
     const int wid = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * 4 + wid;
     const int64_t *off = a.offsets;
-    const Share sh = find_share(off, a.S, a.NW, wave, lane, s_probe, (int64_t)CH);
+    const int64_t S = seg_count(a);
+    const Share sh = find_share(off, S, a.NW, wave, lane, s_probe, (int64_t)CH);
     const int64_t o0 = sh.o0, base = sh.o0 + sh.j0;
     uint32_t *sx = s_x[wid];
-    uint32_t *sy = s_y[wid];
+    uint8_t *sp = reinterpret_cast<uint8_t *>(s_p[wid]);
     uint32_t *se = s_e[wid];
     uint32_t *sm = s_m[wid];
     uint64_t *sc = s_c[wid];
 
-    // Fetch a chunk: its first NB * 64 ends (indices clamped, loads
-    // unconditional) and its elements through a descriptor limited to the
-    // share's remaining rows (reads past them return 0).
+    // Fetch a chunk: its first EC ends (indices clamped, loads unconditional)
+    // and its elements through a descriptor limited to the share's remaining
+    // rows (reads past them return 0).
     uint4 X[V / 4];
     int64_t E[NB];
     auto fetch = [&](int64_t ic_, int64_t jc_) __attribute__((always_inline)) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) E[b] = off[min(ic_ + 1 + b * 64 + lane, a.S)];
+        for (int b = 0; b < NB; ++b) E[b] = off[min(ic_ + 1 + b * 64 + lane, S)];
         const int64_t rmax = ic_ + jc_ < sh.d1 ? min((int64_t)CH, sh.j1 - jc_) : 0;
         const auto rs = make_rsrc(a.values + (o0 + jc_), (uint32_t)(rmax * 4));
 #pragma unroll
@@ -616,22 +679,21 @@ __global__ __launch_bounds__(256) void seg_reduce_flat(const KArgs a) {
         wave_lds_sync();
         int ne = 0;
         bool more = true;
-        auto take_ends = [&](int b, int64_t eabs) __attribute__((always_inline)) {
-            const int k = b * 64 + lane;
-            const int64_t e = eabs - o0 - jc;
-            const bool cond = k < ends_avail && e <= rows_avail;
-            const int cnt = popc64(ballot(cond));
-            if (cond) {
-                se[k] = (uint32_t)e;
-                if (e < CH) lds_or(&sm[e >> 5], 1u << (e & 31));
-            }
-            ne += cnt;
-            more = cnt == 64;
-        };
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-            if (more) take_ends(b, E[b]);
-        for (int b = NB; more && b < EC / 64; ++b) take_ends(b, off[min(ic + 1 + b * 64 + lane, a.S)]);
+        for (int b = 0; b < NB; ++b) {
+            if (more) {
+                const int k = b * 64 + lane;
+                const int64_t e = E[b] - o0 - jc;
+                const bool cond = k < ends_avail && e <= rows_avail;
+                const int cnt = popc64(ballot(cond));
+                if (cond) {
+                    se[k] = (uint32_t)e;
+                    if (e < CH) lds_or(&sm[e >> 5], 1u << (e & 31));
+                }
+                ne += cnt;
+                more = cnt == 64;
+            }
+        }
         wave_lds_sync();
         // With EC ends the chunk stops at the last of them.
         const int rows = ne == EC ? (int)__builtin_amdgcn_readfirstlane(se[EC - 1]) : (int)rows_avail;
@@ -654,23 +716,15 @@ __global__ __launch_bounds__(256) void seg_reduce_flat(const KArgs a) {
             x[4 * c + 3] = q.w;
         }
         const uint32_t keep = ~sm[lane];
+        const uint32_t rel0 = (uint32_t)(jc - sh.j0) + (uint32_t)(lane * V);  // row code base of the lane
 
         // One pass over the lane's elements, restarting at every reset.
+        // Elements past `rows` (a partial chunk) are not excluded: nothing
+        // reads a running value at or past them (the carry out of the chunk
+        // is looked up at position `rows` like a segment end).
         lacc_t acc{};
-        uint32_t y[kMM ? V : 1];
-        // Elements at or past `rows` (a partial chunk) take no part: sums
-        // zero them, min/max mask their candidate words.
-        const int nv = rows - lane * V;
-        const uint32_t vmask = nv >= V ? 0xFFFFFFFFu : (nv <= 0 ? 0u : (1u << nv) - 1u);
-        if constexpr (!kMM) {
-            if (rows < CH) {
-#pragma unroll
-                for (int t = 0; t < V; ++t) x[t] &= sbit(vmask, t);
-            }
-        }
-        auto lane_pass = [&](auto partial) __attribute__((always_inline)) {
-            constexpr bool kPartial = decltype(partial)::value;
-            const uint32_t ncode0 = ~(uint32_t)(jc - sh.j0 + lane * V);  // ~row code of element 0
+        {
+            uint32_t pk = 0;
 #pragma unroll
             for (int t = 0; t < V; ++t) {
                 const uint32_t km = sbit(keep, t);
@@ -678,36 +732,35 @@ __global__ __launch_bounds__(256) void seg_reduce_flat(const KArgs a) {
                     acc &= ((uint64_t)km << 32) | km;
                     uint32_t key = okey<DT>(x[t]);
                     if constexpr (OP == OP_MIN) key = ~key;
-                    uint64_t cand = ((uint64_t)key << 32) | (ncode0 - (uint32_t)t);
-                    if constexpr (kPartial) {
-                        const uint32_t vm = sbit(vmask, t);
-                        cand &= ((uint64_t)vm << 32) | vm;
-                    }
+                    const uint64_t cand = ((uint64_t)key << 32) | (uint32_t)(V - t);
                     acc = cand > acc ? cand : acc;
-                    x[t] = (uint32_t)(acc >> 32);
-                    y[t] = (uint32_t)acc;
+                    // position byte of the best element so far (V - t)
+                    pk |= ((uint32_t)acc & 0xFFu) << (8 * (t & 3));
+                    if ((t & 3) == 3) {
+                        reinterpret_cast<uint32_t *>(sp)[lane * (V / 4) + (t >> 2)] = pk;
+                        pk = 0;
+                    }
                 } else {
                     if constexpr (kSumF) acc = __uint_as_float(__float_as_uint(acc) & km) + __uint_as_float(x[t]);
                     else acc = (acc & km) + x[t];
                     x[t] = kSumF ? __float_as_uint(acc) : (uint32_t)acc;
                 }
             }
-        };
-        if (kMM && rows < CH) lane_pass(std::true_type{});
-        else lane_pass(std::false_type{});
-
+        }
+        if constexpr (!kMM) {
 #pragma unroll
-        for (int c = 0; c < V / 4; ++c) {
-            *reinterpret_cast<uint4 *>(&sx[flat_unit(lane, c) * 4]) =
-                make_uint4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
-            if constexpr (kMM)
-                *reinterpret_cast<uint4 *>(&sy[flat_unit(lane, c) * 4]) =
-                    make_uint4(y[4 * c], y[4 * c + 1], y[4 * c + 2], y[4 * c + 3]);
+            for (int c = 0; c < V / 4; ++c)
+                *reinterpret_cast<uint4 *>(&sx[flat_unit(lane, c) * 4]) =
+                    make_uint4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
         }
 
         // Segmented scan across the lanes of the lanes' open parts.
         bool fl = keep != 0xFFFFFFFFu;
         lacc_t xs = acc;
+        if constexpr (kMM) {
+            // local (key, V - t) word -> (key, ~row code)
+            if (acc != 0) xs = (acc & 0xFFFFFFFF00000000ull) | ~(rel0 + (uint32_t)V - (uint32_t)acc);
+        }
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             const int src = (lane - o) & 63;
@@ -727,16 +780,27 @@ __global__ __launch_bounds__(256) void seg_reduce_flat(const KArgs a) {
         }
         const acc_t cin = fx ? widen(ex) : acomb(cm, widen(ex));
         sc[lane] = R::to_slot(cin);
-        {
-            // The part of the open segment after the chunk; none when the
-            // chunk's last end closes its last row (an end at position CH
-            // has no reset bit inside the chunk).
-            const lacc_t x63 = lane_get(xs, 63);
-            const bool f63 = lane_get(fl, 63);
-            carry = to_max(f63 ? widen(x63) : acomb(cm, widen(x63)));
-            if (ne > 0 && __builtin_amdgcn_readfirstlane(se[ne - 1]) == (uint32_t)rows) carry = R::id();
-        }
         wave_lds_sync();
+
+        // Value (maximum domain) of the part of a segment inside this chunk
+        // that ends right before element p >= 1, given the previous end pp
+        // (kNone: the segment began before the chunk).
+        const uint32_t relc = (uint32_t)(jc - sh.j0);
+        auto piece = [&](uint32_t p, uint32_t pp) __attribute__((always_inline)) -> acc_t {
+            const uint32_t l2 = (p - 1) >> 5, t2 = (p - 1) & 31;
+            acc_t v;
+            if constexpr (kMM) {
+                const uint32_t tb = (uint32_t)V - sp[l2 * V + t2];  // the best element of the piece
+                const uint32_t bits = sx[flat_unit((int)l2, (int)(tb >> 2)) * 4 + (int)(tb & 3)];
+                v = mm_word(bits, relc + l2 * V + tb);
+            } else {
+                const uint32_t b = sx[flat_unit((int)l2, (int)(t2 >> 2)) * 4 + (int)(t2 & 3)];
+                if constexpr (kSumF) v = (double)__uint_as_float(b);
+                else v = b;
+            }
+            if (pp == kNone || pp < (l2 << 5)) v = acomb(R::from_slot(sc[l2]), v);
+            return v;
+        };
 
         // One lane per end: look up the segment's value and store it.
         for (int q = lane; q < ne; q += 64) {
@@ -749,12 +813,7 @@ __global__ __launch_bounds__(256) void seg_reduce_flat(const KArgs a) {
             } else if (p == 0) {
                 v = R::from_slot(sc[0]);  // ends where the chunk starts
             } else {
-                const uint32_t l2 = (p - 1) >> 5, t2 = (p - 1) & 31;
-                const int u = flat_unit((int)l2, (int)(t2 >> 2)) * 4 + (int)(t2 & 3);
-                if constexpr (kMM) v = ((uint64_t)sx[u] << 32) | sy[u];
-                else if constexpr (kSumF) v = (double)__uint_as_float(sx[u]);
-                else v = sx[u];
-                if (pp == kNone || pp < (l2 << 5)) v = acomb(R::from_slot(sc[l2]), v);
+                v = piece(p, pp);
             }
             v = to_max(v);
             if (sh.split_head && seg == sh.i0) {
@@ -764,6 +823,13 @@ __global__ __launch_bounds__(256) void seg_reduce_flat(const KArgs a) {
                 if constexpr (OP == OP_MEAN) len = off[seg + 1] - off[seg];
                 store_final<DT, OP, 1>(a, seg, 0, &v, base, len);
             }
+        }
+        // The part of the open segment after the chunk: the chunk's rows
+        // after its last end (none when the last end closes the last row).
+        {
+            const uint32_t last = ne > 0 ? __builtin_amdgcn_readfirstlane(se[ne - 1]) : kNone;
+            if (last == (uint32_t)rows) carry = R::id();
+            else if (rows > 0) carry = to_max(piece((uint32_t)rows, last));
         }
         ic = icn;
         jc = jcn;
@@ -991,9 +1057,9 @@ extern "C" int64_t segred_get_shares(int32_t dtype, int32_t op, int64_t feat) {
     }
 }
 
-extern "C" int segred_reduce(const void *values, int32_t dtype, int64_t feat, const int64_t *offsets,
-                             int64_t num_segments, int32_t op, void *out, int64_t *arg_out,
-                             hipStream_t stream) {
+static int reduce_impl(const void *values, int32_t dtype, int64_t feat, const int64_t *offsets,
+                       int64_t num_segments, const int64_t *num_segments_dev, int32_t op, void *out,
+                       int64_t *arg_out, hipStream_t stream) {
     if (num_segments < 0 || feat < 1 || dtype < SEGRED_U32 || dtype > SEGRED_F32 || op < SEGRED_SUM ||
         op > SEGRED_MEAN)
         return SEGRED_ERR_INVALID_ARGUMENT;
@@ -1001,7 +1067,8 @@ extern "C" int segred_reduce(const void *values, int32_t dtype, int64_t feat, co
     if (feat > kMaxFeat) return SEGRED_ERR_UNSUPPORTED;  // 32-bit in-chunk byte offsets
     if (num_segments == 0) return SEGRED_OK;
     if (!values || !offsets || !out) return SEGRED_ERR_INVALID_ARGUMENT;
-    if (!aligned(values, 4) || !aligned(out, 4) || !aligned(offsets, 8) || (arg_out && !aligned(arg_out, 8)))
+    if (!aligned(values, 4) || !aligned(out, 4) || !aligned(offsets, 8) || (arg_out && !aligned(arg_out, 8)) ||
+        !aligned(num_segments_dev, 8))
         return SEGRED_ERR_INVALID_ARGUMENT;
     if (op == SEGRED_SUM || op == SEGRED_MEAN) arg_out = nullptr;
 
@@ -1009,8 +1076,22 @@ extern "C" int segred_reduce(const void *values, int32_t dtype, int64_t feat, co
     k.values = static_cast<const uint32_t *>(values);
     k.offsets = offsets;
     k.S = num_segments;
+    k.S_dev = num_segments_dev;
     k.F = feat;
     k.out = static_cast<uint32_t *>(out);
     k.arg = arg_out;
     return dispatch(dtype, op, k, stream);
+}
+
+extern "C" int segred_reduce(const void *values, int32_t dtype, int64_t feat, const int64_t *offsets,
+                             int64_t num_segments, int32_t op, void *out, int64_t *arg_out,
+                             hipStream_t stream) {
+    return reduce_impl(values, dtype, feat, offsets, num_segments, nullptr, op, out, arg_out, stream);
+}
+
+extern "C" int segred_reduce_device_count(const void *values, int32_t dtype, int64_t feat, const int64_t *offsets,
+                                          const int64_t *num_segments, int64_t max_segments, int32_t op, void *out,
+                                          int64_t *arg_out, hipStream_t stream) {
+    if (!num_segments) return SEGRED_ERR_INVALID_ARGUMENT;
+    return reduce_impl(values, dtype, feat, offsets, max_segments, num_segments, op, out, arg_out, stream);
 }

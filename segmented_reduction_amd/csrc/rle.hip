@@ -109,39 +109,77 @@ __device__ __forceinline__ int64_t block_inclusive_scan(int64_t v, int64_t *s_tm
 }
 
 // One workgroup: run index of each tile's first start (exclusive scan of the
-// counts), the start following each tile (scan of first starts from the
-// right), the run count and offsets[count] = n.
+// tile counts) and the first start after each tile (exclusive minimum of the
+// tiles' first starts, from the right).  Each thread takes K consecutive
+// tiles of a batch of 1024 * K, so a batch costs one round of loads issued
+// together, a short serial pass per thread and one block-wide scan.
+constexpr int kScanPer = 4;
 __global__ __launch_bounds__(kScanThreads) void rle_scan(int64_t tiles, int64_t n, const int64_t *tile_count,
                                                          const int64_t *tile_first, int64_t *tile_base,
                                                          int64_t *tile_next, int64_t *count, int64_t *offsets) {
+    constexpr int K = kScanPer;
+    constexpr int64_t kBatch = (int64_t)kScanThreads * K;
     __shared__ int64_t s_tmp[2 * (kScanThreads / 64)];
-    __shared__ int64_t s_incl[kScanThreads];
     const int tid = threadIdx.x;
+
+    // Left to right: run index of each tile's first start.
     int64_t running = 0;
-    for (int64_t b = 0; b < tiles; b += kScanThreads) {
-        const int64_t t = b + tid;
-        const int64_t v = t < tiles ? tile_count[t] : 0;
+    for (int64_t b = 0; b < tiles; b += kBatch) {
+        int64_t v[K], in[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const int64_t t = b + (int64_t)tid * K + j;
+            v[j] = tile_count[t < tiles ? t : 0];
+            if (t >= tiles) v[j] = 0;
+        }
+        int64_t acc = 0;
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            in[j] = acc;
+            acc += v[j];
+        }
         int64_t total;
-        const int64_t incl = block_inclusive_scan<false>(v, s_tmp, total);
-        if (t < tiles) tile_base[t] = running + incl - v;
+        const int64_t ex = block_inclusive_scan<false>(acc, s_tmp, total) - acc;
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const int64_t t = b + (int64_t)tid * K + j;
+            if (t < tiles) tile_base[t] = running + ex + in[j];
+        }
         running += total;
     }
-    // Right to left: thread order runs from the last tile down, so the
-    // inclusive min over threads 0..tid is the min over tiles t..(end of this
-    // block of tiles); the exclusive form, joined with the tiles further
-    // right, is the first run start after tile t.
+
+    // Right to left: thread order runs from the last tile down (reversed
+    // position r = tiles - 1 - t), so the exclusive minimum over reversed
+    // positions before r, joined with the tiles further right, is the first
+    // run start after tile t.
     int64_t right = n;
-    for (int64_t b = 0; b < tiles; b += kScanThreads) {
-        const int64_t t = tiles - 1 - (b + tid);
-        const int64_t v = t >= 0 ? tile_first[t] : INT64_MAX;
+    for (int64_t b = 0; b < tiles; b += kBatch) {
+        int64_t w[K], in[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const int64_t t = tiles - 1 - (b + (int64_t)tid * K + j);
+            w[j] = tile_first[t >= 0 ? t : 0];
+            if (t < 0) w[j] = INT64_MAX;
+        }
+        int64_t m = INT64_MAX;
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            in[j] = m;
+            m = w[j] < m ? w[j] : m;
+        }
         int64_t total;
-        const int64_t incl = block_inclusive_scan<true>(v, s_tmp, total);
-        s_incl[tid] = incl;
-        __syncthreads();
-        if (t >= 0) {
-            int64_t ex = tid > 0 ? s_incl[tid - 1] : INT64_MAX;
-            ex = ex < right ? ex : right;
-            tile_next[t] = ex < n ? ex : n;
+        const int64_t incl = block_inclusive_scan<true>(m, s_tmp, total);
+        // exclusive over the threads before this one: lane - 1 of this wave,
+        // or for lane 0 the running minimum of the earlier waves (still in
+        // s_tmp after the block scan)
+        int64_t ex = lane_get(incl, ((tid & 63) - 1) & 63);
+        if ((tid & 63) == 0) ex = tid == 0 ? INT64_MAX : s_tmp[kScanThreads / 64 + (tid >> 6) - 1];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const int64_t t = tiles - 1 - (b + (int64_t)tid * K + j);
+            int64_t e = in[j] < ex ? in[j] : ex;
+            e = e < right ? e : right;
+            if (t >= 0) tile_next[t] = e < n ? e : n;
         }
         __syncthreads();
         right = total < right ? total : right;

@@ -77,6 +77,20 @@ def test_reduce_argument_checks(args, expect):
 
 
 @pytest.mark.parametrize("args,expect", [
+    # (values, dtype, feat, offsets, count_dev, max_S, op, out, arg) -> status
+    ((FAKE, 2, 1, FAKE, None, 4, 0, FAKE, None), 1),   # null device count
+    ((FAKE, 2, 1, FAKE, FAKE + 4, 4, 0, FAKE, None), 1),  # device count not 8-byte aligned
+    ((FAKE, 2, 1, FAKE, FAKE, -1, 0, FAKE, None), 1),  # negative bound
+    ((FAKE, 0, 1, FAKE, FAKE, 4, 3, FAKE, None), 2),   # MEAN of u32
+    ((FAKE, 2, 1, None, FAKE, 4, 0, FAKE, None), 1),   # null offsets
+    ((None, 2, 1, None, FAKE, 0, 0, None, None), 0),   # bound 0 enqueues nothing
+])
+def test_reduce_device_count_argument_checks(args, expect):
+    lib = _lib()
+    assert lib.segred_reduce_device_count(*args, None) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
     # (keys, n, values, lengths, offsets, count) -> status
     ((FAKE, -1, FAKE, FAKE, FAKE, FAKE), 1),
     ((FAKE, 2 ** 32, FAKE, FAKE, FAKE, FAKE), 1),      # lengths are uint32
