@@ -9,33 +9,34 @@
 // Work partition.  The rows and the segment ends are merged into one
 // sequence (a segment's rows, then its end), the merge-path view of
 // Merrill & Garland's merge-based SpMV that the graph-reduce README cites.
-// The sequence is cut into NW equal shares, one per resident wave; a wave
-// finds its share's (segment, row) coordinates with a search over the
-// offsets (a shared first round in LDS, then 256-way rounds).  Long or skewed
-// segments are therefore spread over many waves instead of serialising on
-// one.
+// The sequence is cut into NW equal shares, one per resident wave; the four
+// waves of a workgroup find their shares' (segment, row) coordinates with a
+// joint search over the offsets.  Long or skewed segments are therefore
+// spread over many waves instead of serialising on one.
 //
-// Inside a share the wave walks chunks of CH items.  For rows of F >= 2
-// features each lane owns one feature; a chunk's rows are split into G
-// groups of V consecutive rows (G = 1 for F >= 64, where segment control is
-// wave-uniform).  For 1-D values each lane owns 16 consecutive elements,
-// staged through LDS.  A group walks its rows in order, finishing every
-// segment that ends inside it; a segmented scan over the groups (cross-lane
-// moves) completes segments cut by group and chunk boundaries.  Segments cut
-// by a share boundary leave one partial per share in scratch; a second kernel
-// combines them in share order.  No atomics are used anywhere, and every
-// summation order is a fixed function of the offsets and NW, so results
-// repeat bit for bit.
+// Inside a share the wave walks chunks.  For rows of F >= 2 features each
+// lane owns one feature; a chunk's rows are split into G groups of V
+// consecutive rows (G = 1 for F >= 64, where segment control is
+// wave-uniform); a group walks its rows in order, finishing every segment
+// that ends inside it, and a segmented scan over the groups completes the
+// segments cut by group and chunk boundaries.  For 1-D values a chunk is 2048
+// elements staged through LDS, 32 consecutive ones per lane, reduced by one
+// branch-free pass per lane over reset masks (see seg_reduce_flat).  Segments
+// cut by a share boundary leave one partial per share in scratch; a second
+// kernel combines them in share order.  Every summation order is a fixed
+// function of the offsets and NW, so results repeat bit for bit; no atomic
+// operation touches global memory (the only atomic is a bit-OR in LDS).
 //
 // Memory: rows are read through buffer descriptors that cover exactly the
 // valid part of a chunk (reads past it return 0, so no clamping), and the
-// next chunk streams into each register as soon as the current chunk has
-// consumed it.
+// next chunk streams into registers while the current one is processed.
 //
-// Accumulators: float sums in float64 (rounded to float32 once), integer sums
-// in wrapping uint32, min/max as a 64-bit word (order key << 32 | row code)
-// whose integer max/min picks the extremum and, on equal keys, the lowest row
-// (the packed value/row word of the graph-reduce README's "Method").
+// Accumulators: float sums in float64 (rounded to float32 once; the 1-D
+// kernel adds runs of <= 32 elements and a 64-way tree of them in float32
+// first), integer sums in wrapping uint32, min/max as a 64-bit word (order
+// key << 32 | row code) whose integer max/min picks the extremum and, on
+// equal keys, the lowest row (the packed value/row word of the graph-reduce
+// README's "Method").
 #include <map>
 #include <mutex>
 #include <type_traits>
