@@ -268,6 +268,7 @@ __device__ __forceinline__ Share find_share(const int64_t *off, int64_t S, int64
     __syncthreads();
     Bracket b0 = bracket(s_probe, L, stepB, H, o0, d0, lane);
     Bracket b1 = bracket(s_probe, L, stepB, H, o0, d1, lane);
+    __syncthreads();  // the probe array is free from here on
 
     // Round C: 256-way rounds on both diagonals of this wave.
     int64_t lo0 = b0.lo, hi0 = b0.hi, k0lo = b0.klo;
@@ -605,7 +606,7 @@ void seg_reduce_flat(const KArgs a) {
     using R = Red<DT, OP>;
     using acc_t = typename R::acc_t;
     constexpr bool kSumF = R::kSumF, kMM = R::kMinMax;
-    constexpr int V = 32, CH = 64 * V, EC = 128, NB = EC / 64;
+    constexpr int V = 32, CH = 64 * V, EC = 512, NB = 2;
     constexpr uint32_t kNone = 0xFFFFFFFFu;
     // in-chunk value: float for float sums, else the accumulator itself
     // (min/max in the "maximum" domain)
@@ -635,10 +636,12 @@ void seg_reduce_flat(const KArgs a) {
 
     __shared__ __attribute__((aligned(16))) uint32_t s_x[4][CH];            // elements (sums: then running values)
     __shared__ __attribute__((aligned(16))) uint32_t s_p[4][kMM ? CH / 4 : 4];  // min/max: position bytes
-    __shared__ uint32_t s_e[4][EC];                                         // end positions in the chunk
+    __shared__ uint16_t s_e[4][EC];                                         // end positions in the chunk
     __shared__ uint32_t s_m[4][64];                                         // reset masks
     __shared__ uint64_t s_c[4][64];                                         // carried-in part per lane
-    __shared__ int64_t s_probe[256];
+    // the partition search's probes share wave 0's staging area (the search
+    // ends with a barrier, before any wave stages a chunk)
+    int64_t *s_probe = reinterpret_cast<int64_t *>(s_x[0]);
 
     const int wid = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -649,7 +652,7 @@ void seg_reduce_flat(const KArgs a) {
     const int64_t o0 = sh.o0, base = sh.o0 + sh.j0;
     uint32_t *sx = s_x[wid];
     uint8_t *sp = reinterpret_cast<uint8_t *>(s_p[wid]);
-    uint32_t *se = s_e[wid];
+    uint16_t *se = s_e[wid];
     uint32_t *sm = s_m[wid];
     uint64_t *sc = s_c[wid];
 
@@ -680,21 +683,23 @@ void seg_reduce_flat(const KArgs a) {
         wave_lds_sync();
         int ne = 0;
         bool more = true;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            if (more) {
-                const int k = b * 64 + lane;
-                const int64_t e = E[b] - o0 - jc;
-                const bool cond = k < ends_avail && e <= rows_avail;
-                const int cnt = popc64(ballot(cond));
-                if (cond) {
-                    se[k] = (uint32_t)e;
-                    if (e < CH) lds_or(&sm[e >> 5], 1u << (e & 31));
-                }
-                ne += cnt;
-                more = cnt == 64;
+        auto take = [&](int b, int64_t eabs) __attribute__((always_inline)) {
+            const int k = b * 64 + lane;
+            const int64_t e = eabs - o0 - jc;
+            const bool cond = k < ends_avail && e <= rows_avail;
+            const int cnt = popc64(ballot(cond));
+            if (cond) {
+                se[k] = (uint16_t)e;
+                if (e < CH) lds_or(&sm[e >> 5], 1u << (e & 31));
             }
-        }
+            ne += cnt;
+            more = cnt == 64;
+        };
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            if (more) take(b, E[b]);
+        // dense stretches: further ends, fetched on demand
+        for (int b = NB; more && b < EC / 64; ++b) take(b, off[min(ic + 1 + b * 64 + lane, S)]);
         wave_lds_sync();
         // With EC ends the chunk stops at the last of them.
         const int rows = ne == EC ? (int)__builtin_amdgcn_readfirstlane(se[EC - 1]) : (int)rows_avail;

@@ -216,13 +216,16 @@ def test_three_dimensional_values_flatten_features():
 
 def _edge_offsets(chunk=2048):
     """1-D lengths that put segment ends on chunk edges for a single share
-    starting at row 0: ends exactly at multiples of the chunk, a run of 300
-    empty segments inside one chunk and another right on a chunk edge (more
-    ends than one chunk takes), a segment spanning several chunks, and a
+    starting at row 0: ends exactly at multiples of the chunk, runs of 300
+    empty segments inside a chunk and on a chunk edge, a segment spanning
+    several chunks, stretches with more ends than one chunk takes, and a
     last segment ending inside a partial chunk."""
     lengths = [chunk, chunk, 5, chunk - 5, 2 * chunk, 1, chunk - 1]
     lengths += [0] * 300 + [7, 100] + [0] * 300 + [chunk - 107]
     lengths += [3 * chunk + 17, chunk - 17] + [0] * 5 + [11, 0, 0, 29]
+    # more ends than one chunk holds: 700 empty segments at one position,
+    # then 1500 one-row segments and 600 two-row ones
+    lengths += [0] * 700 + [1] * 1500 + [2] * 600 + [chunk // 2]
     return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
 
 
