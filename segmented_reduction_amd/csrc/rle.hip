@@ -29,18 +29,30 @@ struct TileKeys {
     bool head[kRleKeysPerThread];
 };
 
+// All loads are unconditional buffer loads, issued together: the tile's keys
+// through a descriptor limited to the keys that exist (reads past n return
+// 0), and for each wave's first position the key before it (one address for
+// the whole wave; for position 0 of the input the offset wraps out of range
+// and the value is not used).
 __device__ __forceinline__ void load_tile(const uint32_t *keys, int64_t n, int64_t start, int tid, TileKeys &t) {
-    const int lane = tid & 63;
+    const int lane = tid & 63, wid = tid >> 6;
+    const int64_t avail = min((int64_t)kRleTile, n - start);
+    const int64_t back = start > 0 ? 1 : 0;
+    const auto rs = make_rsrc(keys + start, (uint32_t)(avail * 4));
+    const auto rp = make_rsrc(keys + start - back, (uint32_t)((avail + back) * 4));
+    uint32_t p0[kRleKeysPerThread];
 #pragma unroll
     for (int u = 0; u < kRleKeysPerThread; ++u) {
-        const int64_t i = start + u * kRleThreads + tid;
-        t.k[u] = i < n ? keys[i] : 0u;
+        t.k[u] = ld32(rs, (uint32_t)((u * kRleThreads + tid) * 4), 0);
+        p0[u] = ld32(rp, (uint32_t)((u * kRleThreads + wid * 64 - 1 + (int)back) * 4), 0);
     }
 #pragma unroll
     for (int u = 0; u < kRleKeysPerThread; ++u) {
         const int64_t i = start + u * kRleThreads + tid;
+        // the cross-lane read runs in every lane (a disabled source lane
+        // would read as 0); lane 0 then takes the loaded key instead
         uint32_t prev = lane_get(t.k[u], (lane - 1) & 63);
-        if (lane == 0 && i > 0 && i < n) prev = keys[i - 1];
+        if (lane == 0) prev = p0[u];
         t.head[u] = i < n && (i == 0 || t.k[u] != prev);
     }
 }
