@@ -983,8 +983,8 @@ static const void *pick_kernel(int64_t feat) {
     case 4: return reinterpret_cast<const void *>(&seg_reduce_rows<DT, OP, 4, 16>);
     case 8: return reinterpret_cast<const void *>(&seg_reduce_rows<DT, OP, 8, 16>);
     case 16: return reinterpret_cast<const void *>(&seg_reduce_rows<DT, OP, 16, 16>);
-    case 32: return reinterpret_cast<const void *>(&seg_reduce_rows<DT, OP, 32, 32>);
-    default: return reinterpret_cast<const void *>(&seg_reduce_rows<DT, OP, 64, 32>);
+    case 32: return reinterpret_cast<const void *>(&seg_reduce_rows<DT, OP, 32, 24>);
+    default: return reinterpret_cast<const void *>(&seg_reduce_rows<DT, OP, 64, 24>);
     }
 }
 
