@@ -15,7 +15,7 @@ cache cannot serve them and the rate is an HBM rate.
 Prints ONE JSON line: the effective bandwidth (algorithmic bytes / wall time
 of the K timed steps), Gelem/s, the roofline of the dominant kernel (its
 algorithmic bytes per launch / its average duration, from kernel-stamped HIP
-events on its stream over a second pass of the same K steps) and the CPU
+stop events on its stream over a second pass of the same K steps) and the CPU
 oracle timed on the host on the same workload.
 """
 from __future__ import annotations
@@ -85,6 +85,7 @@ class ReduceWorkload(Workload):
         self.off = torch.from_numpy(self.host_off).cuda()
         self.outs = {}
         self.calls = [(op, op) for op in ops]
+        self.kernels_per_step = 2 * len(ops)  # two kernels per call
         self.ncalls = 0
 
     def step(self, i):
@@ -116,6 +117,7 @@ class RleWorkload(Workload):
         self.sets = [(k, pu, pi)] + [(k.clone(), pu.clone(), pi.clone()) for _ in range(copies - 1)]
         self.n = int(cfg["keys"].size)
         self.calls = [("sum_u32", "sum"), ("min_i32", "min")]
+        self.kernels_per_step = 3 + 2 * 2  # three RLE kernels, two per reduce call
         # the run count of this input (fixed by the seed), for the byte count
         _, _, _, cnt = sr.offsets_from_rle(k)
         self.count = int(cnt.item())
@@ -294,8 +296,9 @@ def main():
     print(f"[bench] generating {args.config} ...", file=sys.stderr, flush=True)
     wl, cfg = build_workload(args.config, sr, torch)
     torch.cuda.synchronize()
-    if args.steps * len(wl.calls) > 4096:  # launches the timing hook keeps
-        args.steps = 4096 // len(wl.calls)
+    # launches the timing record keeps: at most 4 kernels per call here
+    if args.steps * len(wl.calls) * 4 > 8192:
+        args.steps = 8192 // (4 * len(wl.calls))
 
     for i in range(args.warmup):
         wl.step(i)
@@ -309,18 +312,27 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
-    # Kernel durations for the roofline: the same K steps again, with the
-    # streaming kernel launched with a pair of HIP events that the runtime
-    # stamps with that kernel's start and end on its own stream.  Attaching
-    # the events idles the GPU for a few microseconds around each launch, so
-    # this pass is kept out of the wall-clock figure above.
+    # Kernel durations for the roofline: the same K steps again, with every
+    # library kernel launched with a HIP event that the runtime stamps when the
+    # kernel ends on its stream; a streaming kernel's duration is the time
+    # from the end of the kernel before it (the kernels run back to back).
+    # This pass is kept out of the wall-clock figure above.
+    # Stamping an event at a kernel's end leaves the GPU idle for a few
+    # microseconds before the next kernel starts; that idle time is inside
+    # each stop-to-stop duration.  It is taken out per launch as the extra
+    # wall time of this pass over the untimed one, divided by the number of
+    # kernel launches (the kernels themselves are the same).
     sr.timing_enable(True)
     sr.timing_read()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
     for i in range(args.steps):
         wl.step(args.warmup + args.steps + i)
     torch.cuda.synchronize()
+    t3 = time.perf_counter()
     total_ms, launches, each = sr.timing_read()
     sr.timing_enable(False)
+    gap_ms = max(0.0, ((t3 - t2) - (t1 - t0)) * 1e3 / (args.steps * wl.kernels_per_step))
 
     elapsed = t1 - t0
     ms_per_step = elapsed * 1e3 / args.steps
@@ -332,12 +344,14 @@ def main():
     ncalls = len(wl.calls)
     kernels = {}
     for j, (label, op) in enumerate(wl.calls):
-        times = each[j::ncalls]
+        times = [t for t in each[j::ncalls] if t >= 0]  # -1: first launch, nothing before it
         if not times:
             continue
-        avg_ms = sum(times) / len(times)
+        raw_ms = sum(times) / len(times)
+        avg_ms = raw_ms - gap_ms
         b = wl.call_bytes(label)
-        kernels[label] = {"avg_us": round(avg_ms * 1e3, 2), "launches": len(times), "bytes": b,
+        kernels[label] = {"avg_us": round(avg_ms * 1e3, 2), "event_us": round(raw_ms * 1e3, 2),
+                          "stamp_gap_us": round(gap_ms * 1e3, 2), "launches": len(times), "bytes": b,
                           "GBps": round(b / (avg_ms * 1e-3) / 1e9, 1),
                           "frac": round(b / (avg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
@@ -347,8 +361,9 @@ def main():
     roofline = {"bound": "hbm", "achieved": dk["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": dk["frac"], "traffic": traffic, "kernel": f"seg_reduce_pass1 ({dominant})",
                 "algorithmic_bytes_per_launch": dk["bytes"], "avg_launch_us": dk["avg_us"],
-                "timing": "kernel-stamped HIP events (hipExtLaunchKernel) on the launch stream, "
-                          "a second pass of the same K steps"}
+                "timing": "kernel-stamped HIP stop events (hipExtLaunchKernel) on the launch stream, end of "
+                          "previous kernel to end of this one, a second pass of the same K steps, minus the "
+                          "per-launch idle time the stamping adds (extra wall time of that pass / launches)"}
 
     cpu = None
     parity = None

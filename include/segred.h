@@ -166,14 +166,18 @@ int64_t segred_get_shares(int32_t dtype, int32_t op, int64_t feat);
 
 /*
  * Kernel timing (instrumentation for benchmarks).  While enabled, every
- * segred_reduce call launches its streaming (first) kernel with a pair of
- * HIP events that the runtime stamps with that kernel's own start and end
- * (hipExtLaunchKernel), so a duration is the kernel's execution time.  segred_timing_read waits for the recorded
- * events, returns the summed duration in milliseconds and the number of
- * timed launches, writes the first `capacity` per-launch durations (ms, in
- * launch order) to the host array `each_ms` (may be NULL when capacity is
- * 0), and clears the record.  Up to 4096 launches are kept; later ones are
- * not timed.  Host-side state, process-wide, not thread-safe.
+ * kernel the library launches carries a HIP event that the runtime stamps
+ * when that kernel ends (hipExtLaunchKernel).  segred_timing_read waits for
+ * the recorded events and reports, for every streaming (first) kernel of a
+ * segred_reduce call, the time from the end of the launch recorded before it
+ * to its own end (-1 for the first launch of the record, which has none):
+ * when the library's kernels run back to back on one stream (nothing else
+ * queued in between), this is the streaming kernel's execution time.  It
+ * returns the summed duration of the timed launches in milliseconds and the
+ * number of streaming launches, writes the first `capacity` durations (ms,
+ * in launch order) to the host array `each_ms` (may be NULL when capacity is
+ * 0), and clears the record.  Up to 8192 launches are kept;
+ * later ones are not timed.  Host-side state, process-wide, not thread-safe.
  */
 int segred_timing_enable(int enable);
 int segred_timing_read(double *total_ms, int64_t *launches, float *each_ms, int64_t capacity);

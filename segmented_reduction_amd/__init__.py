@@ -191,7 +191,8 @@ def timing_enable(enable: bool = True):
 
 
 def timing_read(capacity: int = 4096):
-    """(total ms, launches, per-launch ms list) of the streaming kernel since the last read."""
+    """(total ms, launches, per-launch ms list) of the streaming kernels since the last read:
+    each is the time from the end of the kernel launched before it (-1 for the first)."""
     ms = ctypes.c_double(0.0)
     n = ctypes.c_int64(0)
     each = (ctypes.c_float * max(capacity, 1))()

@@ -36,11 +36,12 @@ hipMemPool_t pool_for_current_device() {
     return g_pools[dev];
 }
 
-constexpr int kMaxTimed = 4096;
+constexpr int kMaxTimed = 8192;  // kernel launches recorded between reads
 struct Timing {
     bool on = false;
     int used = 0;
-    hipEvent_t ev[2 * kMaxTimed] = {};
+    hipEvent_t ev[kMaxTimed] = {};   // stop event of each launch, in launch order
+    bool streaming[kMaxTimed] = {};  // launch i is a streaming (first) kernel
     bool created = false;
 };
 Timing g_timing;
@@ -116,12 +117,11 @@ int scratch_acquire(ScratchLease &lease, size_t bytes, hipStream_t stream) {
 
 bool timing_on() { return g_timing.on; }
 
-void timing_events(hipEvent_t *start, hipEvent_t *stop) {
-    *start = *stop = nullptr;
-    if (!g_timing.on || g_timing.used >= kMaxTimed) return;
+hipEvent_t timing_stop(bool streaming) {
+    if (!g_timing.on || g_timing.used >= kMaxTimed) return nullptr;
     const int slot = g_timing.used++;
-    *start = g_timing.ev[2 * slot];
-    *stop = g_timing.ev[2 * slot + 1];
+    g_timing.streaming[slot] = streaming;
+    return g_timing.ev[slot];
 }
 
 int64_t shares_override() { return g_shares.load(std::memory_order_relaxed); }
@@ -149,8 +149,11 @@ extern "C" int segred_set_shares(int64_t shares) {
 
 extern "C" int segred_timing_enable(int enable) {
     if (enable && !g_timing.created) {
-        for (int i = 0; i < 2 * kMaxTimed; ++i)
-            if (hipEventCreate(&g_timing.ev[i]) != hipSuccess) return SEGRED_ERR_HIP;
+        // no system-scope cache writeback at each stamp: it would slow the
+        // kernels being timed (only this process reads the timestamps)
+        for (int i = 0; i < kMaxTimed; ++i)
+            if (hipEventCreateWithFlags(&g_timing.ev[i], hipEventDisableSystemFence) != hipSuccess)
+                return SEGRED_ERR_HIP;
         g_timing.created = true;
     }
     g_timing.on = enable != 0;
@@ -161,15 +164,20 @@ extern "C" int segred_timing_enable(int enable) {
 extern "C" int segred_timing_read(double *total_ms, int64_t *launches, float *each_ms, int64_t capacity) {
     if (!total_ms || !launches || capacity < 0 || (capacity > 0 && !each_ms)) return SEGRED_ERR_INVALID_ARGUMENT;
     double sum = 0.0;
+    int64_t n = 0;
     for (int i = 0; i < g_timing.used; ++i) {
-        if (hipEventSynchronize(g_timing.ev[2 * i + 1]) != hipSuccess) return SEGRED_ERR_HIP;
-        float ms = 0.f;
-        if (hipEventElapsedTime(&ms, g_timing.ev[2 * i], g_timing.ev[2 * i + 1]) != hipSuccess) return SEGRED_ERR_HIP;
-        if (i < capacity) each_ms[i] = ms;
-        sum += ms;
+        if (!g_timing.streaming[i]) continue;
+        if (hipEventSynchronize(g_timing.ev[i]) != hipSuccess) return SEGRED_ERR_HIP;
+        float ms = -1.f;  // no launch recorded before this one
+        if (i > 0) {
+            if (hipEventElapsedTime(&ms, g_timing.ev[i - 1], g_timing.ev[i]) != hipSuccess) return SEGRED_ERR_HIP;
+            sum += ms;
+        }
+        if (n < capacity) each_ms[n] = ms;
+        ++n;
     }
     *total_ms = sum;
-    *launches = g_timing.used;
+    *launches = n;
     g_timing.used = 0;
     return SEGRED_OK;
 }

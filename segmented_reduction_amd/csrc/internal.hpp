@@ -42,11 +42,13 @@ struct ScratchLease {
 };
 int scratch_acquire(ScratchLease &lease, size_t bytes, hipStream_t stream);
 
-// Launch timing of the streaming kernel (segred_timing_enable): the next
-// pair of events to hand to hipExtLaunchKernel, which stamps them with the
-// kernel's own start and end; both null when timing is off or the ring is full.
+// Launch timing (segred_timing_enable): while it is on, every kernel the
+// library launches carries a stop event that the runtime stamps when that
+// kernel ends (hipExtLaunchKernel); timing_stop returns the next one (null
+// when timing is off or the record is full).  A streaming kernel's duration
+// is the time from the end of the launch before it to its own end.
 bool timing_on();
-void timing_events(hipEvent_t *start, hipEvent_t *stop);
+hipEvent_t timing_stop(bool streaming);
 
 // Process-wide share override (0 = default).
 int64_t shares_override();

@@ -1010,14 +1010,11 @@ static int run(KArgs k, hipStream_t st) {
     k.tval = k.hval + (size_t)nw * (size_t)k.F;
 
     const dim3 grid((unsigned)(nw / 4)), block(256);
-    hipEvent_t t0, t1;
-    timing_events(&t0, &t1);
     void *params[] = {&k};
-    hipError_t e = hipExtLaunchKernel(kernel, grid, block, params, 0, st, t0, t1, 0);
-    if (e == hipSuccess) {
-        hipLaunchKernelGGL((seg_reduce_pass2<DT, OP>), grid, block, 0, st, k);
-        e = hipGetLastError();
-    }
+    hipError_t e = hipExtLaunchKernel(kernel, grid, block, params, 0, st, nullptr, timing_stop(true), 0);
+    if (e == hipSuccess)
+        e = hipExtLaunchKernel(reinterpret_cast<const void *>(&seg_reduce_pass2<DT, OP>), grid, block, params, 0,
+                               st, nullptr, timing_stop(false), 0);
     return e == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
 }
 

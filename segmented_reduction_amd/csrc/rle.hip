@@ -273,12 +273,13 @@ extern "C" int segred_offsets_from_rle(const uint32_t *sorted_keys, int64_t n, u
     int64_t *tnext = tbase + tiles;
 
     if (tiles > 0)
-        hipLaunchKernelGGL(rle_count, dim3((unsigned)tiles), dim3(kRleThreads), 0, stream, sorted_keys, n, tcount,
-                           tfirst);
-    hipLaunchKernelGGL(rle_scan, dim3(1), dim3(kScanThreads), 0, stream, tiles, n, tcount, tfirst, tbase, tnext,
-                       count, offsets);
+        hipExtLaunchKernelGGL(rle_count, dim3((unsigned)tiles), dim3(kRleThreads), 0, stream, nullptr,
+                              timing_stop(false), 0, sorted_keys, n, tcount, tfirst);
+    hipExtLaunchKernelGGL(rle_scan, dim3(1), dim3(kScanThreads), 0, stream, nullptr, timing_stop(false), 0, tiles,
+                          n, (const int64_t *)tcount, (const int64_t *)tfirst, tbase, tnext, count, offsets);
     if (tiles > 0)
-        hipLaunchKernelGGL(rle_materialize, dim3((unsigned)tiles), dim3(kRleThreads), 0, stream, sorted_keys, n,
-                           tbase, tnext, values, lengths, offsets);
+        hipExtLaunchKernelGGL(rle_materialize, dim3((unsigned)tiles), dim3(kRleThreads), 0, stream, nullptr,
+                              timing_stop(false), 0, sorted_keys, n, (const int64_t *)tbase,
+                              (const int64_t *)tnext, values, lengths, offsets);
     return hipGetLastError() == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
 }
