@@ -186,17 +186,19 @@ __device__ __forceinline__ int count_le(const uint32_t *arr, int n, uint32_t x) 
 // key(i) = offsets[i] - o0 + i (strictly increasing in i).  The four waves
 // of a workgroup own four consecutive shares, so their five boundary
 // diagonals lie close together and the workgroup searches for them jointly:
-//   round A: 256 evenly spaced offsets (the same for every workgroup, so they
-//            stay cached), which also give o0 and the item count T;
-//   round B: 256 evenly spaced offsets over the range round A leaves for the
+//   round A: 1024 evenly spaced offsets (the same for every workgroup, so
+//            they stay cached), which also give o0 and the item count T;
+//   round B: 64 evenly spaced offsets over the range round A leaves for the
 //            workgroup's first and last diagonal;
-//   round C: each wave narrows its own two diagonals with 256-way rounds (one
-//            round unless the workgroup's range is wider than 65K ends).
-// Rounds A and B are one load per thread; round C reads a few consecutive
-// cache lines.  Every probe is clamped into the array and loaded
-// unconditionally (a load under a branch would be waited for inside the
-// branch).  The key of the last probe at or below a diagonal is kept, which
-// gives offsets[i(d)] without another load.
+//   round C: each wave narrows its own two diagonals with 256-way rounds over
+//            consecutive offsets (one round unless the workgroup's range is
+//            wider than 16K ends).
+// The workgroup-specific loads touch about 64 + 8 * 3 cache lines of the
+// offsets, most of which its waves read again for their segment ends.
+// Every probe is clamped into the array and loaded unconditionally (a load
+// under a branch would be waited for inside the branch).  The key of the
+// last probe at or below a diagonal is kept, which gives offsets[i(d)]
+// without another load.
 
 // A wave's share of the merged (rows + segment ends) sequence: items
 // [d0, d1), i.e. segment ends [i0, i1) and rows [j0, j1) (rows relative to
@@ -208,66 +210,77 @@ struct Share {
     bool has_tail;     // segment i1 has rows in the share and continues past it
 };
 
-// Where d falls among 256 probes p_k = lo + k * step (k < 255) and p_255 = hi
-// whose raw offsets are in s[]: the last probe with key <= d (there is one)
-// and its key; i(d) then lies in [lo', hi'].
+// Where d falls among N probes p_k = lo + k * step (k < N - 1) and
+// p_{N-1} = hi whose raw offsets are in s[]: the last probe with key <= d
+// (there is one) and its key; i(d) then lies in [lo', hi'].
 struct Bracket {
     int64_t lo, hi, klo;
 };
+template <int N>
 __device__ __forceinline__ int64_t probe_pos(int k, int64_t lo, int64_t step, int64_t hi) {
-    return k == 255 ? hi : min(lo + (int64_t)k * step, hi);
+    return k == N - 1 ? hi : min(lo + (int64_t)k * step, hi);
 }
+template <int N>
 __device__ __forceinline__ Bracket bracket(const int64_t *s, int64_t lo, int64_t step, int64_t hi, int64_t o0,
                                            int64_t d, int lane) {
+    constexpr int U = N / 64;
     int cnt = 0;
-    int64_t kk[4];
+    int64_t kk[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
         const int k = u * 64 + lane;
-        kk[u] = s[k] - o0 + probe_pos(k, lo, step, hi);
+        kk[u] = s[k] - o0 + probe_pos<N>(k, lo, step, hi);
         cnt += popc64(ballot(kk[u] <= d));
     }
     // cnt >= 1: probe 0 has key <= d
     const int last = cnt - 1, ul = last >> 6;
-    const int64_t klast = ul == 0 ? kk[0] : ul == 1 ? kk[1] : ul == 2 ? kk[2] : kk[3];
+    int64_t klast = kk[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u) klast = ul == u ? kk[u] : klast;
     Bracket b;
     b.klo = (int64_t)__builtin_amdgcn_readlane((uint32_t)klast, last & 63) |
             ((int64_t)__builtin_amdgcn_readlane((uint32_t)((uint64_t)klast >> 32), last & 63) << 32);
-    b.lo = probe_pos(last, lo, step, hi);
-    b.hi = cnt >= 256 ? hi : probe_pos(cnt, lo, step, hi) - 1;
+    b.lo = probe_pos<N>(last, lo, step, hi);
+    b.hi = cnt >= N ? hi : probe_pos<N>(cnt, lo, step, hi) - 1;
     if (b.hi < b.lo) b.hi = b.lo;
     return b;
 }
 
+constexpr int kProbesA = 1024, kProbesB = 64;
+
 __device__ __forceinline__ Share find_share(const int64_t *off, int64_t S, int64_t NW, int64_t wave, int lane,
-                                            int64_t *s_probe /* LDS [256], workgroup-wide */,
+                                            int64_t *s_probe /* LDS [kProbesA], workgroup-wide */,
                                             int64_t min_share = 1) {
     const int tid = threadIdx.x;
     const int wid = tid >> 6;
     const int64_t blk = (int64_t)blockIdx.x;
 
-    // Round A.
-    const int64_t stepA = (S + 254) / 255;
-    s_probe[tid] = off[probe_pos(tid, 0, stepA, S)];
+    // Round A (4 probes per thread).
+    const int64_t stepA = (S + kProbesA - 2) / (kProbesA - 1);
+#pragma unroll
+    for (int u = 0; u < kProbesA / 256; ++u) {
+        const int k = u * 256 + tid;
+        s_probe[k] = off[probe_pos<kProbesA>(k, 0, stepA, S)];
+    }
     __syncthreads();
     const int64_t o0 = s_probe[0];
-    const int64_t T = (s_probe[255] - o0) + S;
+    const int64_t T = (s_probe[kProbesA - 1] - o0) + S;
     // Shares of at least min_share items: small inputs use fewer waves (the
     // rest get empty shares and only write their header).
     const int64_t D = max((T + NW - 1) / NW, min_share);
     const int64_t g0 = min(blk * 4 * D, T), g4 = min((blk * 4 + 4) * D, T);
     const int64_t d0 = min((blk * 4 + wid) * D, T), d1 = min(d0 + D, T);
-    const Bracket a0 = bracket(s_probe, 0, stepA, S, o0, g0, lane);
-    const Bracket a4 = bracket(s_probe, 0, stepA, S, o0, g4, lane);
+    const Bracket a0 = bracket<kProbesA>(s_probe, 0, stepA, S, o0, g0, lane);
+    const Bracket a4 = bracket<kProbesA>(s_probe, 0, stepA, S, o0, g4, lane);
     __syncthreads();  // every wave is done with round A
 
     // Round B over [L, H], which holds i(d) for every diagonal of the group.
     const int64_t L = a0.lo, H = a4.hi;
-    const int64_t stepB = max((H - L + 254) / 255, (int64_t)1);
-    s_probe[tid] = off[probe_pos(tid, L, stepB, H)];
+    const int64_t stepB = max((H - L + kProbesB - 2) / (kProbesB - 1), (int64_t)1);
+    if (tid < kProbesB) s_probe[tid] = off[probe_pos<kProbesB>(tid, L, stepB, H)];
     __syncthreads();
-    Bracket b0 = bracket(s_probe, L, stepB, H, o0, d0, lane);
-    Bracket b1 = bracket(s_probe, L, stepB, H, o0, d1, lane);
+    Bracket b0 = bracket<kProbesB>(s_probe, L, stepB, H, o0, d0, lane);
+    Bracket b1 = bracket<kProbesB>(s_probe, L, stepB, H, o0, d1, lane);
     __syncthreads();  // the probe array is free from here on
 
     // Round C: 256-way rounds on both diagonals of this wave.
@@ -365,7 +378,7 @@ __global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
     const int c = lane % L;
     const int64_t wave = (int64_t)blockIdx.x * 4 + wid;
     const int64_t *off = a.offsets;
-    __shared__ int64_t s_probe[256];
+    __shared__ int64_t s_probe[kProbesA];
     const int64_t S = seg_count(a);
     const Share sh = find_share(off, S, a.NW, wave, lane, s_probe);
     const int64_t o0 = sh.o0, base = sh.o0 + sh.j0;
@@ -432,7 +445,15 @@ __global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
             }
             const int rows = (int)(items - ne);
             const int64_t icn = ic + ne, jcn = jc + rows;
-            en = off[min(icn + 1 + lane, S)];
+            {
+                // The next chunk's first 64 ends: the ones this chunk did not
+                // use move down (a cross-lane read in every lane, since a
+                // disabled source lane would read as 0); only lanes past the
+                // old batch load (offsets are not refetched chunk after chunk).
+                int64_t nx = lane_get(en, (lane + ne) & 63);
+                if (lane + ne >= 64) nx = off[min(icn + 1 + lane, S)];
+                en = nx;
+            }
             const auto rsn = rows_of(icn, jcn);
             const uint32_t relbase = (uint32_t)(jc - sh.j0);
 
@@ -641,6 +662,7 @@ void seg_reduce_flat(const KArgs a) {
     __shared__ uint64_t s_c[4][64];                                         // carried-in part per lane
     // the partition search's probes share wave 0's staging area (the search
     // ends with a barrier, before any wave stages a chunk)
+    static_assert(kProbesA * sizeof(int64_t) <= CH * sizeof(uint32_t), "probes must fit one staging area");
     int64_t *s_probe = reinterpret_cast<int64_t *>(s_x[0]);
 
     const int wid = threadIdx.x >> 6;
