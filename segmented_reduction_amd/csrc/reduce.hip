@@ -429,23 +429,29 @@ __global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
 
             // Segment ends inside this chunk: end k (row position e relative
             // to jc) is one of the first `items` items iff e + k + 1 <= items.
+            // (Lane 0 holds the first candidate; when it lies past the chunk,
+            // which is the common case for long segments, nothing else is
+            // looked at.)
             const int64_t e0 = en - o0 - jc;
             const bool c0 = lane < ends_left && e0 + lane + 1 <= items;
-            int cnt = popc64(ballot(c0));
-            if (c0) se[lane] = (uint32_t)e0;
-            int ne = cnt;
-            for (int b = 64; cnt == 64 && b < CH; b += 64) {
-                const int k = b + lane;
-                const bool valid = k < ends_left;
-                const int64_t e = off[min(ic + 1 + k, S)] - o0 - jc;
-                const bool cond = valid && e + k + 1 <= items;
-                cnt = popc64(ballot(cond));
-                if (cond) se[k] = (uint32_t)e;
-                ne += cnt;
+            int ne = 0;
+            if (ends_left > 0 && readfirst(e0) + 1 <= items) {
+                int cnt = popc64(ballot(c0));
+                if (c0) se[lane] = (uint32_t)e0;
+                ne = cnt;
+                for (int b = 64; cnt == 64 && b < CH; b += 64) {
+                    const int k = b + lane;
+                    const bool valid = k < ends_left;
+                    const int64_t e = off[min(ic + 1 + k, S)] - o0 - jc;
+                    const bool cond = valid && e + k + 1 <= items;
+                    cnt = popc64(ballot(cond));
+                    if (cond) se[k] = (uint32_t)e;
+                    ne += cnt;
+                }
             }
             const int rows = (int)(items - ne);
             const int64_t icn = ic + ne, jcn = jc + rows;
-            {
+            if (ne > 0) {
                 // The next chunk's first 64 ends: the ones this chunk did not
                 // use move down (a cross-lane read in every lane, since a
                 // disabled source lane would read as 0); only lanes past the
