@@ -1,4 +1,4 @@
-"""CPU oracle for segmented reduction and run-length encoding.
+"""CPU oracle for segmented reduction, run-length encoding and scatter reduction.
 
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline
 leg of the benchmark may import this package; the product (the HIP library
@@ -57,6 +57,10 @@ def _bind(lib):
     lib.oracle_reduce.restype = ctypes.c_int
     lib.oracle_rle.argtypes = [vp, i64, vp, vp, vp, vp]
     lib.oracle_rle.restype = ctypes.c_int
+    lib.oracle_scatter.argtypes = [vp, i32, i64, i64, vp, i64, i32, vp, vp, vp, vp]
+    lib.oracle_scatter.restype = ctypes.c_int
+    lib.oracle_offsets_from_index.argtypes = [vp, i64, i64, vp]
+    lib.oracle_offsets_from_index.restype = ctypes.c_int
     lib.oracle_order_key.argtypes = [ctypes.c_uint32, i32]
     lib.oracle_order_key.restype = ctypes.c_uint32
     return lib
@@ -125,3 +129,39 @@ def order_key(bits: int, dtype: str, lib=None) -> int:
     """The monotone uint32 key the oracle orders min/max by."""
     lib = lib or load()
     return int(lib.oracle_order_key(ctypes.c_uint32(bits & 0xFFFFFFFF), DTYPES[dtype]))
+
+
+def scatter(values: np.ndarray, index: np.ndarray, dim_size: int, op: str, lib=None) -> Reduced:
+    """Scatter reduction: row r of ``values`` ([rows] or [rows, F]) goes to
+    output ``index[r]`` (int64, any order; rows outside [0, dim_size) are
+    ignored).  Returns a ``Reduced`` with dim_size outputs."""
+    lib = lib or load()
+    values = np.ascontiguousarray(values)
+    index = np.ascontiguousarray(index, dtype=np.int64)
+    dt = dtype_name(values)
+    feat = 1 if values.ndim == 1 else int(np.prod(values.shape[1:]))
+    rows = int(values.shape[0])
+    if index.shape[0] != rows:
+        raise ValueError("index needs one entry per row")
+    out = np.zeros((dim_size, feat), dtype=np.float32 if op == "mean" else _NP[dt])
+    arg = np.zeros((dim_size, feat), dtype=np.int64) if op in ("min", "max") else None
+    ref = mag = None
+    if dt == "f32" and op in ("sum", "mean"):
+        ref = np.zeros((dim_size, feat), dtype=np.float64)
+        mag = np.zeros((dim_size, feat), dtype=np.float64)
+    rc = lib.oracle_scatter(_ptr(values), DTYPES[dt], feat, rows, _ptr(index), int(dim_size), OPS[op],
+                            _ptr(out), _ptr(arg), _ptr(ref), _ptr(mag))
+    if rc != 0:
+        raise ValueError(f"oracle_scatter rejected dtype={dt} op={op} feat={feat} (rc={rc})")
+    return Reduced(out, arg, ref, mag)
+
+
+def offsets_from_index(index: np.ndarray, dim_size: int, lib=None) -> np.ndarray:
+    """CSR offsets [dim_size + 1] of an int64 index (rows outside the range not counted)."""
+    lib = lib or load()
+    index = np.ascontiguousarray(index, dtype=np.int64)
+    offsets = np.zeros(int(dim_size) + 1, dtype=np.int64)
+    rc = lib.oracle_offsets_from_index(_ptr(index), int(index.shape[0]), int(dim_size), _ptr(offsets))
+    if rc != 0:
+        raise ValueError("oracle_offsets_from_index rejected its input")
+    return offsets

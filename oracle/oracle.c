@@ -1,7 +1,7 @@
 /*
  * oracle.c -- the plain, slow CPU oracle for segmented reduction over
- * offset-delimited segments and for the run-length encoding that produces
- * such segments.
+ * offset-delimited segments, for the run-length encoding that produces such
+ * segments, and for the index-addressed (scatter) form of the same reduction.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * CPU-baseline leg of the benchmark may load or call this code.  The HIP
@@ -29,6 +29,11 @@
  *     adjacent run of equal uint32 values becomes (value, length), first
  *     occurrence order is kept, lengths [3,2,4] correspond to offsets
  *     [0,3,5,9], an empty input gives count 0.
+ *   - phanerozoic/graph-reduce README, "API" and "Method": the scatter path
+ *     reduces every row into the output its index names (the index need not
+ *     be sorted), with the same sum / mean / min / max (+ row) semantics;
+ *     "Usage": the CSR pointer of a destination-sorted edge list is a
+ *     bincount of the index followed by a cumulative sum with a leading 0.
  *
  * Readings where the pages leave a step open (each one is also listed in the
  * design notes of the repository):
@@ -40,9 +45,12 @@
  *     -0.0 < +0.0 and NaNs sit at the ends ordered by their bits; a tie means
  *     identical bits, hence out == values[arg] bit for bit;
  *   - arg is the absolute row index (int64) per (segment, feature);
- *   - empty min/max: value 0 (luma.gl contract) with arg -1 (graph-reduce).
+ *   - empty min/max: value 0 (luma.gl contract) with arg -1 (graph-reduce);
+ *   - scatter: rows whose index lies outside [0, dim_size) take no part; an
+ *     output no row names is empty (0, arg -1, mean 0).
  */
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORC_U32 0
@@ -202,5 +210,116 @@ int oracle_rle(const uint32_t *keys, int64_t n, uint32_t *values, uint32_t *leng
     for (int64_t r = 0; r < c; ++r)
         lengths[r] = (uint32_t)(offsets[r + 1] - offsets[r]);
     *count = c;
+    return 0;
+}
+
+/*
+ * oracle_scatter: out[s, f] = op over the rows r with index[r] == s of
+ * values[r, f] (graph-reduce README, "API": scatter_sum / scatter_mean /
+ * scatter_max / scatter_min).  Rows are visited in ascending order, one at a
+ * time; each output keeps its own running sum (double for float32, wrapping
+ * uint32 for integers), row count and best (key, row).  Outputs, arg_out,
+ * ref_out and abs_out are as for oracle_reduce with dim_size outputs.
+ * Returns 0, -1 for an argument it does not accept, -2 if out of memory.
+ */
+int oracle_scatter(const void *values, int32_t dtype, int64_t feat, int64_t rows,
+                   const int64_t *index, int64_t dim_size, int32_t op,
+                   void *out, int64_t *arg_out, double *ref_out, double *abs_out)
+{
+    if (dtype < ORC_U32 || dtype > ORC_F32 || op < ORC_SUM || op > ORC_MEAN || feat < 1 || rows < 0 ||
+        dim_size < 0)
+        return -1;
+    if (op == ORC_MEAN && dtype != ORC_F32)
+        return -1;
+    const int64_t cells = dim_size * feat;
+    double *sum = calloc((size_t)(cells > 0 ? cells : 1), sizeof(double));
+    double *mag = calloc((size_t)(cells > 0 ? cells : 1), sizeof(double));
+    uint32_t *isum = calloc((size_t)(cells > 0 ? cells : 1), sizeof(uint32_t));
+    uint32_t *best_key = calloc((size_t)(cells > 0 ? cells : 1), sizeof(uint32_t));
+    int64_t *best_row = malloc((size_t)(cells > 0 ? cells : 1) * sizeof(int64_t));
+    int64_t *count = calloc((size_t)(dim_size > 0 ? dim_size : 1), sizeof(int64_t));
+    if (!sum || !mag || !isum || !best_key || !best_row || !count) {
+        free(sum); free(mag); free(isum); free(best_key); free(best_row); free(count);
+        return -2;
+    }
+    for (int64_t cell = 0; cell < cells; ++cell)
+        best_row[cell] = -1;
+
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t s = index[r];
+        if (s < 0 || s >= dim_size)
+            continue;
+        count[s] += 1;
+        for (int64_t f = 0; f < feat; ++f) {
+            const int64_t cell = s * feat + f;
+            const uint32_t b = load_bits(values, r * feat + f);
+            if (op == ORC_SUM || op == ORC_MEAN) {
+                if (dtype == ORC_F32) {
+                    const double x = (double)bits_to_float(b);
+                    sum[cell] += x;
+                    mag[cell] += x < 0 ? -x : x;
+                } else {
+                    isum[cell] += b;
+                }
+            } else {
+                /* the first row seen wins until a strictly better key comes:
+                 * ties keep the lower row */
+                const uint32_t k = oracle_order_key(b, dtype);
+                const int better = best_row[cell] < 0 || ((op == ORC_MIN) ? (k < best_key[cell]) : (k > best_key[cell]));
+                if (better) {
+                    best_key[cell] = k;
+                    best_row[cell] = r;
+                }
+            }
+        }
+    }
+
+    for (int64_t s = 0; s < dim_size; ++s) {
+        for (int64_t f = 0; f < feat; ++f) {
+            const int64_t cell = s * feat + f;
+            if (op == ORC_SUM || op == ORC_MEAN) {
+                if (dtype == ORC_F32) {
+                    double result = sum[cell];
+                    if (op == ORC_MEAN)
+                        result = count[s] > 0 ? sum[cell] / (double)count[s] : 0.0;
+                    store_bits(out, cell, float_to_bits((float)result));
+                    if (ref_out)
+                        ref_out[cell] = result;
+                    if (abs_out)
+                        abs_out[cell] = mag[cell];
+                } else {
+                    store_bits(out, cell, isum[cell]);
+                }
+            } else {
+                const int64_t br = best_row[cell];
+                store_bits(out, cell, br < 0 ? 0u : load_bits(values, br * feat + f));
+                if (arg_out)
+                    arg_out[cell] = br;
+            }
+        }
+    }
+    free(sum); free(mag); free(isum); free(best_key); free(best_row); free(count);
+    return 0;
+}
+
+/*
+ * oracle_offsets_from_index: offsets[s] = number of rows whose index is in
+ * [0, s), for s = 0..dim_size (graph-reduce README, "Usage": bincount of the
+ * index, then a cumulative sum after a leading 0).  Rows outside
+ * [0, dim_size) are not counted.
+ */
+int oracle_offsets_from_index(const int64_t *index, int64_t rows, int64_t dim_size, int64_t *offsets)
+{
+    if (rows < 0 || dim_size < 0)
+        return -1;
+    for (int64_t s = 0; s <= dim_size; ++s)
+        offsets[s] = 0;
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t s = index[r];
+        if (s >= 0 && s < dim_size)
+            offsets[s + 1] += 1;
+    }
+    for (int64_t s = 0; s < dim_size; ++s)
+        offsets[s + 1] += offsets[s];
     return 0;
 }

@@ -81,3 +81,48 @@ def rle(keys):
     for ln in lengths:
         offsets.append(offsets[-1] + ln)
     return values, lengths, offsets
+
+
+def scatter(rows, index, dim_size, op, kind, feat):
+    """Scatter by definition (graph-reduce README, "API"): output s gathers the
+    rows r with index[r] == s, in row order; indices outside [0, dim_size)
+    belong to no output.  Same result conventions as ``reduce``."""
+    members = [[] for _ in range(dim_size)]
+    for r, s in enumerate(index):
+        if 0 <= s < dim_size:
+            members[s].append(r)
+    out, arg, exact = [], [], []
+    for s in range(dim_size):
+        o_row, a_row, e_row = [], [], []
+        for f in range(feat):
+            col = [(rows[r][f], r) for r in members[s]]
+            n = len(col)
+            if op in ("sum", "mean"):
+                if kind == "f32":
+                    total = math.fsum(v for v, _ in col)
+                    val = total / n if (op == "mean" and n) else (total if op == "sum" else 0.0)
+                    e_row.append(val)
+                    o_row.append(_round_f32(val))
+                else:
+                    total = sum(v for v, _ in col) % (1 << 32)
+                    if kind == "i32" and total >= (1 << 31):
+                        total -= 1 << 32
+                    o_row.append(total)
+                a_row.append(None)
+            elif not col:
+                o_row.append(0)
+                a_row.append(-1)
+            else:
+                # (value, row) tuples: the extreme value, then the lowest row
+                best = min(col) if op == "min" else max(col, key=lambda t: (t[0], -t[1]))
+                o_row.append(best[0])
+                a_row.append(best[1])
+        out.append(o_row)
+        arg.append(a_row)
+        exact.append(e_row)
+    return out, arg, (exact if kind == "f32" else None)
+
+
+def offsets_from_index(index, dim_size):
+    """Counting by definition: offsets[s] = #{r : 0 <= index[r] < s}."""
+    return [sum(1 for x in index if 0 <= x < s) for s in range(dim_size + 1)]

@@ -321,7 +321,136 @@ def pin_rle_groupby(lib, seed=13):
         assert (v.tolist(), ln.tolist(), off.tolist()) == (bv, bl, bo)
 
 
+# ---------------------------------------------------------------- scatter path
+
+def _index_of_offsets(off):
+    """The index vector of a CSR offsets array: row r -> the segment holding it
+    (rows before offsets[0] or past offsets[-1] get -1, i.e. no output)."""
+    n = int(off[-1])
+    idx = np.full(n, -1, dtype=np.int64)
+    for s in range(len(off) - 1):
+        idx[int(off[s]):int(off[s + 1])] = s
+    return idx
+
+
+def pin_scatter_worked_example(lib):
+    """The luma.gl worked example written as a destination index (graph-reduce
+    README, 'Usage': the sorted edge list and its CSR pointer describe the same
+    grouping), then with its rows shuffled: the values may not change."""
+    g = _golden("segmented_reduction_worked_example.json")
+    off = np.array(g["offsets"], dtype=np.int64)
+    idx = _index_of_offsets(off)
+    s = len(off) - 1
+    assert oracle.offsets_from_index(idx, s, lib=lib).tolist() == off.tolist()
+    perm = np.random.default_rng(0).permutation(len(idx))
+    for kind in ("u32", "i32", "f32"):
+        vals = np.array(g["values"], dtype=NP_T[kind])[: len(idx)]
+        for op in ("sum", "min", "max"):
+            r = oracle.scatter(vals, idx, s, op, lib=lib)
+            assert _col(r.out) == g[op], (kind, op)
+            if op != "sum":
+                assert _col(r.arg) == g["derived"]["arg" + op], (kind, op)
+            rp = oracle.scatter(vals[perm], idx[perm], s, op, lib=lib)
+            assert _col(rp.out) == g[op], (kind, op, "shuffled")
+
+
+def _random_scatter_case(rng, kind, feat):
+    rows = int(rng.integers(0, 40))
+    dim = int(rng.integers(0, 9))
+    index = rng.integers(-2, dim + 3, rows).astype(np.int64)  # some rows fall outside
+    pool = {"f32": lambda n: rng.choice(np.array([-2.5, -1.0, 0.5, 0.125, 3.0, 7e-4], np.float32), n),
+            "i32": lambda n: rng.integers(-3, 3, n).astype(np.int32),
+            "u32": lambda n: rng.integers(0, 2 ** 32, n, dtype=np.uint64).astype(np.uint32)}[kind]
+    vals = pool(rows * feat).reshape(rows, feat)
+    if kind == "u32":
+        vals[rng.random((rows, feat)) < 0.5] = 7  # ties
+    return vals, index, dim
+
+
+def pin_scatter_brute(lib, cases=300, seed=4321):
+    """Scatter oracle == pure-Python brute force on tiny random inputs with
+    unsorted, repeated and out-of-range indices (F in 1, 2, 3)."""
+    rng = np.random.default_rng(seed)
+    for i in range(cases):
+        kind = ("u32", "i32", "f32")[i % 3]
+        feat = (1, 2, 3)[(i // 3) % 3]
+        vals, index, dim = _random_scatter_case(rng, kind, feat)
+        ops = ("sum", "min", "max") + (("mean",) if kind == "f32" else ())
+        for op in ops:
+            r = oracle.scatter(vals if feat > 1 else vals[:, 0], index, dim, op, lib=lib)
+            b_out, b_arg, b_exact = brute_ref.scatter(vals.tolist(), index.tolist(), dim, op, kind, feat)
+            if op in ("min", "max"):
+                assert r.out.tolist() == b_out and r.arg.tolist() == b_arg, (i, kind, op)
+            elif kind == "f32":
+                for s in range(dim):
+                    for f in range(feat):
+                        ex = b_exact[s][f]
+                        a = math.fsum(abs(float(vals[k, f])) for k in range(len(index)) if index[k] == s)
+                        assert abs(r.ref[s, f] - ex) <= 1e-13 * a + 1e-300, (i, op, s, f)
+                        assert abs(r.mag[s, f] - a) <= 1e-13 * a + 1e-300, (i, op, s, f)
+                        assert abs(float(r.out[s, f]) - ex) <= 2.0 ** -23 * abs(ex) + 1e-13 * a + 1e-300, (i, op, s, f)
+            else:
+                assert r.out.tolist() == b_out, (i, kind, op)
+        assert oracle.offsets_from_index(index, dim, lib=lib).tolist() == brute_ref.offsets_from_index(index.tolist(), dim)
+
+
+def pin_scatter_library(lib, seed=17):
+    """torch on the CPU, the baselines the graph-reduce README names: index_add_
+    for sums, scatter_reduce(amax / amin, include_self=False) for values,
+    torch.bincount + cumsum for the CSR pointer; and on a sorted index the
+    scatter equals the segmented reduction over that pointer."""
+    import torch
+    rng = np.random.default_rng(seed)
+    rows, dim, feat = 6000, 700, 3
+    index = rng.integers(0, dim, rows).astype(np.int64)
+    index[rng.random(rows) < 0.05] = dim + 5  # out of range: dropped before torch sees it
+    keep = index < dim
+    v = rng.standard_normal((rows, feat)).astype(np.float32)
+    ti = torch.from_numpy(index[keep])
+    tv = torch.from_numpy(v[keep].astype(np.float64))
+    want = torch.zeros(dim, feat, dtype=torch.float64).index_add_(0, ti, tv).numpy()
+    r = oracle.scatter(v, index, dim, "sum", lib=lib)
+    assert np.allclose(r.ref, want, rtol=0, atol=1e-12 * max(1.0, np.abs(v).sum()))
+    counts = torch.bincount(ti, minlength=dim).numpy()
+    rm = oracle.scatter(v, index, dim, "mean", lib=lib)
+    assert np.allclose(rm.ref, np.where(counts[:, None] > 0, want / np.maximum(counts, 1)[:, None], 0.0),
+                       rtol=1e-12, atol=1e-14)
+    for op, red in (("min", "amin"), ("max", "amax")):
+        for arr in (v, rng.integers(-50, 50, (rows, feat)).astype(np.int32)):
+            tgt = torch.zeros(dim, feat, dtype=torch.from_numpy(arr).dtype)
+            t = tgt.scatter_reduce(0, ti[:, None].expand(-1, feat), torch.from_numpy(arr[keep]), red,
+                                   include_self=False).numpy()
+            rr = oracle.scatter(arr, index, dim, op, lib=lib)
+            assert np.array_equal(rr.out, t), (op, arr.dtype)
+            # the arg is gathered back and is the lowest row among equals
+            for s in range(0, dim, 7):
+                for f in range(feat):
+                    members = np.nonzero(index == s)[0]
+                    a = int(rr.arg[s, f])
+                    if members.size == 0:
+                        assert a == -1
+                        continue
+                    col = arr[members, f]
+                    best = col.min() if op == "min" else col.max()
+                    assert index[a] == s and arr[a, f] == best and a == members[col == best][0]
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    assert np.array_equal(oracle.offsets_from_index(index, dim, lib=lib), off)
+    # sorted index: scatter == segmented reduction over the counted pointer
+    order = np.argsort(index, kind="stable")
+    si, sv = index[order], v[order]
+    soff = oracle.offsets_from_index(si, dim, lib=lib)
+    for op in ("sum", "min", "max", "mean"):
+        a = oracle.scatter(sv, si, dim, op, lib=lib)
+        b = oracle.reduce(sv[: int(soff[-1])], soff, op, lib=lib)
+        assert np.array_equal(a.out, b.out), op
+        if a.arg is not None:
+            assert np.array_equal(a.arg, b.arg), op
+
+
 ALL_PINS = [
+    pin_scatter_worked_example,
+    pin_scatter_brute,
+    pin_scatter_library,
     pin_worked_example,
     pin_empty_segments,
     pin_rle_examples,

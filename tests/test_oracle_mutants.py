@@ -38,6 +38,23 @@ MUTANTS = [
     ("arg_relative_to_segment", "arg_out[o] = best_row;", "arg_out[o] = best_row - lo;"),
     ("rle_only_increasing_boundaries", "keys[i] != keys[i - 1]", "keys[i] > keys[i - 1]"),
     ("rle_last_offset_short", "offsets[c] = n;", "offsets[c] = n - (n > 0);"),
+    ("scatter_drops_output_zero", "if (s < 0 || s >= dim_size)\n            continue;\n        count",
+     "if (s < 1 || s >= dim_size)\n            continue;\n        count"),
+    ("scatter_drops_first_row", "for (int64_t r = 0; r < rows; ++r) {\n        const int64_t s = index[r];\n        if (s < 0",
+     "for (int64_t r = 1; r < rows; ++r) {\n        const int64_t s = index[r];\n        if (s < 0"),
+    ("index_offsets_drop_first_row", "for (int64_t r = 0; r < rows; ++r) {\n        const int64_t s = index[r];\n        if (s >= 0",
+     "for (int64_t r = 1; r < rows; ++r) {\n        const int64_t s = index[r];\n        if (s >= 0"),
+    ("scatter_int_sum_overwrites", "isum[cell] += b;", "isum[cell] = b;"),
+    ("scatter_float_sum_wrong_sign", "sum[cell] += x;", "sum[cell] -= x;"),
+    ("scatter_mean_wrong_count", "sum[cell] / (double)count[s]", "sum[cell] / (double)(count[s] + 1)"),
+    ("scatter_ties_to_later_row", "(k < best_key[cell]) : (k > best_key[cell])",
+     "(k <= best_key[cell]) : (k >= best_key[cell])"),
+    ("scatter_min_max_swapped", "(k < best_key[cell]) : (k > best_key[cell])",
+     "(k > best_key[cell]) : (k < best_key[cell])"),
+    ("scatter_feature_stride_dropped", "const uint32_t b = load_bits(values, r * feat + f);",
+     "const uint32_t b = load_bits(values, r + f * (r + 1 < rows));"),
+    ("index_offsets_shifted", "offsets[s + 1] += 1;", "offsets[s] += 1;"),
+    ("index_offsets_not_cumulative", "offsets[s + 1] += offsets[s];", "offsets[s + 1] = offsets[s + 1];"),
     ("rle_length_off_by_one", "(uint32_t)(offsets[r + 1] - offsets[r])", "(uint32_t)(offsets[r + 1] - offsets[r] - 1)"),
 ]
 
