@@ -36,7 +36,8 @@ MALL_BYTES = 256 << 20
 METRIC = "effective HBM GB/s (+% of peak) and Gelem/s for CSR segmented reduce, 1 GPU"
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["segmented_reduction_amd/csrc/reduce.hip", "segmented_reduction_amd/csrc/wave.hpp",
-                  "segmented_reduction_amd/csrc/rle.hip"]
+                  "segmented_reduction_amd/csrc/rle.hip", "segmented_reduction_amd/csrc/keys.hpp",
+                  "segmented_reduction_amd/csrc/scan.hpp", "segmented_reduction_amd/csrc/scatter.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -148,6 +149,47 @@ class RleWorkload(Workload):
         return 3 * self.n
 
 
+class ScatterWorkload(Workload):
+    """The scatter path: rows in edge order with an unsorted destination index,
+    one scatter sum and one scatter max (+row) per step."""
+
+    kernel_name = "scatter_kernel"
+
+    def __init__(self, cfg, ops, copies, sr, torch):
+        self.sr, self.torch = sr, torch
+        self.cfg = cfg
+        self.host_vals, self.host_index, self.dim = cfg["f32"], cfg["index"], int(cfg["dim"])
+        self.ops = ops
+        self.rows = int(self.host_index.size)
+        self.feat = 1 if self.host_vals.ndim == 1 else int(self.host_vals.shape[1])
+        v = torch.from_numpy(self.host_vals).cuda()
+        i = torch.from_numpy(self.host_index).cuda()
+        self.sets = [(v, i)] + [(v.clone(), i.clone()) for _ in range(copies - 1)]
+        self.vals = [x[0] for x in self.sets]
+        self.calls = [(op, op) for op in ops]
+        # init + scatter (+ finish for min/max/mean; + a second init for mean)
+        self.kernels_per_step = sum({"sum": 2, "min": 3, "max": 3, "mean": 4}[op] for op in ops)
+        self.outs = {}
+
+    def step(self, i):
+        for j, op in enumerate(self.ops):
+            v, idx = self.sets[(i * len(self.ops) + j) % len(self.sets)]
+            self.outs[op] = self.sr.scatter(v, idx, self.dim, op)
+
+    def call_bytes(self, op):
+        """Values and index read once, each output element (and row) written once."""
+        b = self.rows * self.feat * 4 + self.rows * 8 + self.dim * self.feat * 4
+        if op in ("min", "max"):
+            b += self.dim * self.feat * 8
+        return b
+
+    def bytes_per_step(self):
+        return sum(self.call_bytes(op) for op in self.ops)
+
+    def elems_per_step(self):
+        return self.rows * self.feat * len(self.ops)
+
+
 DESCRIPTIONS = {
     "small": "1-D f32 and i32, 4,096 segments, lengths uniform in [0,64] (~3% empty): f32 sum/min/max/mean",
     "message": "graph message passing: 1,000,000 destination-sorted rows x F=64 f32 normal(0,1) into "
@@ -158,6 +200,10 @@ DESCRIPTIONS = {
             "segment, 10% empty); sum and min+argmin",
     "powerlaw": "power-law graph: 2M nodes, 32M destination-sorted edges (in-degree Lomax alpha=2, hub of "
                 "200K), F=32 f32 normal(0,1), int64 indptr; sum, mean and max+argmax",
+    "scatter": "scatter path: 1,000,000 rows x F=64 f32 normal(0,1) in edge order, unsorted int64 destination "
+               "index uniform over 10,000 outputs; atomic scatter sum and scatter max+argmax",
+    "scatter16": "scatter path: 1,000,000 rows x F=16 f32 normal(0,1) in edge order, unsorted int64 "
+                 "destination index uniform over 10,000 outputs; atomic scatter sum and scatter max+argmax",
 }
 
 
@@ -166,6 +212,11 @@ def build_workload(name, sr, torch):
     if name == "rle":
         cfg = W.rle_keys()
         return RleWorkload(cfg, copies=4, sr=sr, torch=torch), cfg
+    if name in ("scatter", "scatter16"):
+        cfg = W.scatter(feat=64 if name == "scatter" else 16)
+        nbytes = cfg["f32"].nbytes + cfg["index"].nbytes
+        copies = max(1, min(4, -(-4 * MALL_BYTES // nbytes)))
+        return ScatterWorkload(cfg, ["sum", "max"], copies, sr, torch), cfg
     gen = {"small": W.small, "message": W.message, "skew": W.skew, "powerlaw": W.powerlaw}[name]
     cfg = gen()
     ops = {"small": ["sum", "min", "max", "mean"], "message": ["sum", "max"], "skew": ["sum", "min"],
@@ -195,6 +246,14 @@ def cpu_baseline(wl, name, budget_s):
             reps += 1
         results["rle"] = (v, ln, off, c)
         sample = f"full workload ({name}), {reps} rep(s)"
+    elif isinstance(wl, ScatterWorkload):
+        while reps == 0 or (t < budget_s and reps < 50):
+            t0 = time.perf_counter()
+            for op in wl.ops:
+                results[op] = oracle.scatter(wl.host_vals, wl.host_index, wl.dim, op, lib=lib)
+            t += time.perf_counter() - t0
+            reps += 1
+        sample = f"full workload ({name}), all {len(wl.ops)} ops, {reps} rep(s)"
     else:
         while reps == 0 or (t < budget_s and reps < 50):
             t0 = time.perf_counter()
@@ -226,6 +285,25 @@ def check_parity(wl, results):
             if arg is not None:
                 ok = ok and np.array_equal(arg[:c].cpu().numpy(), ref.arg[:, 0])
             verdict[label] = bool(ok)
+        return verdict
+    if isinstance(wl, ScatterWorkload):
+        inr = (wl.host_index >= 0) & (wl.host_index < wl.dim)
+        n = np.bincount(wl.host_index[inr], minlength=wl.dim).reshape(-1, 1).astype(np.float64)
+        for op in wl.ops:
+            out, arg = wl.outs[op]
+            ref = results[op]
+            got = out.cpu().numpy().reshape(ref.out.shape)
+            if op in ("min", "max"):
+                ok = np.array_equal(got.view(np.uint32), ref.out.view(np.uint32)) and \
+                    np.array_equal(arg.cpu().numpy().reshape(ref.arg.shape), ref.arg)
+            else:
+                # float32 atomic adds in arrival order: gamma(n - 1) * sum|x|
+                k = np.maximum(n - 1, 0) * 2.0 ** -24
+                tol = k / (1 - k) * ref.mag * 1.0001 + 1e-30
+                if op == "mean":
+                    tol = tol / np.maximum(n, 1) + 1.0001 * 2.0 ** -24 * np.abs(ref.ref)
+                ok = bool((np.abs(got.astype(np.float64) - ref.ref) <= tol).all())
+            verdict[op] = bool(ok)
         return verdict
     for op in wl.ops:
         out, arg = wl.outs[op]
@@ -359,7 +437,8 @@ def main():
     src_hash = kernel_source_hash()
     traffic = load_traffic(args.config, dominant, src_hash)
     roofline = {"bound": "hbm", "achieved": dk["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": dk["frac"], "traffic": traffic, "kernel": f"seg_reduce_pass1 ({dominant})",
+                "frac": dk["frac"], "traffic": traffic,
+                "kernel": f"{getattr(wl, 'kernel_name', 'seg_reduce_pass1')} ({dominant})",
                 "algorithmic_bytes_per_launch": dk["bytes"], "avg_launch_us": dk["avg_us"],
                 "timing": "kernel-stamped HIP stop events (hipExtLaunchKernel) on the launch stream, end of "
                           "previous kernel to end of this one, a second pass of the same K steps, minus the "
@@ -374,6 +453,12 @@ def main():
 
     # bitwise repeat: the rotated copies hold identical inputs
     repeat_ok = None
+    if isinstance(wl, ScatterWorkload) and len(wl.sets) > 1 and "max" in wl.ops:
+        # float atomic sums may move in the last bits; max and its rows may not
+        a, aa = sr.scatter(wl.sets[0][0], wl.sets[0][1], wl.dim, "max")
+        b, bb = sr.scatter(wl.sets[-1][0], wl.sets[-1][1], wl.dim, "max")
+        torch.cuda.synchronize()
+        repeat_ok = bool(torch.equal(a.view(torch.int32), b.view(torch.int32)) and torch.equal(aa, bb))
     if isinstance(wl, ReduceWorkload) and len(wl.vals) > 1:
         op = wl.ops[0]
         a, _ = sr.reduce(wl.vals[0], wl.off, op)
@@ -405,7 +490,9 @@ def main():
         "parity": parity,
         "bitwise_repeat": repeat_ok,
         "kernel_source_hash": src_hash,
-        "accumulate": "f64 for float sums, wrapping u32 for integer sums",
+        "accumulate": ("f32 atomic adds in arrival order (not bitwise repeatable); max via packed 64-bit "
+                       "atomic max" if isinstance(wl, ScatterWorkload)
+                       else "f64 for float sums, wrapping u32 for integer sums"),
     }
     print(json.dumps(line), flush=True)
 

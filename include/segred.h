@@ -144,6 +144,78 @@ int segred_reduce_device_count(const void *values, int32_t dtype, int64_t feat,
                                int64_t max_segments, int32_t op, void *out,
                                int64_t *arg_out, hipStream_t stream);
 
+/*
+ * segred_scatter_reduce -- reduction of rows into the outputs an index names
+ * (the scatter form: the index need not be sorted).
+ *
+ * Defined by the graph-reduce README: "API" (scatter_sum / scatter_mean /
+ * scatter_max / scatter_min over src [N, ...] with an int64 index [N] and
+ * dim_size outputs; the mean of an output no row reaches is 0; max and min
+ * also return the producing row), "Method" (one atomic operation per element;
+ * max/min resolve value and row together in one 64-bit atomic on the word
+ * (order key << 32) | row code, ties to the lower row).
+ *
+ *   values     [rows, feat] row-major, 4-byte elements of type `dtype`.
+ *   dtype      SEGRED_U32, SEGRED_I32 or SEGRED_F32.
+ *   feat       features per row, >= 1.
+ *   rows       N >= 0.
+ *   index      int64 [rows]: index[r] is the output row r goes to.  Rows whose
+ *              index is outside [0, dim_size) take part in no output.
+ *   dim_size   number of outputs >= 0 (0: nothing is written).
+ *   op         SEGRED_SUM, SEGRED_MIN, SEGRED_MAX or SEGRED_MEAN.
+ *   out        [dim_size, feat] of the input type (float32 for MEAN); every
+ *              element is written.  An output no row reaches gets 0.
+ *              Integer SUM wraps modulo 2^32 and is exact; MIN/MAX use the
+ *              same order as segred_reduce and are exact.  Float SUM and MEAN
+ *              are float32 atomic additions in arrival order: the result can
+ *              differ in its last bits from run to run (error at most
+ *              (n - 1) * 2^-24 * sum|x| for an output of n rows, to first
+ *              order; MEAN adds one rounding of the division).  Use
+ *              segred_reduce on destination-sorted rows for a reproducible
+ *              sum.
+ *   arg_out    int64 [dim_size, feat] or NULL; MIN/MAX only: the row that
+ *              produced the value, the lowest such row on ties, -1 for an
+ *              output no row reaches.  When given, it also serves as the
+ *              call's working memory for the packed words.
+ *   stream     HIP stream the work is ordered on.
+ *
+ * Errors: SEGRED_ERR_INVALID_ARGUMENT for rows < 0, dim_size < 0, feat < 1,
+ * an unknown dtype or op, a NULL values/index with rows > 0 or out with
+ * dim_size > 0, values/out not 4-byte or index/arg_out not 8-byte aligned,
+ * dim_size * feat or rows * feat above INT64_MAX.  SEGRED_ERR_UNSUPPORTED for
+ * MEAN of an integer type, or MIN/MAX/MEAN with rows > 2^32 - 2 (rows are
+ * packed into 32 bits).  SEGRED_ERR_OUT_OF_MEMORY, SEGRED_ERR_HIP as for
+ * segred_reduce.  `out`/`arg_out` must not overlap the inputs.
+ */
+int segred_scatter_reduce(const void *values, int32_t dtype, int64_t feat, int64_t rows,
+                          const int64_t *index, int64_t dim_size, int32_t op,
+                          void *out, int64_t *arg_out, hipStream_t stream);
+
+/*
+ * segred_offsets_from_index -- the CSR offsets of an index: offsets[s] = the
+ * number of rows whose index lies in [0, s), for s = 0..dim_size.
+ *
+ * Defined by the graph-reduce README, "Usage": for an edge list sorted by
+ * destination, the pointer that segment_*_csr takes is the per-destination
+ * count of the index with a running sum behind a leading 0.  For a sorted
+ * index, segment s of segred_reduce(values, ..., offsets, dim_size, ...) then
+ * holds exactly the rows with index s.
+ *
+ *   index     int64 [rows], any order; entries outside [0, dim_size) are not
+ *             counted.
+ *   rows      >= 0.
+ *   dim_size  >= 0.
+ *   offsets   int64 [dim_size + 1], every entry written (offsets[0] = 0).
+ *   stream    HIP stream the work is ordered on.
+ *
+ * Errors: SEGRED_ERR_INVALID_ARGUMENT for rows < 0, dim_size < 0, a NULL
+ * offsets (or index with rows > 0), misalignment (8 bytes).
+ * SEGRED_ERR_UNSUPPORTED above 2^31 workgroups (rows > 2^44 or dim_size >
+ * 2^43).  SEGRED_ERR_OUT_OF_MEMORY, SEGRED_ERR_HIP as for segred_reduce.
+ */
+int segred_offsets_from_index(const int64_t *index, int64_t rows, int64_t dim_size,
+                              int64_t *offsets, hipStream_t stream);
+
 /* Static, host-side description of a status code (never NULL). */
 const char *segred_status_string(int status);
 

@@ -8,6 +8,8 @@ There is no CPU fallback: if the library is missing, calls raise.
 
     out, arg = reduce(values, offsets, "max")        # values [N] or [N, F] on the GPU
     values, lengths, offsets, count = offsets_from_rle(sorted_keys)
+    out, arg = scatter(values, index, dim_size, "max")  # unsorted int64 index [N]
+    offsets = offsets_from_index(sorted_index, dim_size)
 """
 from __future__ import annotations
 
@@ -56,6 +58,10 @@ def library(path: str | None = None):
             lib.segred_reduce_device_count.restype = ctypes.c_int
             lib.segred_offsets_from_rle.argtypes = [vp, i64, vp, vp, vp, vp, vp]
             lib.segred_offsets_from_rle.restype = ctypes.c_int
+            lib.segred_scatter_reduce.argtypes = [vp, i32, i64, i64, vp, i64, i32, vp, vp, vp]
+            lib.segred_scatter_reduce.restype = ctypes.c_int
+            lib.segred_offsets_from_index.argtypes = [vp, i64, i64, vp, vp]
+            lib.segred_offsets_from_index.restype = ctypes.c_int
             lib.segred_status_string.argtypes = [ctypes.c_int]
             lib.segred_status_string.restype = ctypes.c_char_p
             lib.segred_set_shares.argtypes = [i64]
@@ -175,6 +181,74 @@ def rle(keys: torch.Tensor):
     values, lengths, offsets, count = offsets_from_rle(keys)
     c = int(count.item())
     return values[:c], lengths[:c], offsets[: c + 1], c
+
+
+def scatter(values: torch.Tensor, index: torch.Tensor, dim_size: int, op: str, *, want_arg: bool = True,
+            out: torch.Tensor | None = None, arg: torch.Tensor | None = None):
+    """Scatter ``op`` ("sum", "min", "max", "mean"): row r of ``values`` goes
+    to output ``index[r]`` (segred_scatter_reduce).
+
+    values  [N] or [N, ...] uint32 / int32 / float32 on a GPU, contiguous.
+    index   int64 [N] on the same GPU, any order; entries outside
+            [0, dim_size) are ignored.
+    Returns (out [dim_size, ...], arg [dim_size, ...] int64 or None).  Float
+    sums use atomic additions and may differ in the last bits run to run.
+    """
+    if op not in OPS:
+        raise ValueError(f"op must be one of {sorted(OPS)}")
+    if not (values.is_cuda and index.is_cuda) or values.device != index.device:
+        raise ValueError("values and index must be tensors on the same GPU")
+    if values.dtype not in DTYPES:
+        raise TypeError(f"values dtype {values.dtype} is not uint32, int32 or float32")
+    if values.dim() == 0 or not values.is_contiguous():
+        raise ValueError("values must be contiguous with at least one dimension")
+    if index.dtype != torch.int64 or index.dim() != 1 or not index.is_contiguous():
+        raise ValueError("index must be a contiguous 1-D int64 tensor")
+    n = values.shape[0]
+    if index.numel() != n:
+        raise ValueError("index needs one entry per row of values")
+    dim_size = int(dim_size)
+    if dim_size < 0:
+        raise ValueError("dim_size must be >= 0")
+    feat_shape = tuple(values.shape[1:])
+    feat = 1
+    for d in feat_shape:
+        feat *= d
+    if feat < 1:
+        raise ValueError("values has an empty feature dimension")
+    odt = torch.float32 if op == "mean" else values.dtype
+    if out is None:
+        out = torch.empty((dim_size,) + feat_shape, dtype=odt, device=values.device)
+    want = op in ("min", "max") and want_arg
+    if want and arg is None:
+        arg = torch.empty((dim_size,) + feat_shape, dtype=torch.int64, device=values.device)
+    if not want:
+        arg = None
+    with torch.cuda.device(values.device):
+        rc = library().segred_scatter_reduce(values.data_ptr() if n else None, DTYPES[values.dtype], feat, n,
+                                             index.data_ptr() if n else None, dim_size, OPS[op],
+                                             out.data_ptr() if dim_size else None,
+                                             arg.data_ptr() if (arg is not None and dim_size) else None,
+                                             _stream(values.device))
+    _check(rc, "segred_scatter_reduce")
+    return out, arg
+
+
+def offsets_from_index(index: torch.Tensor, dim_size: int) -> torch.Tensor:
+    """CSR offsets [dim_size + 1] of an int64 GPU ``index``: offsets[s] = rows
+    with index in [0, s) (segred_offsets_from_index)."""
+    if not index.is_cuda or index.dtype != torch.int64 or index.dim() != 1 or not index.is_contiguous():
+        raise ValueError("index must be a contiguous 1-D int64 GPU tensor")
+    dim_size = int(dim_size)
+    if dim_size < 0:
+        raise ValueError("dim_size must be >= 0")
+    n = index.numel()
+    offsets = torch.empty(dim_size + 1, dtype=torch.int64, device=index.device)
+    with torch.cuda.device(index.device):
+        rc = library().segred_offsets_from_index(index.data_ptr() if n else None, n, dim_size,
+                                                 offsets.data_ptr(), _stream(index.device))
+    _check(rc, "segred_offsets_from_index")
+    return offsets
 
 
 def set_shares(shares: int):

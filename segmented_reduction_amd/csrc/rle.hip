@@ -13,6 +13,7 @@
 // position order through LDS and writes values, offsets and lengths with
 // consecutive lanes on consecutive runs.
 #include "internal.hpp"
+#include "scan.hpp"
 #include "wave.hpp"
 
 namespace segred {
@@ -88,38 +89,6 @@ __global__ __launch_bounds__(kRleThreads) void rle_count(const uint32_t *keys, i
     }
 }
 
-// Inclusive scan over the 1024 threads of a workgroup; `op` is + or min.
-template <bool MIN>
-__device__ __forceinline__ int64_t block_inclusive_scan(int64_t v, int64_t *s_tmp, int64_t &total) {
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    constexpr int kWaves = kScanThreads / 64;
-    int64_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int64_t y = lane_get(x, (lane - o) & 63);
-        if (lane >= o) x = MIN ? (y < x ? y : x) : x + y;
-    }
-    if (lane == 63) s_tmp[wid] = x;
-    __syncthreads();
-    if (wid == 0) {
-        int64_t w = lane < kWaves ? s_tmp[lane] : (MIN ? INT64_MAX : 0);
-#pragma unroll
-        for (int o = 1; o < kWaves; o <<= 1) {
-            const int64_t y = lane_get(w, (lane - o) & 63);
-            if (lane >= o) w = MIN ? (y < w ? y : w) : w + y;
-        }
-        if (lane < kWaves) s_tmp[kWaves + lane] = w;
-    }
-    __syncthreads();
-    if (wid > 0) {
-        const int64_t p = s_tmp[kWaves + wid - 1];
-        x = MIN ? (p < x ? p : x) : p + x;
-    }
-    total = s_tmp[2 * kWaves - 1];
-    __syncthreads();
-    return x;
-}
-
 // One workgroup: run index of each tile's first start (exclusive scan of the
 // tile counts) and the first start after each tile (exclusive minimum of the
 // tiles' first starts, from the right).  Each thread takes K consecutive
@@ -151,7 +120,7 @@ __global__ __launch_bounds__(kScanThreads) void rle_scan(int64_t tiles, int64_t 
             acc += v[j];
         }
         int64_t total;
-        const int64_t ex = block_inclusive_scan<false>(acc, s_tmp, total) - acc;
+        const int64_t ex = block_inclusive_scan<kScanThreads, false>(acc, s_tmp, total) - acc;
 #pragma unroll
         for (int j = 0; j < K; ++j) {
             const int64_t t = b + (int64_t)tid * K + j;
@@ -180,7 +149,7 @@ __global__ __launch_bounds__(kScanThreads) void rle_scan(int64_t tiles, int64_t 
             m = w[j] < m ? w[j] : m;
         }
         int64_t total;
-        const int64_t incl = block_inclusive_scan<true>(m, s_tmp, total);
+        const int64_t incl = block_inclusive_scan<kScanThreads, true>(m, s_tmp, total);
         // exclusive over the threads before this one: lane - 1 of this wave,
         // or for lane 0 the running minimum of the earlier waves (still in
         // s_tmp after the block scan)

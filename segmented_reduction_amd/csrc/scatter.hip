@@ -1,0 +1,442 @@
+// scatter.hip -- reduction of rows into the outputs an index names (the
+// scatter form of the segmented reduction), and the CSR offsets of an index.
+//
+// Operation (phanerozoic/graph-reduce README): "API" -- scatter_sum,
+// scatter_mean, scatter_max and scatter_min take rows [N, ...], an int64
+// index [N] and dim_size outputs; the mean of an output no row reaches is 0;
+// max and min also give the producing row.  "Method" -- one atomic operation
+// per element; max and min resolve value and row in a single 64-bit atomic on
+// the word (order key << 32) | row code, ties to the lower row.  "Usage" --
+// the CSR pointer of a destination-sorted index is the count of rows per
+// destination, cumulatively summed behind a leading 0.
+//
+// These kernels use global atomic operations, so a float sum depends on the
+// order in which the atomics arrive and may differ in its last bits from run
+// to run (the README's "Correctness" notes the same of its atomic path);
+// integer sums, min/max with their rows, counts and offsets are exact.
+//
+// Scatter launch.  Items are (row, 64-feature chunk) pairs.  Each lane owns
+// one feature of one item: L lanes per item (L = the smallest power of two
+// >= min(F, 64)), G = 64 / L consecutive items per wave step, kSteps steps per
+// wave, all index and value loads of a wave issued before its atomics.  For
+// 1-D values (L = 1) a step's 64 consecutive rows are first combined over
+// runs of equal index by a segmented scan across the wave (skipped when no
+// two neighbours share an index), so a sorted or clustered index sends one
+// atomic per run rather than one per row.
+//
+// Rows whose index lies outside [0, dim_size) are skipped: they take part in
+// no output (and no memory outside the outputs is touched for them).
+#include "internal.hpp"
+#include "keys.hpp"
+#include "scan.hpp"
+#include "wave.hpp"
+
+namespace segred {
+
+constexpr int kScThreads = 256;
+constexpr int kScSteps = 8;
+constexpr int kCountTile = 4096;            // counts per tile of the offsets scan
+constexpr int kCountThreads = 256;          // 16 counts per thread
+constexpr int kCountScanThreads = 1024;
+constexpr int kCountScanPer = 4;
+
+struct ScArgs {
+    const uint32_t *values;  // element bits, row-major [rows, F]
+    const int64_t *index;    // [rows]
+    int64_t rows, F, chunks, dim, items;  // chunks = ceil(F / 64) when F > 64, else 1; items = rows * chunks
+    int lg;                  // log2 of the lanes per item
+    uint32_t *out;           // [dim, F]: sums (SUM, MEAN)
+    uint64_t *words;         // [dim, F]: packed key/row words (MIN, MAX)
+    uint32_t *counts;        // [dim]: rows per output (MEAN)
+};
+
+// Packed word of (key, row): the integer max of MAX words is the largest key
+// and, among equal keys, the lowest row (row code ~row); the integer min of
+// MIN words is the smallest key, then the lowest row.  Rows are below
+// 2^32 - 1, so an untouched word (0 for MAX, all ones for MIN) is no row's.
+template <int OP>
+__device__ __forceinline__ uint64_t pack(uint32_t key, int64_t row) {
+    const uint32_t code = OP == OP_MAX ? ~(uint32_t)row : (uint32_t)row;
+    return ((uint64_t)key << 32) | code;
+}
+template <int OP>
+constexpr uint64_t kEmptyWord = OP == OP_MAX ? 0ull : ~0ull;
+
+// Fill kernel for the outputs' starting state (no memset node, so a caller
+// may capture the call in a graph).
+__global__ __launch_bounds__(kScThreads) void scatter_init(uint32_t *p32, int64_t n32, uint32_t v32, uint64_t *p64,
+                                                           int64_t n64, uint64_t v64) {
+    const int64_t stride = (int64_t)gridDim.x * kScThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kScThreads + threadIdx.x; i < n32; i += stride) p32[i] = v32;
+    for (int64_t i = (int64_t)blockIdx.x * kScThreads + threadIdx.x; i < n64; i += stride) p64[i] = v64;
+}
+
+template <int DT, int OP>
+__device__ __forceinline__ void scatter_apply(const ScArgs &a, int64_t cell, uint32_t x, uint64_t w) {
+    if constexpr (OP == OP_MAX) {
+        __hip_atomic_fetch_max(a.words + cell, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if constexpr (OP == OP_MIN) {
+        __hip_atomic_fetch_min(a.words + cell, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if constexpr (DT == DT_F32) {
+        unsafeAtomicAdd(reinterpret_cast<float *>(a.out) + cell, __uint_as_float(x));
+    } else {
+        __hip_atomic_fetch_add(a.out + cell, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Combine two partials of one run (x, w as in scatter_apply).
+template <int DT, int OP>
+__device__ __forceinline__ void combine(uint32_t &x, uint64_t &w, uint32_t y, uint64_t v) {
+    if constexpr (OP == OP_MAX) w = v > w ? v : w;
+    else if constexpr (OP == OP_MIN) w = v < w ? v : w;
+    else if constexpr (DT == DT_F32) x = __float_as_uint(__uint_as_float(y) + __uint_as_float(x));
+    else x = y + x;
+}
+
+template <int DT, int OP, bool RUNS>
+__global__ __launch_bounds__(kScThreads) void scatter_kernel(ScArgs a) {
+    constexpr bool kWord = OP == OP_MIN || OP == OP_MAX;
+    const int lane = threadIdx.x & 63;
+    const int lg = RUNS ? 0 : a.lg;
+    const int64_t G = 64 >> lg;
+    const int64_t wave = (int64_t)blockIdx.x * (kScThreads / 64) + (threadIdx.x >> 6);
+    const int64_t qbase = wave * kScSteps * G;
+    const int sub = lane & ((1 << lg) - 1);
+
+    int64_t s[kScSteps], row[kScSteps], fe[kScSteps];
+    uint32_t x[kScSteps];
+    bool live[kScSteps];
+#pragma unroll
+    for (int u = 0; u < kScSteps; ++u) {
+        int64_t q = qbase + u * G + (lane >> lg);
+        int64_t r = q, f = sub;
+        if (!RUNS && a.chunks > 1) {
+            // one item per wave step here (64 lanes per item): q is uniform
+            q = readfirst(q);
+            r = q / a.chunks;
+            f = (q - r * a.chunks) * 64 + lane;
+        }
+        live[u] = q < a.items && f < a.F;
+        s[u] = live[u] ? a.index[r] : -1;
+        x[u] = live[u] ? a.values[r * a.F + f] : 0u;
+        row[u] = r;
+        fe[u] = f;
+    }
+
+#pragma unroll
+    for (int u = 0; u < kScSteps; ++u) {
+        const int64_t r = row[u], f = fe[u];
+        uint64_t w = 0;
+        if constexpr (kWord) w = pack<OP>(okey<DT>(x[u]), r);
+        uint32_t xv = x[u];
+        bool act = s[u] >= 0 && s[u] < a.dim && live[u];
+        uint32_t cnt = 1;
+        if constexpr (RUNS) {
+            // runs of equal index among the step's 64 consecutive rows
+            const int64_t prev = lane_get(s[u], (lane - 1) & 63);
+            const bool head = lane == 0 || s[u] != prev;
+            const uint64_t heads = ballot(head);
+            if (heads != ~0ull) {
+                bool fl = head;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const uint32_t yx = lane_get(xv, (lane - o) & 63);
+                    uint64_t yw = 0;
+                    if constexpr (kWord) yw = lane_get(w, (lane - o) & 63);
+                    const bool yf = lane_get(fl, (lane - o) & 63);
+                    if (lane >= o && !fl) {
+                        combine<DT, OP>(xv, w, yx, yw);
+                        fl = yf;
+                    }
+                }
+                const bool last = lane == 63 || ((heads >> (lane + 1)) & 1ull);
+                const uint64_t upto = heads & (lane == 63 ? ~0ull : ((2ull << lane) - 1));
+                cnt = (uint32_t)(lane - (63 - __clzll((long long)upto)) + 1);
+                act = act && last;
+            }
+        }
+        if (act) {
+            scatter_apply<DT, OP>(a, s[u] * a.F + f, xv, w);
+            if constexpr (OP == OP_MEAN) {
+                if (f == 0)
+                    __hip_atomic_fetch_add(a.counts + s[u], cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+}
+
+// Final values: MIN/MAX unpack the word (value from its key, row from its
+// code; untouched -> 0 and -1); MEAN divides by the row count (0 rows -> 0).
+template <int DT, int OP>
+__global__ __launch_bounds__(kScThreads) void scatter_finish(ScArgs a, int64_t *arg) {
+    const int64_t cells = a.dim * a.F;
+    const int64_t stride = (int64_t)gridDim.x * kScThreads;
+    for (int64_t c = (int64_t)blockIdx.x * kScThreads + threadIdx.x; c < cells; c += stride) {
+        if constexpr (OP == OP_MEAN) {
+            const uint32_t n = a.counts[c / a.F];
+            const float sum = __uint_as_float(a.out[c]);
+            a.out[c] = n ? __float_as_uint(sum / (float)n) : 0u;
+        } else {
+            const uint64_t w = a.words[c];
+            const bool empty = w == kEmptyWord<OP>;
+            const uint32_t code = (uint32_t)w;
+            a.out[c] = empty ? 0u : okey_inv<DT>((uint32_t)(w >> 32));
+            if (arg) arg[c] = empty ? -1 : (int64_t)(OP == OP_MAX ? ~code : code);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- offsets of an index
+
+// Rows per destination, added into counts[s] = offsets[s + 1] (zeroed
+// before).  A step's 64 consecutive rows are merged over runs of equal index
+// first (run length from the ballot of run heads), so a sorted index costs one
+// atomic per run and wave step.
+__global__ __launch_bounds__(kScThreads) void index_count(const int64_t *index, int64_t rows, int64_t dim,
+                                                          uint64_t *counts) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * (kScThreads / 64) + (threadIdx.x >> 6);
+    const int64_t base = wave * kScSteps * 64;
+    int64_t s[kScSteps];
+#pragma unroll
+    for (int u = 0; u < kScSteps; ++u) {
+        const int64_t r = base + u * 64 + lane;
+        s[u] = r < rows ? index[r] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kScSteps; ++u) {
+        const int64_t next = lane_get(s[u], (lane + 1) & 63);
+        const int64_t prev = lane_get(s[u], (lane - 1) & 63);
+        const bool head = lane == 0 || s[u] != prev;
+        const bool last = lane == 63 || s[u] != next;
+        const uint64_t heads = ballot(head);
+        const uint64_t upto = heads & (lane == 63 ? ~0ull : ((2ull << lane) - 1));
+        const uint64_t len = (uint64_t)(lane - (63 - __clzll((long long)upto)) + 1);
+        if (last && s[u] >= 0 && s[u] < dim)
+            __hip_atomic_fetch_add(counts + s[u], len, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Tile totals of the counts: tile t covers counts[t * 4096, (t + 1) * 4096).
+__global__ __launch_bounds__(kCountThreads) void count_tiles(const int64_t *counts, int64_t dim, int64_t *tsum) {
+    __shared__ int64_t s_tmp[2 * (kCountThreads / 64)];
+    const int tid = threadIdx.x;
+    const int64_t t0 = (int64_t)blockIdx.x * kCountTile;
+    int64_t acc = 0;
+#pragma unroll
+    for (int u = 0; u < kCountTile / kCountThreads; ++u) {
+        const int64_t i = t0 + u * kCountThreads + tid;
+        acc += i < dim ? counts[i] : 0;
+    }
+    int64_t total;
+    block_inclusive_scan<kCountThreads, false>(acc, s_tmp, total);
+    if (tid == 0) tsum[blockIdx.x] = total;
+}
+
+// One workgroup: exclusive scan of the tile totals (tile base).
+__global__ __launch_bounds__(kCountScanThreads) void count_scan(const int64_t *tsum, int64_t tiles,
+                                                                int64_t *tbase) {
+    constexpr int K = kCountScanPer;
+    constexpr int64_t kBatch = (int64_t)kCountScanThreads * K;
+    __shared__ int64_t s_tmp[2 * (kCountScanThreads / 64)];
+    const int tid = threadIdx.x;
+    int64_t running = 0;
+    for (int64_t b = 0; b < tiles; b += kBatch) {
+        int64_t v[K], in[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const int64_t t = b + (int64_t)tid * K + j;
+            v[j] = t < tiles ? tsum[t] : 0;
+        }
+        int64_t acc = 0;
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            in[j] = acc;
+            acc += v[j];
+        }
+        int64_t total;
+        const int64_t ex = block_inclusive_scan<kCountScanThreads, false>(acc, s_tmp, total) - acc;
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const int64_t t = b + (int64_t)tid * K + j;
+            if (t < tiles) tbase[t] = running + ex + in[j];
+        }
+        running += total;
+    }
+}
+
+// Counts -> inclusive sums in place (offsets[s + 1] = rows with index < s + 1).
+// The tile goes through LDS so that global reads and writes are coalesced
+// while each thread scans 16 consecutive counts.
+__global__ __launch_bounds__(kCountThreads) void count_apply(int64_t *counts, int64_t dim, const int64_t *tbase) {
+    constexpr int P = kCountTile / kCountThreads;
+    __shared__ int64_t s_c[kCountTile];
+    __shared__ int64_t s_tmp[2 * (kCountThreads / 64)];
+    const int tid = threadIdx.x;
+    const int64_t t0 = (int64_t)blockIdx.x * kCountTile;
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+        const int64_t i = t0 + u * kCountThreads + tid;
+        s_c[u * kCountThreads + tid] = i < dim ? counts[i] : 0;
+    }
+    __syncthreads();
+    int64_t v[P];
+    int64_t acc = 0;
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        acc += s_c[tid * P + j];
+        v[j] = acc;
+    }
+    int64_t total;
+    const int64_t ex = block_inclusive_scan<kCountThreads, false>(acc, s_tmp, total) - acc + tbase[blockIdx.x];
+#pragma unroll
+    for (int j = 0; j < P; ++j) s_c[tid * P + j] = v[j] + ex;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+        const int64_t i = t0 + u * kCountThreads + tid;
+        if (i < dim) counts[i] = s_c[u * kCountThreads + tid];
+    }
+}
+
+template <int DT, int OP>
+int scatter_launch(const ScArgs &a, int64_t *arg, hipStream_t st) {
+    const int64_t per_wave = (int64_t)kScSteps * (64 >> a.lg);
+    const int64_t waves = (a.items + per_wave - 1) / per_wave;
+    const int64_t wgs = (waves + kScThreads / 64 - 1) / (kScThreads / 64);
+    if (wgs > INT32_MAX) return SEGRED_ERR_UNSUPPORTED;
+    hipError_t e = hipSuccess;
+    if (wgs > 0) {
+        if (a.lg == 0)
+            hipExtLaunchKernelGGL((scatter_kernel<DT, OP, true>), dim3((unsigned)wgs), dim3(kScThreads), 0, st,
+                                  nullptr, timing_stop(true), 0, a);
+        else
+            hipExtLaunchKernelGGL((scatter_kernel<DT, OP, false>), dim3((unsigned)wgs), dim3(kScThreads), 0, st,
+                                  nullptr, timing_stop(true), 0, a);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess && OP != OP_SUM) {
+        const int64_t cells = a.dim * a.F;
+        const unsigned grid = (unsigned)std::min<int64_t>((cells + kScThreads - 1) / kScThreads, 4096);
+        hipExtLaunchKernelGGL((scatter_finish<DT, OP>), dim3(grid), dim3(kScThreads), 0, st, nullptr,
+                              timing_stop(false), 0, a, arg);
+        e = hipGetLastError();
+    }
+    return e == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
+}
+
+template <int DT>
+int scatter_dispatch_op(int op, const ScArgs &a, int64_t *arg, hipStream_t st) {
+    switch (op) {
+    case OP_SUM: return scatter_launch<DT, OP_SUM>(a, arg, st);
+    case OP_MIN: return scatter_launch<DT, OP_MIN>(a, arg, st);
+    case OP_MAX: return scatter_launch<DT, OP_MAX>(a, arg, st);
+    default:
+        if constexpr (DT == DT_F32) return scatter_launch<DT, OP_MEAN>(a, arg, st);
+        return SEGRED_ERR_UNSUPPORTED;
+    }
+}
+
+unsigned fill_grid(int64_t n) { return (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + kScThreads - 1) / kScThreads, 4096)); }
+
+}  // namespace segred
+
+using namespace segred;
+
+extern "C" int segred_scatter_reduce(const void *values, int32_t dtype, int64_t feat, int64_t rows,
+                                     const int64_t *index, int64_t dim_size, int32_t op, void *out,
+                                     int64_t *arg_out, hipStream_t stream) {
+    if (dtype < SEGRED_U32 || dtype > SEGRED_F32 || op < SEGRED_SUM || op > SEGRED_MEAN) return SEGRED_ERR_INVALID_ARGUMENT;
+    if (feat < 1 || rows < 0 || dim_size < 0) return SEGRED_ERR_INVALID_ARGUMENT;
+    if (dim_size > 0 && feat > INT64_MAX / dim_size) return SEGRED_ERR_INVALID_ARGUMENT;
+    if (rows > 0 && feat > INT64_MAX / rows) return SEGRED_ERR_INVALID_ARGUMENT;
+    if (rows > 0 && (!values || !index)) return SEGRED_ERR_INVALID_ARGUMENT;
+    if (dim_size > 0 && !out) return SEGRED_ERR_INVALID_ARGUMENT;
+    if ((values && !aligned(values, 4)) || (index && !aligned(index, 8)) || (out && !aligned(out, 4)) ||
+        (arg_out && !aligned(arg_out, 8)))
+        return SEGRED_ERR_INVALID_ARGUMENT;
+    if (op == SEGRED_MEAN && dtype != SEGRED_F32) return SEGRED_ERR_UNSUPPORTED;
+    if (op != SEGRED_SUM && rows > (int64_t)0xFFFFFFFE) return SEGRED_ERR_UNSUPPORTED;
+    if (dim_size == 0) return SEGRED_OK;
+
+    ScArgs a{};
+    a.values = static_cast<const uint32_t *>(values);
+    a.index = index;
+    a.rows = rows;
+    a.F = feat;
+    a.dim = dim_size;
+    a.chunks = feat > 64 ? (feat + 63) / 64 : 1;
+    a.items = rows * a.chunks;
+    int lg = 0;
+    while ((1 << lg) < std::min<int64_t>(feat, 64)) ++lg;
+    a.lg = lg;
+    a.out = static_cast<uint32_t *>(out);
+    const int64_t cells = dim_size * feat;
+    int64_t *arg = (op == SEGRED_MIN || op == SEGRED_MAX) ? arg_out : nullptr;
+
+    // MIN/MAX words live in arg_out when the caller gives it (8 bytes per
+    // cell, unpacked in place), else in scratch; MEAN counts in scratch.
+    size_t need = 0;
+    if ((op == SEGRED_MIN || op == SEGRED_MAX) && !arg) need = (size_t)cells * 8;
+    if (op == SEGRED_MEAN) need = (size_t)dim_size * 4;
+    ScratchLease scratch;
+    if (need > 0) {
+        const int rc = scratch_acquire(scratch, need, stream);
+        if (rc != SEGRED_OK) return rc;
+    }
+    if (op == SEGRED_MIN || op == SEGRED_MAX) {
+        a.words = arg ? reinterpret_cast<uint64_t *>(arg) : static_cast<uint64_t *>(scratch.ptr);
+        const uint64_t empty = op == SEGRED_MAX ? kEmptyWord<OP_MAX> : kEmptyWord<OP_MIN>;
+        hipExtLaunchKernelGGL(scatter_init, dim3(fill_grid(cells)), dim3(kScThreads), 0, stream, nullptr,
+                              timing_stop(false), 0, (uint32_t *)nullptr, (int64_t)0, 0u, a.words, cells, empty);
+    } else {
+        if (op == SEGRED_MEAN) a.counts = static_cast<uint32_t *>(scratch.ptr);
+        hipExtLaunchKernelGGL(scatter_init, dim3(fill_grid(cells)), dim3(kScThreads), 0, stream, nullptr,
+                              timing_stop(false), 0, a.out, cells, 0u, (uint64_t *)nullptr, (int64_t)0, 0ull);
+        if (op == SEGRED_MEAN && hipGetLastError() == hipSuccess)
+            hipExtLaunchKernelGGL(scatter_init, dim3(fill_grid(dim_size)), dim3(kScThreads), 0, stream, nullptr,
+                                  timing_stop(false), 0, a.counts, dim_size, 0u, (uint64_t *)nullptr, (int64_t)0,
+                                  0ull);
+    }
+    if (hipGetLastError() != hipSuccess) return SEGRED_ERR_HIP;
+    switch (dtype) {
+    case SEGRED_U32: return scatter_dispatch_op<DT_U32>(op, a, arg, stream);
+    case SEGRED_I32: return scatter_dispatch_op<DT_I32>(op, a, arg, stream);
+    default: return scatter_dispatch_op<DT_F32>(op, a, arg, stream);
+    }
+}
+
+extern "C" int segred_offsets_from_index(const int64_t *index, int64_t rows, int64_t dim_size, int64_t *offsets,
+                                         hipStream_t stream) {
+    if (rows < 0 || dim_size < 0 || !offsets || (rows > 0 && !index)) return SEGRED_ERR_INVALID_ARGUMENT;
+    if (!aligned(offsets, 8) || (index && !aligned(index, 8))) return SEGRED_ERR_INVALID_ARGUMENT;
+    const int64_t per_wg = (int64_t)kScSteps * 64 * (kScThreads / 64);
+    const int64_t wgs = (rows + per_wg - 1) / per_wg;
+    const int64_t tiles = (dim_size + kCountTile - 1) / kCountTile;
+    if (wgs > INT32_MAX || tiles > INT32_MAX) return SEGRED_ERR_UNSUPPORTED;
+
+    ScratchLease scratch;
+    if (tiles > 0) {
+        const int rc = scratch_acquire(scratch, (size_t)tiles * 2 * sizeof(int64_t), stream);
+        if (rc != SEGRED_OK) return rc;
+    }
+    int64_t *tsum = static_cast<int64_t *>(scratch.ptr);
+    int64_t *tbase = tsum + tiles;
+    int64_t *counts = offsets + 1;
+
+    hipExtLaunchKernelGGL(scatter_init, dim3(fill_grid(dim_size + 1)), dim3(kScThreads), 0, stream, nullptr,
+                          timing_stop(false), 0, (uint32_t *)nullptr, (int64_t)0, 0u,
+                          reinterpret_cast<uint64_t *>(offsets), dim_size + 1, 0ull);
+    if (wgs > 0 && dim_size > 0)
+        hipExtLaunchKernelGGL(index_count, dim3((unsigned)wgs), dim3(kScThreads), 0, stream, nullptr,
+                              timing_stop(true), 0, index, rows, dim_size, reinterpret_cast<uint64_t *>(counts));
+    if (tiles > 0) {
+        hipExtLaunchKernelGGL(count_tiles, dim3((unsigned)tiles), dim3(kCountThreads), 0, stream, nullptr,
+                              timing_stop(false), 0, (const int64_t *)counts, dim_size, tsum);
+        hipExtLaunchKernelGGL(count_scan, dim3(1), dim3(kCountScanThreads), 0, stream, nullptr, timing_stop(false), 0,
+                              (const int64_t *)tsum, tiles, tbase);
+        hipExtLaunchKernelGGL(count_apply, dim3((unsigned)tiles), dim3(kCountThreads), 0, stream, nullptr,
+                              timing_stop(false), 0, counts, dim_size, (const int64_t *)tbase);
+    }
+    return hipGetLastError() == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
+}

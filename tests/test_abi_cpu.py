@@ -27,7 +27,8 @@ def _declared():
 
 def test_header_declares_the_boundary():
     names = _declared()
-    for required in ("segred_reduce", "segred_offsets_from_rle", "segred_status_string"):
+    for required in ("segred_reduce", "segred_offsets_from_rle", "segred_status_string", "segred_scatter_reduce",
+                     "segred_offsets_from_index"):
         assert required in names
 
 
@@ -108,6 +109,44 @@ def test_rle_argument_checks(args, expect):
     assert lib.segred_offsets_from_rle(*args, None) == expect
 
 
+@pytest.mark.parametrize("args,expect", [
+    # (values, dtype, feat, rows, index, dim_size, op, out, arg) -> status
+    ((FAKE, 2, 1, -1, FAKE, 4, 0, FAKE, None), 1),     # rows < 0
+    ((FAKE, 2, 1, 8, FAKE, -1, 0, FAKE, None), 1),     # dim_size < 0
+    ((FAKE, 2, 0, 8, FAKE, 4, 0, FAKE, None), 1),      # feat < 1
+    ((FAKE, 3, 1, 8, FAKE, 4, 0, FAKE, None), 1),      # dtype out of range
+    ((FAKE, 2, 1, 8, FAKE, 4, 4, FAKE, None), 1),      # op out of range
+    ((FAKE, 0, 1, 8, FAKE, 4, 3, FAKE, None), 2),      # MEAN of u32
+    ((FAKE, 2, 1, 2 ** 32 - 1, FAKE, 4, 2, FAKE, None), 2),  # rows do not fit the packed word
+    ((None, 2, 1, 8, FAKE, 4, 0, FAKE, None), 1),      # null values
+    ((FAKE, 2, 1, 8, None, 4, 0, FAKE, None), 1),      # null index
+    ((FAKE, 2, 1, 8, FAKE, 4, 0, None, None), 1),      # null out
+    ((FAKE + 2, 2, 1, 8, FAKE, 4, 0, FAKE, None), 1),  # values not 4-byte aligned
+    ((FAKE, 2, 1, 8, FAKE + 4, 4, 0, FAKE, None), 1),  # index not 8-byte aligned
+    ((FAKE, 2, 1, 8, FAKE, 4, 1, FAKE, FAKE + 4), 1),  # arg not 8-byte aligned
+    ((FAKE, 2, 2 ** 40, 8, FAKE, 2 ** 40, 0, FAKE, None), 1),  # dim_size * feat overflows
+    ((None, 2, 1, 0, None, 0, 0, None, None), 0),      # nothing to do
+    ((FAKE, 2, 3, 8, FAKE, 0, 2, None, None), 0),      # dim_size == 0 writes nothing
+])
+def test_scatter_argument_checks(args, expect):
+    lib = _lib()
+    assert lib.segred_scatter_reduce(*args, None) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    # (index, rows, dim_size, offsets) -> status
+    ((FAKE, -1, 4, FAKE), 1),
+    ((FAKE, 4, -1, FAKE), 1),
+    ((None, 4, 4, FAKE), 1),
+    ((FAKE, 4, 4, None), 1),
+    ((FAKE + 4, 4, 4, FAKE), 1),
+    ((FAKE, 4, 4, FAKE + 4), 1),
+])
+def test_offsets_from_index_argument_checks(args, expect):
+    lib = _lib()
+    assert lib.segred_offsets_from_index(*args, None) == expect
+
+
 def test_share_knob_range():
     lib = _lib()
     assert lib.segred_set_shares(-1) == 1
@@ -137,21 +176,27 @@ def test_binding_refuses_cpu_tensors():
 
 
 def test_kernel_sources_have_no_atomics_or_foreign_backends():
-    """No atomics on global memory (results are combined in a fixed order
-    instead) and no CUDA/Triton/dual-platform code in the library sources.
-    The one atomic allowed is the wave-scope LDS bit-OR helper `lds_or`
-    (it sets flag bits, so arrival order cannot change a result)."""
+    """No atomics on global memory in the segmented and RLE paths (results are
+    combined in a fixed order instead) and no CUDA/Triton/dual-platform code
+    in the library sources.  The scatter path (scatter.hip) is atomic by
+    definition and is the one file exempt.  Elsewhere the one atomic allowed
+    is the wave-scope LDS bit-OR helper `lds_or` (it sets flag bits, so
+    arrival order cannot change a result)."""
     device_atomic = re.compile(r"\batomic[A-Z]\w*\s*\(|__hip_atomic|__atomic_\w+\s*\(|\bunsafeAtomic")
     allowed = "__hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT)"
     seen_allowed = 0
+    atomic_files = {"scatter.hip"}
     for name in os.listdir(CSRC):
         code = re.sub(r"//[^\n]*", "", open(os.path.join(CSRC, name)).read())
+        for bad in ("cuda", "triton", "__hip_platform"):
+            assert bad not in code.lower(), (name, bad)
+        if name in atomic_files:
+            assert device_atomic.search(code), name
+            continue
         if name == "wave.hpp":
             seen_allowed = code.count(allowed)
             code = code.replace(allowed, "")
         assert not device_atomic.search(code), name
-        for bad in ("cuda", "triton", "__hip_platform"):
-            assert bad not in code.lower(), (name, bad)
         for m in re.finditer(r"\blds_or\(&(\w+)\[", code):
             assert m.group(1) == "sm", (name, m.group(0))  # only the per-wave LDS mask array
     assert seen_allowed == 1

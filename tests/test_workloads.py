@@ -57,3 +57,23 @@ def test_ragged_case():
     off, v = W.ragged(3, 50, 10, feat=3, dtype="u32", base=7, tail_rows=2, long_segment=100)
     assert off[0] == 7 and v.shape == (off[-1] + 2, 3) and v.dtype == np.uint32
     assert np.diff(off).max() == 100
+
+
+def test_scatter_shape():
+    c = W.scatter()
+    idx = c["index"]
+    assert idx.shape == (1_000_000,) and idx.dtype == np.int64 and c["dim"] == 10_000
+    assert idx.min() >= 0 and idx.max() < 10_000 and not (np.diff(idx) >= 0).all()  # unsorted
+    assert abs(np.bincount(idx, minlength=10_000).mean() - 100) < 1e-9
+    assert c["f32"].shape == (1_000_000, 64) and c["f32"].dtype == np.float32
+
+
+def test_scatter_case_orders():
+    idx, v = W.scatter_case(3, 5000, 300, feat=2, order="sorted", out_of_range=0.1)
+    inr = idx[(idx >= 0) & (idx < 300)]
+    assert (np.diff(inr) >= 0).all() and v.shape == (5000, 2)
+    assert 0.05 < ((idx < 0) | (idx >= 300)).mean() < 0.15
+    idx, _ = W.scatter_case(4, 5000, 300, order="runs")
+    assert (np.diff(idx) == 0).mean() > 0.8
+    idx, _ = W.scatter_case(5, 100, 7, order="one")
+    assert (idx == 0).all()

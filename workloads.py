@@ -25,6 +25,11 @@ Configurations (sizes are decimal unless written as powers of two):
   powerlaw  2,000,000 nodes, 32,000,000 destination-sorted edges, in-degree
             Lomax/Pareto-II (alpha = 2) capped at 200,000 with one hub of
             exactly 200,000, F = 32 float32 normal(0, 1).
+  scatter   the message rows in edge order: 1,000,000 rows x F float32
+            normal(0, 1) with an int64 destination index drawn uniformly over
+            10,000 outputs, unsorted (the graph-reduce README's scatter_*
+            usage; its measured table has this 1M -> 10,000 shape at F = 16
+            and F = 64).
 """
 from __future__ import annotations
 
@@ -138,7 +143,16 @@ def powerlaw(seed=0, values=True, feat=32):
     return out
 
 
-CONFIGS = {"small": small, "message": message, "rle": rle_keys, "skew": skew, "powerlaw": powerlaw}
+def scatter(seed=0, feat=64, rows=1_000_000, dim=10_000):
+    rng = np.random.default_rng(seed)
+    index = rng.integers(0, dim, rows, dtype=np.int64)
+    values = rng.standard_normal((rows, feat), dtype=np.float32)
+    return {"name": f"scatter-{rows // 1_000_000}Mx{feat}-{dim // 1000}Kdst", "index": index, "dim": dim,
+            "f32": values}
+
+
+CONFIGS = {"small": small, "message": message, "rle": rle_keys, "skew": skew, "powerlaw": powerlaw,
+           "scatter": scatter}
 
 
 # ---------------------------------------------------------------- test-sized cases
@@ -174,3 +188,39 @@ def ragged(seed, segments, mean_len, feat=1, dtype="f32", empty_frac=0.1, base=0
     else:
         arr = rng.integers(0, 2 ** 32, shape, dtype=np.uint32)
     return off, arr
+
+
+def scatter_case(seed, rows, dim, feat=1, dtype="f32", order="random", out_of_range=0.0, values="normal"):
+    """An index-addressed case for the scatter tests.
+
+    ``order``: "random" (uniform over [0, dim)), "sorted" (the same, sorted),
+    "runs" (runs of 1..40 rows sharing a random destination) or "one" (every
+    row to output 0).  A fraction ``out_of_range`` of the rows is then sent to
+    -1, dim or 2^40 (rows that reach no output).  ``values`` as in ragged."""
+    rng = np.random.default_rng(seed)
+    hi = max(dim, 1)
+    if order == "runs":
+        lens = rng.integers(1, 41, rows + 1)
+        dest = rng.integers(0, hi, lens.size)
+        index = np.repeat(dest, lens)[:rows].astype(np.int64)
+    elif order == "one":
+        index = np.zeros(rows, dtype=np.int64)
+    else:
+        index = rng.integers(0, hi, rows, dtype=np.int64)
+        if order == "sorted":
+            index.sort()
+    if out_of_range > 0 and rows:
+        bad = rng.random(rows) < out_of_range
+        index[bad] = rng.choice(np.array([-1, dim, 2 ** 40], dtype=np.int64), int(bad.sum()))
+    shape = (rows,) if feat == 1 else (rows, feat)
+    if values == "ties":
+        v = rng.integers(-2, 3, shape)
+        arr = {"f32": (v * 0.5).astype(np.float32), "i32": v.astype(np.int32),
+               "u32": (v + 2).astype(np.uint32)}[dtype]
+    elif dtype == "f32":
+        arr = rng.standard_normal(shape, dtype=np.float32)
+    elif dtype == "i32":
+        arr = rng.integers(-(2 ** 31), 2 ** 31, shape, dtype=np.int32)
+    else:
+        arr = rng.integers(0, 2 ** 32, shape, dtype=np.uint32)
+    return index, arr
