@@ -61,6 +61,10 @@ def _bind(lib):
     lib.oracle_scatter.restype = ctypes.c_int
     lib.oracle_offsets_from_index.argtypes = [vp, i64, i64, vp]
     lib.oracle_offsets_from_index.restype = ctypes.c_int
+    lib.oracle_unique.argtypes = [vp, i64, vp, vp]
+    lib.oracle_unique.restype = ctypes.c_int
+    lib.oracle_offsets_from_flags.argtypes = [vp, i64, vp, vp]
+    lib.oracle_offsets_from_flags.restype = ctypes.c_int
     lib.oracle_order_key.argtypes = [ctypes.c_uint32, i32]
     lib.oracle_order_key.restype = ctypes.c_uint32
     return lib
@@ -123,6 +127,33 @@ def rle(keys: np.ndarray, lib=None):
         raise ValueError("oracle_rle rejected its input")
     c = int(count[0])
     return values[:c], lengths[:c], offsets[: c + 1], c
+
+
+def unique(keys: np.ndarray, lib=None):
+    """Distinct adjacent values of uint32 ``keys``: returns (values[:count], count)."""
+    lib = lib or load()
+    keys = np.ascontiguousarray(keys, dtype=np.uint32)
+    n = int(keys.shape[0])
+    values = np.zeros(max(n, 1), dtype=np.uint32)
+    count = np.zeros(1, dtype=np.int64)
+    if lib.oracle_unique(_ptr(keys), n, _ptr(values), _ptr(count)) != 0:
+        raise ValueError("oracle_unique rejected its input")
+    c = int(count[0])
+    return values[:c], c
+
+
+def offsets_from_flags(flags: np.ndarray, lib=None):
+    """Offsets of the segments that uint32 start ``flags`` (nonzero = start)
+    open: returns (offsets[:count + 1], count)."""
+    lib = lib or load()
+    flags = np.ascontiguousarray(flags, dtype=np.uint32)
+    n = int(flags.shape[0])
+    offsets = np.zeros(n + 1, dtype=np.int64)
+    count = np.zeros(1, dtype=np.int64)
+    if lib.oracle_offsets_from_flags(_ptr(flags), n, _ptr(offsets), _ptr(count)) != 0:
+        raise ValueError("oracle_offsets_from_flags rejected its input")
+    c = int(count[0])
+    return offsets[: c + 1], c
 
 
 def order_key(bits: int, dtype: str, lib=None) -> int:

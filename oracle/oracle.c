@@ -28,7 +28,10 @@
  *     encoding?", "Why RLE matters for GPU grouping" and "Contract": each
  *     adjacent run of equal uint32 values becomes (value, length), first
  *     occurrence order is kept, lengths [3,2,4] correspond to offsets
- *     [0,3,5,9], an empty input gives count 0.
+ *     [0,3,5,9], an empty input gives count 0; "GPUUnique": the distinct
+ *     adjacent values under the same equality, without lengths.
+ *   - luma.gl "GPUSegmentedReduction", "Composition": a segmented layout
+ *     materialises offsets from segment-start flags.
  *   - phanerozoic/graph-reduce README, "API" and "Method": the scatter path
  *     reduces every row into the output its index names (the index need not
  *     be sorted), with the same sum / mean / min / max (+ row) semantics;
@@ -209,6 +212,48 @@ int oracle_rle(const uint32_t *keys, int64_t n, uint32_t *values, uint32_t *leng
     offsets[c] = n;
     for (int64_t r = 0; r < c; ++r)
         lengths[r] = (uint32_t)(offsets[r + 1] - offsets[r]);
+    *count = c;
+    return 0;
+}
+
+/*
+ * oracle_unique: the distinct adjacent values of n uint32 keys (luma.gl
+ * "GPURunLengthEncode and GPUUnique", section "GPUUnique": the run values of
+ * the RLE, with the same bitwise equality and first-occurrence order, and no
+ * lengths).  Writes values[0..count) and *count.
+ */
+int oracle_unique(const uint32_t *keys, int64_t n, uint32_t *values, int64_t *count)
+{
+    if (n < 0)
+        return -1;
+    int64_t c = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const int starts_run = (c == 0) || (keys[i] != values[c - 1]);
+        if (starts_run)
+            values[c++] = keys[i];
+    }
+    *count = c;
+    return 0;
+}
+
+/*
+ * oracle_offsets_from_flags: segment offsets from segment-start flags (luma.gl
+ * "GPUSegmentedReduction", "Composition": the segmented layout turns start
+ * flags into offsets).  Position i starts a segment iff flags[i] != 0; the
+ * starts, in position order, are offsets[0..count), offsets[count] = n closes
+ * the last segment, *count = number of starts.  Positions before the first
+ * start belong to no segment (offsets[0] may be above 0); no flag set gives
+ * count 0 and offsets[0] = n.
+ */
+int oracle_offsets_from_flags(const uint32_t *flags, int64_t n, int64_t *offsets, int64_t *count)
+{
+    if (n < 0)
+        return -1;
+    int64_t c = 0;
+    for (int64_t i = 0; i < n; ++i)
+        if (flags[i] != 0)
+            offsets[c++] = i;
+    offsets[c] = n;
     *count = c;
     return 0;
 }

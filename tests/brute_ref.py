@@ -126,3 +126,17 @@ def scatter(rows, index, dim_size, op, kind, feat):
 def offsets_from_index(index, dim_size):
     """Counting by definition: offsets[s] = #{r : 0 <= index[r] < s}."""
     return [sum(1 for x in index if 0 <= x < s) for s in range(dim_size + 1)]
+
+
+def unique(keys):
+    """Adjacent distinct values by definition: keep a key when it differs from the last kept one."""
+    out = []
+    for k in keys:
+        if not out or out[-1] != k:
+            out.append(k)
+    return out
+
+
+def offsets_from_flags(flags):
+    """Segment starts by definition: every position with a nonzero flag, then the length."""
+    return [i for i, f in enumerate(flags) if f] + [len(flags)]

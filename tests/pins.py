@@ -447,7 +447,57 @@ def pin_scatter_library(lib, seed=17):
             assert np.array_equal(a.arg, b.arg), op
 
 
+# ---------------------------------------------------------------- unique and start flags
+
+def pin_unique(lib, seed=19):
+    """GPUUnique (luma.gl RLE page, 'GPUUnique'): the printed RLE examples'
+    values, then itertools.groupby, numpy's adjacent-difference mask and the
+    brute-force definition on random keys (long runs and all-distinct)."""
+    g = _golden("run_length_encode_examples.json")
+    for case in g["cases"]:
+        v, c = oracle.unique(np.array(case["input"], dtype=np.uint32), lib=lib)
+        assert v.tolist() == case["values"] and c == len(case["values"]), case["cite"]
+    rng = np.random.default_rng(seed)
+    for trial in range(40):
+        n = int(rng.integers(0, 500))
+        keys = np.repeat(rng.integers(0, 4, n), rng.integers(1, 7, n))[:n].astype(np.uint32)
+        if trial % 3 == 0:
+            keys = rng.integers(0, 2 ** 32, n, dtype=np.uint64).astype(np.uint32)
+        v, c = oracle.unique(keys, lib=lib)
+        assert v.tolist() == [k for k, _ in itertools.groupby(keys.tolist())]
+        if n:
+            assert np.array_equal(v, keys[np.concatenate([[True], keys[1:] != keys[:-1]])])
+        assert v.tolist() == brute_ref.unique(keys.tolist()) and c == v.size
+
+
+def pin_offsets_from_flags(lib, seed=23):
+    """Offsets from segment-start flags: the printed layouts (tests/golden),
+    numpy flatnonzero, brute force, and the RLE identity: the run-start flags
+    of any key vector give the RLE offsets."""
+    g = _golden("segment_start_flags.json")
+    for case in g["cases"]:
+        off, c = oracle.offsets_from_flags(np.array(case["flags"], dtype=np.uint32), lib=lib)
+        assert off.tolist() == case["offsets"] and c == case["count"], case["cite"]
+    rng = np.random.default_rng(seed)
+    for trial in range(40):
+        n = int(rng.integers(0, 600))
+        flags = (rng.random(n) < rng.choice([0.0, 0.02, 0.3, 1.0])).astype(np.uint32)
+        flags *= rng.integers(1, 2 ** 32, n, dtype=np.uint64).astype(np.uint32) | np.uint32(2)  # any nonzero word
+        off, c = oracle.offsets_from_flags(flags, lib=lib)
+        assert off.tolist() == np.flatnonzero(flags).tolist() + [n]
+        assert off.tolist() == brute_ref.offsets_from_flags(flags.tolist()) and c == off.size - 1
+        keys = np.repeat(rng.integers(0, 3, n), rng.integers(1, 5, n))[:n].astype(np.uint32)
+        heads = np.ones(n, dtype=np.uint32)
+        if n:
+            heads[1:] = keys[1:] != keys[:-1]
+        _, _, roff, rc = oracle.rle(keys, lib=lib)
+        off2, c2 = oracle.offsets_from_flags(heads, lib=lib)
+        assert off2.tolist() == roff.tolist() and c2 == rc
+
+
 ALL_PINS = [
+    pin_unique,
+    pin_offsets_from_flags,
     pin_scatter_worked_example,
     pin_scatter_brute,
     pin_scatter_library,

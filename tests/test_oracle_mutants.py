@@ -37,7 +37,7 @@ MUTANTS = [
      "load_bits(values, r + f));\n                        sum"),
     ("arg_relative_to_segment", "arg_out[o] = best_row;", "arg_out[o] = best_row - lo;"),
     ("rle_only_increasing_boundaries", "keys[i] != keys[i - 1]", "keys[i] > keys[i - 1]"),
-    ("rle_last_offset_short", "offsets[c] = n;", "offsets[c] = n - (n > 0);"),
+    ("rle_last_offset_short", "offsets[c] = n;\n    for (int64_t r", "offsets[c] = n - (n > 0);\n    for (int64_t r"),
     ("scatter_drops_output_zero", "if (s < 0 || s >= dim_size)\n            continue;\n        count",
      "if (s < 1 || s >= dim_size)\n            continue;\n        count"),
     ("scatter_drops_first_row", "for (int64_t r = 0; r < rows; ++r) {\n        const int64_t s = index[r];\n        if (s < 0",
@@ -55,6 +55,11 @@ MUTANTS = [
      "const uint32_t b = load_bits(values, r + f * (r + 1 < rows));"),
     ("index_offsets_shifted", "offsets[s + 1] += 1;", "offsets[s] += 1;"),
     ("index_offsets_not_cumulative", "offsets[s + 1] += offsets[s];", "offsets[s + 1] = offsets[s + 1];"),
+    ("unique_only_increasing", "keys[i] != values[c - 1]", "keys[i] > values[c - 1]"),
+    ("unique_compares_first_kept", "keys[i] != values[c - 1]", "keys[i] != values[0]"),
+    ("flags_low_bit_only", "if (flags[i] != 0)", "if ((flags[i] & 1u) != 0)"),
+    ("flags_offset_shifted", "offsets[c++] = i;", "offsets[c++] = i + (i + 1 < n);"),
+    ("flags_last_offset_short", "offsets[c] = n;\n    *count = c;", "offsets[c] = n - (n > 0);\n    *count = c;"),
     ("rle_length_off_by_one", "(uint32_t)(offsets[r + 1] - offsets[r])", "(uint32_t)(offsets[r + 1] - offsets[r] - 1)"),
 ]
 
