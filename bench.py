@@ -117,7 +117,7 @@ class RleWorkload(Workload):
         pi = torch.from_numpy(cfg["i32"]).cuda()
         self.sets = [(k, pu, pi)] + [(k.clone(), pu.clone(), pi.clone()) for _ in range(copies - 1)]
         self.n = int(cfg["keys"].size)
-        self.calls = [("sum_u32", "sum"), ("min_i32", "min")]
+        self.calls = [("rle_count", None), ("rle_materialize", None), ("sum_u32", "sum"), ("min_i32", "min")]
         self.kernels_per_step = 3 + 2 * 2  # three RLE kernels, two per reduce call
         # the run count of this input (fixed by the seed), for the byte count
         _, _, _, cnt = sr.offsets_from_rle(k)
@@ -140,6 +140,10 @@ class RleWorkload(Workload):
         return self.n * 4 + self.count * (4 + 4 + 8) + 8 + 8
 
     def call_bytes(self, label):
+        if label == "rle_count":
+            return self.n * 4
+        if label == "rle_materialize":
+            return self.n * 4 + self.count * (4 + 4 + 8) + 8
         return reduce_bytes(self.n, 1, self.count, "min" if label == "min_i32" else "sum")
 
     def bytes_per_step(self):
@@ -190,6 +194,49 @@ class ScatterWorkload(Workload):
         return self.rows * self.feat * len(self.ops)
 
 
+class RunsWorkload(Workload):
+    """The RLE's relatives on the same 16M Zipf keys: the distinct adjacent
+    values (unique) or the offsets of the run-start flags (flags)."""
+
+    kernel_name = "rle_materialize"
+
+    def __init__(self, cfg, mode, copies, sr, torch):
+        import numpy as np
+        self.sr, self.torch, self.cfg, self.mode = sr, torch, cfg, mode
+        keys = cfg["keys"]
+        self.n = int(keys.size)
+        if mode == "flags":
+            heads = np.ones(self.n, dtype=np.uint32)
+            heads[1:] = keys[1:] != keys[:-1]
+            self.host_in = heads
+        else:
+            self.host_in = keys
+        x = torch.from_numpy(self.host_in).cuda()
+        self.inputs = [x] + [x.clone() for _ in range(copies - 1)]
+        self.calls = [("rle_count", None), ("rle_materialize", None)]
+        self.kernels_per_step = 3
+        fn = sr.unique if mode == "unique" else sr.offsets_from_flags
+        _, cnt = fn(x)
+        self.count = int(cnt.item())
+        self.outs = {}
+
+    def step(self, i):
+        x = self.inputs[i % len(self.inputs)]
+        self.outs[self.mode] = self.sr.unique(x) if self.mode == "unique" else self.sr.offsets_from_flags(x)
+
+    def out_bytes(self):
+        return self.count * 4 + 8 if self.mode == "unique" else (self.count + 1) * 8 + 8
+
+    def call_bytes(self, label):
+        return self.n * 4 + (self.out_bytes() if label == "rle_materialize" else 0)
+
+    def bytes_per_step(self):
+        return self.n * 4 + self.out_bytes()
+
+    def elems_per_step(self):
+        return self.n
+
+
 DESCRIPTIONS = {
     "small": "1-D f32 and i32, 4,096 segments, lengths uniform in [0,64] (~3% empty): f32 sum/min/max/mean",
     "message": "graph message passing: 1,000,000 destination-sorted rows x F=64 f32 normal(0,1) into "
@@ -200,6 +247,10 @@ DESCRIPTIONS = {
             "segment, 10% empty); sum and min+argmin",
     "powerlaw": "power-law graph: 2M nodes, 32M destination-sorted edges (in-degree Lomax alpha=2, hub of "
                 "200K), F=32 f32 normal(0,1), int64 indptr; sum, mean and max+argmax",
+    "unique": "distinct adjacent values of 16M sorted uint32 Zipf(1.1) keys over 2^20 values (values + "
+              "device-side count, no lengths)",
+    "flags": "offsets from segment-start flags: the run-start flags (uint32 0/1) of 16M sorted Zipf(1.1) keys "
+             "-> offsets + device-side count",
     "scatter": "scatter path: 1,000,000 rows x F=64 f32 normal(0,1) in edge order, unsorted int64 destination "
                "index uniform over 10,000 outputs; atomic scatter sum and scatter max+argmax",
     "scatter16": "scatter path: 1,000,000 rows x F=16 f32 normal(0,1) in edge order, unsorted int64 "
@@ -212,6 +263,9 @@ def build_workload(name, sr, torch):
     if name == "rle":
         cfg = W.rle_keys()
         return RleWorkload(cfg, copies=4, sr=sr, torch=torch), cfg
+    if name in ("unique", "flags"):
+        cfg = W.rle_keys()
+        return RunsWorkload(cfg, name, copies=4, sr=sr, torch=torch), cfg
     if name in ("scatter", "scatter16"):
         cfg = W.scatter(feat=64 if name == "scatter" else 16)
         nbytes = cfg["f32"].nbytes + cfg["index"].nbytes
@@ -235,7 +289,15 @@ def cpu_baseline(wl, name, budget_s):
     t = 0.0
     reps = 0
     results = {}
-    if isinstance(wl, RleWorkload):
+    if isinstance(wl, RunsWorkload):
+        fn = oracle.unique if wl.mode == "unique" else oracle.offsets_from_flags
+        while reps == 0 or (t < budget_s and reps < 50):
+            t0 = time.perf_counter()
+            results[wl.mode] = fn(wl.host_in, lib=lib)
+            t += time.perf_counter() - t0
+            reps += 1
+        sample = f"full workload ({name}), {reps} rep(s)"
+    elif isinstance(wl, RleWorkload):
         cfg = wl.cfg
         while reps == 0 or (t < budget_s and reps < 50):
             t0 = time.perf_counter()
@@ -271,6 +333,13 @@ def check_parity(wl, results):
     """GPU outputs of the last step against the oracle (same bars as the tests)."""
     import numpy as np
     verdict = {}
+    if isinstance(wl, RunsWorkload):
+        arr, c = results[wl.mode]
+        got, gc = wl.outs[wl.mode]
+        gc = int(gc.item())
+        k = c if wl.mode == "unique" else c + 1
+        verdict[wl.mode] = bool(gc == c == wl.count and np.array_equal(got[:k].cpu().numpy(), arr))
+        return verdict
     if isinstance(wl, RleWorkload):
         v, ln, off, c = results["rle"]
         gv, gl, go, gc = wl.outs["rle"]
@@ -438,7 +507,8 @@ def main():
     traffic = load_traffic(args.config, dominant, src_hash)
     roofline = {"bound": "hbm", "achieved": dk["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": dk["frac"], "traffic": traffic,
-                "kernel": f"{getattr(wl, 'kernel_name', 'seg_reduce_pass1')} ({dominant})",
+                "kernel": (dominant if dominant.startswith("rle_")
+                           else f"{getattr(wl, 'kernel_name', 'seg_reduce_pass1')} ({dominant})"),
                 "algorithmic_bytes_per_launch": dk["bytes"], "avg_launch_us": dk["avg_us"],
                 "timing": "kernel-stamped HIP stop events (hipExtLaunchKernel) on the launch stream, end of "
                           "previous kernel to end of this one, a second pass of the same K steps, minus the "
@@ -477,10 +547,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if args.config != "rle" else "u32/i32",
+        "dtype": {"rle": "u32/i32", "unique": "u32", "flags": "u32"}.get(args.config, "f32"),
         "data": "synthetic (seeded numpy generators, workloads.py)",
         "config": {"workload": DESCRIPTIONS[args.config], "name": cfg.get("name", args.config),
-                   "input_copies_rotated": len(getattr(wl, "vals", getattr(wl, "sets", [None])))},
+                   "input_copies_rotated": len(getattr(wl, "vals", getattr(wl, "sets", getattr(wl, "inputs",
+                                                                                           [None]))))},
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "gelem_per_s": round(gelem, 3),
         "bytes_per_step": bytes_step,

@@ -122,6 +122,56 @@ int segred_offsets_from_rle(const uint32_t *sorted_keys, int64_t n,
                             int64_t *offsets, int64_t *count, hipStream_t stream);
 
 /*
+ * segred_unique -- the distinct adjacent values of uint32 keys.
+ *
+ * Defined by the luma.gl "GPURunLengthEncode and GPUUnique" page, section
+ * "GPUUnique": the same equality (bit for bit) and first-occurrence order as
+ * segred_offsets_from_rle, i.e. its `values` and `count`, without run
+ * lengths; [2,2,5,2] gives [2,5,2] (adjacency, not global uniqueness).
+ *
+ *   keys    uint32 [n], any order.
+ *   n       0 <= n <= 2^40.
+ *   values  uint32, capacity n: values[r] = key of run r.
+ *   count   one int64 on the device: the number of runs.
+ *   stream  HIP stream the work is ordered on.
+ *
+ * Only values[0..count) is written.  Errors: SEGRED_ERR_INVALID_ARGUMENT for
+ * n out of range, a NULL values/count (or keys with n > 0), misalignment
+ * (4 bytes for keys and values, 8 for count).  SEGRED_ERR_OUT_OF_MEMORY,
+ * SEGRED_ERR_HIP as for segred_reduce.
+ */
+int segred_unique(const uint32_t *keys, int64_t n, uint32_t *values, int64_t *count,
+                  hipStream_t stream);
+
+/*
+ * segred_offsets_from_flags -- segment offsets from segment-start flags.
+ *
+ * Defined by the luma.gl "GPUSegmentedReduction" page, section
+ * "Composition" (a segmented layout materialises offsets from segment-start
+ * flags) with the offsets contract of the same page ("What is an
+ * offset-delimited segment?": N segments take N + 1 offsets, the last one
+ * closes the last segment).  Position i starts a segment iff flags[i] != 0.
+ *
+ *   flags    uint32 [n]; any nonzero word marks a start.
+ *   n        0 <= n <= 2^40.
+ *   offsets  int64, capacity n + 1: offsets[0..count) = the flagged
+ *            positions in increasing order, offsets[count] = n.  Positions
+ *            before the first flag belong to no segment (offsets[0] > 0 is
+ *            allowed by segred_reduce); no flag at all gives count 0 and
+ *            offsets[0] = n.
+ *   count    one int64 on the device: the number of segments.
+ *   stream   HIP stream the work is ordered on.
+ *
+ * Only offsets[0..count] is written.  The result feeds segred_reduce (read
+ * `count` back) or segred_reduce_device_count (no readback).  Errors:
+ * SEGRED_ERR_INVALID_ARGUMENT for n out of range, a NULL offsets/count (or
+ * flags with n > 0), misalignment (4 bytes for flags, 8 for offsets and
+ * count).  SEGRED_ERR_OUT_OF_MEMORY, SEGRED_ERR_HIP as for segred_reduce.
+ */
+int segred_offsets_from_flags(const uint32_t *flags, int64_t n, int64_t *offsets, int64_t *count,
+                              hipStream_t stream);
+
+/*
  * segred_reduce_device_count -- segred_reduce with the segment count read on
  * the device, for the sort -> RLE -> offsets -> reduce composition that the
  * "GPURunLengthEncode and GPUUnique" page draws ("Composition": run lengths
@@ -240,9 +290,12 @@ int64_t segred_get_shares(int32_t dtype, int32_t op, int64_t feat);
  * Kernel timing (instrumentation for benchmarks).  While enabled, every
  * kernel the library launches carries a HIP event that the runtime stamps
  * when that kernel ends (hipExtLaunchKernel).  segred_timing_read waits for
- * the recorded events and reports, for every streaming (first) kernel of a
- * segred_reduce call, the time from the end of the launch recorded before it
- * to its own end (-1 for the first launch of the record, which has none):
+ * the recorded events and reports, for every streaming kernel (the first
+ * kernel of a segred_reduce call, the atomic kernel of segred_scatter_reduce,
+ * the histogram of segred_offsets_from_index, the counting and materialising
+ * kernels of segred_offsets_from_rle / segred_unique /
+ * segred_offsets_from_flags), the time from the end of the launch recorded
+ * before it to its own end (-1 for the first launch of the record):
  * when the library's kernels run back to back on one stream (nothing else
  * queued in between), this is the streaming kernel's execution time.  It
  * returns the summed duration of the timed launches in milliseconds and the

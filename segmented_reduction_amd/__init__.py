@@ -10,6 +10,8 @@ There is no CPU fallback: if the library is missing, calls raise.
     values, lengths, offsets, count = offsets_from_rle(sorted_keys)
     out, arg = scatter(values, index, dim_size, "max")  # unsorted int64 index [N]
     offsets = offsets_from_index(sorted_index, dim_size)
+    values, count = unique(keys)                       # distinct adjacent values
+    offsets, count = offsets_from_flags(start_flags)   # uint32 flags, nonzero = start
 """
 from __future__ import annotations
 
@@ -62,6 +64,10 @@ def library(path: str | None = None):
             lib.segred_scatter_reduce.restype = ctypes.c_int
             lib.segred_offsets_from_index.argtypes = [vp, i64, i64, vp, vp]
             lib.segred_offsets_from_index.restype = ctypes.c_int
+            lib.segred_unique.argtypes = [vp, i64, vp, vp, vp]
+            lib.segred_unique.restype = ctypes.c_int
+            lib.segred_offsets_from_flags.argtypes = [vp, i64, vp, vp, vp]
+            lib.segred_offsets_from_flags.restype = ctypes.c_int
             lib.segred_status_string.argtypes = [ctypes.c_int]
             lib.segred_status_string.restype = ctypes.c_char_p
             lib.segred_set_shares.argtypes = [i64]
@@ -249,6 +255,41 @@ def offsets_from_index(index: torch.Tensor, dim_size: int) -> torch.Tensor:
                                                  offsets.data_ptr(), _stream(index.device))
     _check(rc, "segred_offsets_from_index")
     return offsets
+
+
+def unique(keys: torch.Tensor):
+    """Distinct adjacent values of uint32 ``keys`` (segred_unique).
+
+    Returns (values [n], count [1] int64) on the GPU, written asynchronously;
+    only values[:count] is meaningful."""
+    if not keys.is_cuda or keys.dtype != torch.uint32 or keys.dim() != 1 or not keys.is_contiguous():
+        raise ValueError("keys must be a contiguous 1-D uint32 GPU tensor")
+    n = keys.numel()
+    values = torch.empty(max(n, 1), dtype=torch.uint32, device=keys.device)
+    count = torch.empty(1, dtype=torch.int64, device=keys.device)
+    with torch.cuda.device(keys.device):
+        rc = library().segred_unique(keys.data_ptr() if n else None, n, values.data_ptr(), count.data_ptr(),
+                                     _stream(keys.device))
+    _check(rc, "segred_unique")
+    return values, count
+
+
+def offsets_from_flags(flags: torch.Tensor):
+    """Offsets of the segments that uint32 start ``flags`` open (nonzero =
+    start; segred_offsets_from_flags).
+
+    Returns (offsets [n + 1], count [1] int64) on the GPU, written
+    asynchronously; only offsets[:count + 1] is meaningful."""
+    if not flags.is_cuda or flags.dtype != torch.uint32 or flags.dim() != 1 or not flags.is_contiguous():
+        raise ValueError("flags must be a contiguous 1-D uint32 GPU tensor")
+    n = flags.numel()
+    offsets = torch.empty(n + 1, dtype=torch.int64, device=flags.device)
+    count = torch.empty(1, dtype=torch.int64, device=flags.device)
+    with torch.cuda.device(flags.device):
+        rc = library().segred_offsets_from_flags(flags.data_ptr() if n else None, n, offsets.data_ptr(),
+                                                 count.data_ptr(), _stream(flags.device))
+    _check(rc, "segred_offsets_from_flags")
+    return offsets, count
 
 
 def set_shares(shares: int):

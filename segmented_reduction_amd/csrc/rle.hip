@@ -12,6 +12,15 @@
 // (the start that follows each tile); (3) each tile ranks its starts in
 // position order through LDS and writes values, offsets and lengths with
 // consecutive lanes on consecutive runs.
+//
+// The same three launches serve two relatives, chosen by a mode: the
+// distinct adjacent values alone (same page, "GPUUnique": RLE's equality and
+// order, values only, so no lengths, offsets or right-to-left scan), and
+// offsets from segment-start flags (luma.gl "GPUSegmentedReduction",
+// "Composition": position i starts a segment iff flags[i] != 0; offsets
+// only, closed by n).
+#include <algorithm>
+
 #include "internal.hpp"
 #include "scan.hpp"
 #include "wave.hpp"
@@ -22,6 +31,10 @@ constexpr int kRleThreads = 256;
 constexpr int kRleKeysPerThread = 16;
 constexpr int kRleTile = kRleThreads * kRleKeysPerThread;
 constexpr int kScanThreads = 1024;
+
+enum { MODE_RLE = 0, MODE_UNIQUE = 1, MODE_FLAGS = 2 };
+// Unique and flags inputs: the tile count stays below 2^31 workgroups.
+constexpr int64_t kMaxPositions = int64_t(1) << 40;
 
 // Keys of one tile: thread (wave w, lane l) holds positions
 // tile_start + u * 256 + w * 64 + l, u = 0..15, and whether each starts a run.
@@ -35,9 +48,20 @@ struct TileKeys {
 // 0), and for each wave's first position the key before it (one address for
 // the whole wave; for position 0 of the input the offset wraps out of range
 // and the value is not used).
+template <int MODE>
 __device__ __forceinline__ void load_tile(const uint32_t *keys, int64_t n, int64_t start, int tid, TileKeys &t) {
     const int lane = tid & 63, wid = tid >> 6;
     const int64_t avail = min((int64_t)kRleTile, n - start);
+    if constexpr (MODE == MODE_FLAGS) {
+        // a start is a nonzero flag: no neighbour is needed
+        const auto rf = make_rsrc(keys + start, (uint32_t)(avail * 4));
+#pragma unroll
+        for (int u = 0; u < kRleKeysPerThread; ++u) t.k[u] = ld32(rf, (uint32_t)((u * kRleThreads + tid) * 4), 0);
+#pragma unroll
+        for (int u = 0; u < kRleKeysPerThread; ++u)
+            t.head[u] = start + u * kRleThreads + tid < n && t.k[u] != 0u;
+        return;
+    }
     const int64_t back = start > 0 ? 1 : 0;
     const auto rs = make_rsrc(keys + start, (uint32_t)(avail * 4));
     const auto rp = make_rsrc(keys + start - back, (uint32_t)((avail + back) * 4));
@@ -58,6 +82,7 @@ __device__ __forceinline__ void load_tile(const uint32_t *keys, int64_t n, int64
     }
 }
 
+template <int MODE>
 __global__ __launch_bounds__(kRleThreads) void rle_count(const uint32_t *keys, int64_t n, int64_t *tile_count,
                                                          int64_t *tile_first) {
     __shared__ int64_t s_cnt[4];
@@ -65,7 +90,7 @@ __global__ __launch_bounds__(kRleThreads) void rle_count(const uint32_t *keys, i
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int64_t start = (int64_t)blockIdx.x * kRleTile;
     TileKeys t;
-    load_tile(keys, n, start, tid, t);
+    load_tile<MODE>(keys, n, start, tid, t);
     int64_t cnt = 0, first = INT64_MAX;
 #pragma unroll
     for (int u = 0; u < kRleKeysPerThread; ++u) {
@@ -85,7 +110,7 @@ __global__ __launch_bounds__(kRleThreads) void rle_count(const uint32_t *keys, i
             f = s_first[w] < f ? s_first[w] : f;
         }
         tile_count[blockIdx.x] = c;
-        tile_first[blockIdx.x] = f;
+        if (MODE == MODE_RLE) tile_first[blockIdx.x] = f;
     }
 }
 
@@ -94,7 +119,10 @@ __global__ __launch_bounds__(kRleThreads) void rle_count(const uint32_t *keys, i
 // tiles' first starts, from the right).  Each thread takes K consecutive
 // tiles of a batch of 1024 * K, so a batch costs one round of loads issued
 // together, a short serial pass per thread and one block-wide scan.
+// Only the RLE needs the right-to-left pass (it bounds the last run of a
+// tile); the flags mode writes offsets[count] = n as the RLE does.
 constexpr int kScanPer = 4;
+template <int MODE>
 __global__ __launch_bounds__(kScanThreads) void rle_scan(int64_t tiles, int64_t n, const int64_t *tile_count,
                                                          const int64_t *tile_first, int64_t *tile_base,
                                                          int64_t *tile_next, int64_t *count, int64_t *offsets) {
@@ -127,6 +155,14 @@ __global__ __launch_bounds__(kScanThreads) void rle_scan(int64_t tiles, int64_t 
             if (t < tiles) tile_base[t] = running + ex + in[j];
         }
         running += total;
+    }
+
+    if (MODE != MODE_RLE) {
+        if (tid == 0) {
+            *count = running;
+            if (MODE == MODE_FLAGS) offsets[running] = n;
+        }
+        return;
     }
 
     // Right to left: thread order runs from the last tile down (reversed
@@ -171,6 +207,7 @@ __global__ __launch_bounds__(kScanThreads) void rle_scan(int64_t tiles, int64_t 
     }
 }
 
+template <int MODE>
 __global__ __launch_bounds__(kRleThreads) void rle_materialize(const uint32_t *keys, int64_t n,
                                                                const int64_t *tile_base, const int64_t *tile_next,
                                                                uint32_t *values, uint32_t *lengths,
@@ -181,7 +218,7 @@ __global__ __launch_bounds__(kRleThreads) void rle_materialize(const uint32_t *k
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int64_t start = (int64_t)blockIdx.x * kRleTile;
     TileKeys t;
-    load_tile(keys, n, start, tid, t);
+    load_tile<MODE>(keys, n, start, tid, t);
     uint64_t m[kRleKeysPerThread];
 #pragma unroll
     for (int u = 0; u < kRleKeysPerThread; ++u) {
@@ -209,19 +246,50 @@ __global__ __launch_bounds__(kRleThreads) void rle_materialize(const uint32_t *k
     __syncthreads();
     const int cnt = base;
     const int64_t rb = tile_base[blockIdx.x];
-    const int64_t next = tile_next[blockIdx.x];
+    const int64_t next = MODE == MODE_RLE ? tile_next[blockIdx.x] : 0;
     for (int q = tid; q < cnt; q += kRleThreads) {
         const int64_t pos = start + s_pos[q];
-        const int64_t npos = q + 1 < cnt ? start + s_pos[q + 1] : next;
-        values[rb + q] = s_key[q];
-        offsets[rb + q] = pos;
-        lengths[rb + q] = (uint32_t)(npos - pos);
+        if (MODE != MODE_FLAGS) values[rb + q] = s_key[q];
+        if (MODE != MODE_UNIQUE) offsets[rb + q] = pos;
+        if (MODE == MODE_RLE) {
+            const int64_t npos = q + 1 < cnt ? start + s_pos[q + 1] : next;
+            lengths[rb + q] = (uint32_t)(npos - pos);
+        }
     }
 }
 
 }  // namespace segred
 
 using namespace segred;
+
+namespace segred {
+
+// The three launches of one mode; scratch holds the per-tile records.
+template <int MODE>
+int rle_launch(const uint32_t *keys, int64_t n, uint32_t *values, uint32_t *lengths, int64_t *offsets,
+               int64_t *count, hipStream_t stream) {
+    const int64_t tiles = (n + kRleTile - 1) / kRleTile;
+    ScratchLease scratch;
+    int rc = scratch_acquire(scratch, (size_t)std::max<int64_t>(tiles, 1) * 4 * sizeof(int64_t), stream);
+    if (rc != SEGRED_OK) return rc;
+    int64_t *tcount = static_cast<int64_t *>(scratch.ptr);
+    int64_t *tfirst = tcount + tiles;
+    int64_t *tbase = tfirst + tiles;
+    int64_t *tnext = tbase + tiles;
+
+    if (tiles > 0)
+        hipExtLaunchKernelGGL(rle_count<MODE>, dim3((unsigned)tiles), dim3(kRleThreads), 0, stream, nullptr,
+                              timing_stop(true), 0, keys, n, tcount, tfirst);
+    hipExtLaunchKernelGGL(rle_scan<MODE>, dim3(1), dim3(kScanThreads), 0, stream, nullptr, timing_stop(false), 0,
+                          tiles, n, (const int64_t *)tcount, (const int64_t *)tfirst, tbase, tnext, count, offsets);
+    if (tiles > 0)
+        hipExtLaunchKernelGGL(rle_materialize<MODE>, dim3((unsigned)tiles), dim3(kRleThreads), 0, stream, nullptr,
+                              timing_stop(true), 0, keys, n, (const int64_t *)tbase, (const int64_t *)tnext, values,
+                              lengths, offsets);
+    return hipGetLastError() == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
+}
+
+}  // namespace segred
 
 extern "C" int segred_offsets_from_rle(const uint32_t *sorted_keys, int64_t n, uint32_t *values,
                                        uint32_t *lengths, int64_t *offsets, int64_t *count,
@@ -231,24 +299,21 @@ extern "C" int segred_offsets_from_rle(const uint32_t *sorted_keys, int64_t n, u
     if ((sorted_keys && !aligned(sorted_keys, 4)) || !aligned(values, 4) || !aligned(lengths, 4) ||
         !aligned(offsets, 8) || !aligned(count, 8))
         return SEGRED_ERR_INVALID_ARGUMENT;
+    return rle_launch<MODE_RLE>(sorted_keys, n, values, lengths, offsets, count, stream);
+}
 
-    const int64_t tiles = (n + kRleTile - 1) / kRleTile;
-    ScratchLease scratch;
-    int rc = scratch_acquire(scratch, (size_t)tiles * 4 * sizeof(int64_t), stream);
-    if (rc != SEGRED_OK) return rc;
-    int64_t *tcount = static_cast<int64_t *>(scratch.ptr);
-    int64_t *tfirst = tcount + tiles;
-    int64_t *tbase = tfirst + tiles;
-    int64_t *tnext = tbase + tiles;
+extern "C" int segred_unique(const uint32_t *keys, int64_t n, uint32_t *values, int64_t *count,
+                             hipStream_t stream) {
+    if (n < 0 || n > kMaxPositions) return SEGRED_ERR_INVALID_ARGUMENT;
+    if (!values || !count || (n > 0 && !keys)) return SEGRED_ERR_INVALID_ARGUMENT;
+    if ((keys && !aligned(keys, 4)) || !aligned(values, 4) || !aligned(count, 8)) return SEGRED_ERR_INVALID_ARGUMENT;
+    return rle_launch<MODE_UNIQUE>(keys, n, values, nullptr, nullptr, count, stream);
+}
 
-    if (tiles > 0)
-        hipExtLaunchKernelGGL(rle_count, dim3((unsigned)tiles), dim3(kRleThreads), 0, stream, nullptr,
-                              timing_stop(false), 0, sorted_keys, n, tcount, tfirst);
-    hipExtLaunchKernelGGL(rle_scan, dim3(1), dim3(kScanThreads), 0, stream, nullptr, timing_stop(false), 0, tiles,
-                          n, (const int64_t *)tcount, (const int64_t *)tfirst, tbase, tnext, count, offsets);
-    if (tiles > 0)
-        hipExtLaunchKernelGGL(rle_materialize, dim3((unsigned)tiles), dim3(kRleThreads), 0, stream, nullptr,
-                              timing_stop(false), 0, sorted_keys, n, (const int64_t *)tbase,
-                              (const int64_t *)tnext, values, lengths, offsets);
-    return hipGetLastError() == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
+extern "C" int segred_offsets_from_flags(const uint32_t *flags, int64_t n, int64_t *offsets, int64_t *count,
+                                         hipStream_t stream) {
+    if (n < 0 || n > kMaxPositions) return SEGRED_ERR_INVALID_ARGUMENT;
+    if (!offsets || !count || (n > 0 && !flags)) return SEGRED_ERR_INVALID_ARGUMENT;
+    if ((flags && !aligned(flags, 4)) || !aligned(offsets, 8) || !aligned(count, 8)) return SEGRED_ERR_INVALID_ARGUMENT;
+    return rle_launch<MODE_FLAGS>(flags, n, nullptr, nullptr, offsets, count, stream);
 }

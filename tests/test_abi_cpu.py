@@ -28,7 +28,7 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for required in ("segred_reduce", "segred_offsets_from_rle", "segred_status_string", "segred_scatter_reduce",
-                     "segred_offsets_from_index"):
+                     "segred_offsets_from_index", "segred_unique", "segred_offsets_from_flags"):
         assert required in names
 
 
@@ -145,6 +145,30 @@ def test_scatter_argument_checks(args, expect):
 def test_offsets_from_index_argument_checks(args, expect):
     lib = _lib()
     assert lib.segred_offsets_from_index(*args, None) == expect
+
+
+@pytest.mark.parametrize("fn,args,expect", [
+    # (keys, n, values, count) for unique; (flags, n, offsets, count) for flags
+    ("segred_unique", (FAKE, -1, FAKE, FAKE), 1),
+    ("segred_unique", (FAKE, 2 ** 40 + 1, FAKE, FAKE), 1),
+    ("segred_unique", (None, 5, FAKE, FAKE), 1),
+    ("segred_unique", (FAKE, 5, None, FAKE), 1),
+    ("segred_unique", (FAKE, 5, FAKE, None), 1),
+    ("segred_unique", (FAKE + 2, 5, FAKE, FAKE), 1),
+    ("segred_unique", (FAKE, 5, FAKE + 2, FAKE), 1),
+    ("segred_unique", (FAKE, 5, FAKE, FAKE + 4), 1),
+    ("segred_offsets_from_flags", (FAKE, -1, FAKE, FAKE), 1),
+    ("segred_offsets_from_flags", (FAKE, 2 ** 40 + 1, FAKE, FAKE), 1),
+    ("segred_offsets_from_flags", (None, 5, FAKE, FAKE), 1),
+    ("segred_offsets_from_flags", (FAKE, 5, None, FAKE), 1),
+    ("segred_offsets_from_flags", (FAKE, 5, FAKE, None), 1),
+    ("segred_offsets_from_flags", (FAKE + 2, 5, FAKE, FAKE), 1),
+    ("segred_offsets_from_flags", (FAKE, 5, FAKE + 4, FAKE), 1),
+    ("segred_offsets_from_flags", (FAKE, 5, FAKE, FAKE + 4), 1),
+])
+def test_unique_and_flags_argument_checks(fn, args, expect):
+    lib = _lib()
+    assert getattr(lib, fn)(*args, None) == expect
 
 
 def test_share_knob_range():
