@@ -61,6 +61,8 @@ def _bind(lib):
     lib.oracle_scatter.restype = ctypes.c_int
     lib.oracle_offsets_from_index.argtypes = [vp, i64, i64, vp]
     lib.oracle_offsets_from_index.restype = ctypes.c_int
+    lib.oracle_scan.argtypes = [vp, i32, i64, vp, i64, i32, i32, vp, vp, vp]
+    lib.oracle_scan.restype = ctypes.c_int
     lib.oracle_unique.argtypes = [vp, i64, vp, vp]
     lib.oracle_unique.restype = ctypes.c_int
     lib.oracle_offsets_from_flags.argtypes = [vp, i64, vp, vp]
@@ -127,6 +129,36 @@ def rle(keys: np.ndarray, lib=None):
         raise ValueError("oracle_rle rejected its input")
     c = int(count[0])
     return values[:c], lengths[:c], offsets[: c + 1], c
+
+
+class Scanned:
+    """Result of a segmented scan: ``out`` [rows, F] (rows outside the
+    segments hold ``fill``), ``ref``/``mag`` float64 prefixes of x and |x|
+    for float32 sums (else None)."""
+
+    def __init__(self, out, ref, mag):
+        self.out, self.ref, self.mag = out, ref, mag
+
+
+def scan(values: np.ndarray, offsets: np.ndarray, op: str, exclusive: bool = False, fill=0, lib=None) -> Scanned:
+    """Segmented inclusive / exclusive scan (op in sum, min, max) of
+    ``values`` ([rows] or [rows, F]) over int64 ``offsets`` [S + 1]."""
+    lib = lib or load()
+    values = np.ascontiguousarray(values)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int64)
+    dt = dtype_name(values)
+    feat = 1 if values.ndim == 1 else int(np.prod(values.shape[1:]))
+    rows = int(values.shape[0])
+    out = np.full((rows, feat), fill, dtype=_NP[dt])
+    ref = mag = None
+    if dt == "f32" and op == "sum":
+        ref = np.zeros((rows, feat), dtype=np.float64)
+        mag = np.zeros((rows, feat), dtype=np.float64)
+    rc = lib.oracle_scan(_ptr(values), DTYPES[dt], feat, _ptr(offsets), int(offsets.shape[0]) - 1, OPS[op],
+                         int(bool(exclusive)), _ptr(out), _ptr(ref), _ptr(mag))
+    if rc != 0:
+        raise ValueError(f"oracle_scan rejected dtype={dt} op={op} feat={feat} (rc={rc})")
+    return Scanned(out, ref, mag)
 
 
 def unique(keys: np.ndarray, lib=None):

@@ -32,6 +32,8 @@
  *     adjacent values under the same equality, without lengths.
  *   - luma.gl "GPUSegmentedReduction", "Composition": a segmented layout
  *     materialises offsets from segment-start flags.
+ *   - luma.gl RLE page, "Composition": GPUSegmentedScan beside the
+ *     segmented reduction (read as the per-row prefix of the same operation).
  *   - phanerozoic/graph-reduce README, "API" and "Method": the scatter path
  *     reduces every row into the output its index names (the index need not
  *     be sorted), with the same sum / mean / min / max (+ row) semantics;
@@ -213,6 +215,89 @@ int oracle_rle(const uint32_t *keys, int64_t n, uint32_t *values, uint32_t *leng
     for (int64_t r = 0; r < c; ++r)
         lengths[r] = (uint32_t)(offsets[r + 1] - offsets[r]);
     *count = c;
+    return 0;
+}
+
+/*
+ * oracle_scan: segmented inclusive or exclusive scan over offset-delimited
+ * segments.  GPUSegmentedScan is only named by the luma.gl RLE page
+ * ("Composition", next to GPUSegmentedReduction); its reading here follows
+ * the segmented reduction's contract (same segments, dtypes, operations and
+ * order, empty prefix -> 0): for row r of segment s,
+ *   inclusive: out[r, f] = op of values[offsets[s]..r, f]
+ *   exclusive: out[r, f] = op of values[offsets[s]..r-1, f], 0 when r is the
+ *              segment's first row.
+ * Rows are visited in order with one running value per feature: double for
+ * float32 sums (ref_out gets the double prefix, abs_out the prefix of |x|),
+ * wrapping uint32 for integer sums, the best order key for min/max (out gets
+ * that value's bits).  Rows outside [offsets[0], offsets[S]) are not
+ * written.  op is ORC_SUM, ORC_MIN or ORC_MAX.
+ */
+int oracle_scan(const void *values, int32_t dtype, int64_t feat, const int64_t *offsets,
+                int64_t num_segments, int32_t op, int32_t exclusive,
+                void *out, double *ref_out, double *abs_out)
+{
+    if (dtype < ORC_U32 || dtype > ORC_F32 || op < ORC_SUM || op > ORC_MAX || feat < 1 || num_segments < 0)
+        return -1;
+    for (int64_t s = 0; s < num_segments; ++s) {
+        const int64_t lo = offsets[s], hi = offsets[s + 1];
+        for (int64_t f = 0; f < feat; ++f) {
+            double run = 0.0, run_abs = 0.0;
+            uint32_t run_int = 0, top_key = 0, top_bits = 0;
+            int seen = 0;
+            for (int64_t r = lo; r < hi; ++r) {
+                const int64_t o = r * feat + f;
+                const uint32_t b = load_bits(values, o);
+                if (exclusive) {
+                    /* the prefix before row r */
+                    if (op == ORC_SUM) {
+                        if (dtype == ORC_F32) {
+                            store_bits(out, o, float_to_bits((float)run));
+                            if (ref_out)
+                                ref_out[o] = run;
+                            if (abs_out)
+                                abs_out[o] = run_abs;
+                        } else {
+                            store_bits(out, o, run_int);
+                        }
+                    } else {
+                        store_bits(out, o, seen ? top_bits : 0u);
+                    }
+                }
+                if (op == ORC_SUM) {
+                    if (dtype == ORC_F32) {
+                        const double x = (double)bits_to_float(b);
+                        run += x;
+                        run_abs += x < 0 ? -x : x;
+                    } else {
+                        run_int += b;
+                    }
+                } else {
+                    const uint32_t k = oracle_order_key(b, dtype);
+                    if (!seen || ((op == ORC_MAX) ? (k > top_key) : (k < top_key))) {
+                        top_key = k;
+                        top_bits = b;
+                    }
+                    seen = 1;
+                }
+                if (!exclusive) {
+                    if (op == ORC_SUM) {
+                        if (dtype == ORC_F32) {
+                            store_bits(out, o, float_to_bits((float)run));
+                            if (ref_out)
+                                ref_out[o] = run;
+                            if (abs_out)
+                                abs_out[o] = run_abs;
+                        } else {
+                            store_bits(out, o, run_int);
+                        }
+                    } else {
+                        store_bits(out, o, top_bits);
+                    }
+                }
+            }
+        }
+    }
     return 0;
 }
 

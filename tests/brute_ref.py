@@ -140,3 +140,32 @@ def unique(keys):
 def offsets_from_flags(flags):
     """Segment starts by definition: every position with a nonzero flag, then the length."""
     return [i for i, f in enumerate(flags) if f] + [len(flags)]
+
+
+def scan(rows, offsets, op, kind, feat, exclusive):
+    """Segmented prefix by definition: for every row, the op over the rows of
+    its segment before it (exclusive; nothing -> 0) or up to it (inclusive),
+    recomputed from scratch with math.fsum / Python ints / min / max.
+    Returns {row: (list over features of outputs, list of exact float prefixes or None)}."""
+    res = {}
+    for s in range(len(offsets) - 1):
+        lo, hi = offsets[s], offsets[s + 1]
+        for r in range(lo, hi):
+            upto = range(lo, r) if exclusive else range(lo, r + 1)
+            outs, exact = [], []
+            for f in range(feat):
+                col = [rows[q][f] for q in upto]
+                if op == "sum":
+                    if kind == "f32":
+                        t = math.fsum(col)
+                        exact.append(t)
+                        outs.append(_round_f32(t))
+                    else:
+                        t = sum(col) % (1 << 32)
+                        if kind == "i32" and t >= (1 << 31):
+                            t -= 1 << 32
+                        outs.append(t)
+                else:
+                    outs.append((min(col) if op == "min" else max(col)) if col else 0)
+            res[r] = (outs, exact if kind == "f32" and op == "sum" else None)
+    return res

@@ -495,7 +495,93 @@ def pin_offsets_from_flags(lib, seed=23):
         assert off2.tolist() == roff.tolist() and c2 == rc
 
 
+# ---------------------------------------------------------------- segmented scan
+
+def pin_scan_against_printed_reduction(lib):
+    """The inclusive scan ends every segment on the printed segmented sum /
+    min / max (luma.gl GPUSegmentedReduction, 'What is segmented reduction?');
+    the exclusive scan starts every segment at 0 and lags the inclusive one by
+    a row."""
+    g = _golden("segmented_reduction_worked_example.json")
+    off = np.array(g["offsets"], dtype=np.int64)
+    for kind in ("u32", "i32", "f32"):
+        vals = np.array(g["values"], dtype=NP_T[kind])
+        for op in ("sum", "min", "max"):
+            inc = oracle.scan(vals, off, op, exclusive=False, lib=lib).out[:, 0]
+            exc = oracle.scan(vals, off, op, exclusive=True, lib=lib).out[:, 0]
+            assert [inc[int(off[s + 1]) - 1] for s in range(3)] == g[op], (kind, op)
+            for s in range(3):
+                lo, hi = int(off[s]), int(off[s + 1])
+                assert exc[lo] == 0 and np.array_equal(exc[lo + 1:hi], inc[lo:hi - 1]), (kind, op, s)
+
+
+def pin_scan_brute(lib, cases=200, seed=29):
+    """Scan oracle == brute force (each prefix recomputed from scratch) on tiny
+    random inputs with empty segments, offsets[0] > 0 and unread rows."""
+    rng = np.random.default_rng(seed)
+    for i in range(cases):
+        kind = ("u32", "i32", "f32")[i % 3]
+        feat = (1, 2, 3)[(i // 3) % 3]
+        vals, off = _random_case(rng, kind, feat)
+        rows = vals.tolist()
+        for op in ("sum", "min", "max"):
+            for exclusive in (False, True):
+                r = oracle.scan(vals if feat > 1 else vals[:, 0], off, op, exclusive, fill=7, lib=lib)
+                b = brute_ref.scan(rows, off.tolist(), op, kind, feat, exclusive)
+                for q in range(vals.shape[0]):
+                    if q not in b:
+                        assert (r.out[q] == 7).all(), (i, q)  # rows outside the segments are not written
+                        continue
+                    outs, exact = b[q]
+                    if exact is None:
+                        assert r.out[q].tolist() == outs, (i, kind, op, exclusive, q)
+                    else:
+                        for f in range(feat):
+                            assert abs(r.ref[q, f] - exact[f]) <= 1e-13 * r.mag[q, f] + 1e-300, (i, q, f)
+                            assert float(r.out[q, f]) == outs[f] or \
+                                abs(float(r.out[q, f]) - exact[f]) <= 2.0 ** -24 * abs(exact[f]) + 1e-13 * r.mag[q, f]
+
+
+def pin_scan_library(lib, seed=31):
+    """numpy per segment: cumsum (int64 mod 2^32, float64), minimum /
+    maximum.accumulate; the last inclusive row of each segment equals the
+    segmented reduction."""
+    rng = np.random.default_rng(seed)
+    lengths = rng.integers(0, 60, 300)
+    lengths[rng.random(300) < 0.2] = 0
+    off = np.concatenate([[4], 4 + np.cumsum(lengths)]).astype(np.int64)
+    n = int(off[-1]) + 3
+    cases = (("i32", rng.integers(-(2 ** 31), 2 ** 31, (n, 2)).astype(np.int32)),
+             ("u32", rng.integers(0, 2 ** 32, (n, 2), dtype=np.uint64).astype(np.uint32)),
+             ("f32", rng.standard_normal((n, 2)).astype(np.float32)))
+    for kind, vals in cases:
+        for op in ("sum", "min", "max"):
+            inc = oracle.scan(vals, off, op, False, lib=lib)
+            red = oracle.reduce(vals, off, op, lib=lib)
+            for s in range(300):
+                lo, hi = int(off[s]), int(off[s + 1])
+                if lo == hi:
+                    continue
+                seg = vals[lo:hi]
+                if op == "sum" and kind == "f32":
+                    want = np.cumsum(seg.astype(np.float64), axis=0)
+                    assert np.allclose(inc.ref[lo:hi], want, rtol=1e-12, atol=1e-12), (kind, s)
+                    assert abs(inc.ref[hi - 1, 0] - red.ref[s, 0]) <= 1e-12 * red.mag[s, 0] + 1e-300
+                    continue
+                if op == "sum":
+                    want = (np.cumsum(seg.astype(np.int64), axis=0) % (1 << 32)).astype(np.uint64)
+                    got = inc.out[lo:hi].view(np.uint32).astype(np.uint64)
+                else:
+                    acc = np.minimum.accumulate if op == "min" else np.maximum.accumulate
+                    want, got = acc(seg, axis=0), inc.out[lo:hi]
+                assert np.array_equal(got, want), (kind, op, s)
+                assert np.array_equal(inc.out[hi - 1].view(np.uint32), red.out[s].view(np.uint32)), (kind, op, s)
+
+
 ALL_PINS = [
+    pin_scan_against_printed_reduction,
+    pin_scan_brute,
+    pin_scan_library,
     pin_unique,
     pin_offsets_from_flags,
     pin_scatter_worked_example,

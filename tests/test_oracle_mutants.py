@@ -60,6 +60,15 @@ MUTANTS = [
     ("flags_low_bit_only", "if (flags[i] != 0)", "if ((flags[i] & 1u) != 0)"),
     ("flags_offset_shifted", "offsets[c++] = i;", "offsets[c++] = i + (i + 1 < n);"),
     ("flags_last_offset_short", "offsets[c] = n;\n    *count = c;", "offsets[c] = n - (n > 0);\n    *count = c;"),
+    ("scan_exclusive_block_inverted", "if (exclusive) {\n                    /* the prefix", "if (!exclusive) {\n                    /* the prefix"),
+    ("scan_float_sum_wrong_sign", "run += x;", "run -= x;"),
+    ("scan_magnitude_not_absolute", "run_abs += x < 0 ? -x : x;", "run_abs += x;"),
+    ("scan_min_max_swapped", "((op == ORC_MAX) ? (k > top_key) : (k < top_key))",
+     "((op == ORC_MAX) ? (k < top_key) : (k > top_key))"),
+    ("scan_exclusive_start_not_zero", "seen ? top_bits : 0u", "seen ? top_bits : b"),
+    ("scan_feature_stride_dropped", "const int64_t o = r * feat + f;\n                const uint32_t b",
+     "const int64_t o = r + f;\n                const uint32_t b"),
+    ("scan_int_sum_overwrites", "run_int += b;", "run_int = b;"),
     ("rle_length_off_by_one", "(uint32_t)(offsets[r + 1] - offsets[r])", "(uint32_t)(offsets[r + 1] - offsets[r] - 1)"),
 ]
 
