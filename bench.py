@@ -37,7 +37,8 @@ METRIC = "effective HBM GB/s (+% of peak) and Gelem/s for CSR segmented reduce, 
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["segmented_reduction_amd/csrc/reduce.hip", "segmented_reduction_amd/csrc/wave.hpp",
                   "segmented_reduction_amd/csrc/rle.hip", "segmented_reduction_amd/csrc/keys.hpp",
-                  "segmented_reduction_amd/csrc/scan.hpp", "segmented_reduction_amd/csrc/scatter.hip"]
+                  "segmented_reduction_amd/csrc/scan.hpp", "segmented_reduction_amd/csrc/scatter.hip",
+                  "segmented_reduction_amd/csrc/partition.hpp", "segmented_reduction_amd/csrc/segscan.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -194,6 +195,52 @@ class ScatterWorkload(Workload):
         return self.rows * self.feat * len(self.ops)
 
 
+class ScanWorkload(Workload):
+    """Segmented scans over the reduction's inputs: an inclusive sum and an
+    exclusive max (message) / min (skew) per step, outputs in the input
+    layout."""
+
+    kernel_name = "seg_scan_main"
+
+    def __init__(self, cfg, calls, copies, sr, torch):
+        self.sr, self.torch, self.cfg = sr, torch, cfg
+        self.host_off = cfg["offsets"]
+        self.host_vals = cfg["f32"]
+        self.rows = int(self.host_off[-1] - self.host_off[0])
+        self.segs = self.host_off.size - 1
+        self.feat = 1 if self.host_vals.ndim == 1 else int(self.host_vals.shape[1])
+        v = torch.from_numpy(self.host_vals).cuda()
+        self.vals = [v] + [v.clone() for _ in range(copies - 1)]
+        self.off = torch.from_numpy(self.host_off).cuda()
+        self.outs_buf = [torch.empty_like(v) for _ in range(2)]
+        self.ops = calls  # (op, exclusive)
+        # two streaming kernels per call (tails, main): label both
+        self.calls = []
+        for op, ex in calls:
+            tag = f"{'excl' if ex else 'incl'}_{op}"
+            self.calls += [(tag + "_tails", op), (tag, op)]
+        self.kernels_per_step = 2 * len(calls)
+        self.outs = {}
+
+    def step(self, i):
+        for j, (op, ex) in enumerate(self.ops):
+            v = self.vals[(i * len(self.ops) + j) % len(self.vals)]
+            self.outs[(op, ex)] = self.sr.scan(v, self.off, op, exclusive=ex, out=self.outs_buf[j % 2])
+
+    def call_bytes(self, label):
+        """Values read and outputs written once, plus the offsets; the tails
+        kernel reads only the rows of the segments that cross shares."""
+        if label.endswith("_tails"):
+            return (self.segs + 1) * 8
+        return 2 * self.rows * self.feat * 4 + (self.segs + 1) * 8
+
+    def bytes_per_step(self):
+        return len(self.ops) * (2 * self.rows * self.feat * 4 + (self.segs + 1) * 8)
+
+    def elems_per_step(self):
+        return self.rows * self.feat * len(self.ops)
+
+
 class RunsWorkload(Workload):
     """The RLE's relatives on the same 16M Zipf keys: the distinct adjacent
     values (unique) or the offsets of the run-start flags (flags)."""
@@ -251,6 +298,10 @@ DESCRIPTIONS = {
               "device-side count, no lengths)",
     "flags": "offsets from segment-start flags: the run-start flags (uint32 0/1) of 16M sorted Zipf(1.1) keys "
              "-> offsets + device-side count",
+    "scan": "segmented scan over the message-passing input: 1,000,000 destination-sorted rows x F=64 f32 "
+            "normal(0,1), 10,000 segments (multinomial, mean 100); inclusive sum and exclusive max per row",
+    "scan1d": "segmented scan over the heavy-skew input: 50M f32 uniform[0,1) in 1M segments (Pareto 1.5, one "
+              "5M-row segment, 10% empty); inclusive sum and exclusive min per element",
     "scatter": "scatter path: 1,000,000 rows x F=64 f32 normal(0,1) in edge order, unsorted int64 destination "
                "index uniform over 10,000 outputs; atomic scatter sum and scatter max+argmax",
     "scatter16": "scatter path: 1,000,000 rows x F=16 f32 normal(0,1) in edge order, unsorted int64 "
@@ -263,6 +314,12 @@ def build_workload(name, sr, torch):
     if name == "rle":
         cfg = W.rle_keys()
         return RleWorkload(cfg, copies=4, sr=sr, torch=torch), cfg
+    if name in ("scan", "scan1d"):
+        cfg = W.message() if name == "scan" else W.skew()
+        calls = [("sum", False), ("max", True)] if name == "scan" else [("sum", False), ("min", True)]
+        nbytes = cfg["f32"].nbytes
+        copies = max(1, min(4, -(-4 * MALL_BYTES // nbytes)))
+        return ScanWorkload(cfg, calls, copies, sr, torch), cfg
     if name in ("unique", "flags"):
         cfg = W.rle_keys()
         return RunsWorkload(cfg, name, copies=4, sr=sr, torch=torch), cfg
@@ -289,7 +346,15 @@ def cpu_baseline(wl, name, budget_s):
     t = 0.0
     reps = 0
     results = {}
-    if isinstance(wl, RunsWorkload):
+    if isinstance(wl, ScanWorkload):
+        while reps == 0 or (t < budget_s and reps < 50):
+            t0 = time.perf_counter()
+            for op, ex in wl.ops:
+                results[(op, ex)] = oracle.scan(wl.host_vals, wl.host_off, op, ex, lib=lib)
+            t += time.perf_counter() - t0
+            reps += 1
+        sample = f"full workload ({name}), both scans, {reps} rep(s)"
+    elif isinstance(wl, RunsWorkload):
         fn = oracle.unique if wl.mode == "unique" else oracle.offsets_from_flags
         while reps == 0 or (t < budget_s and reps < 50):
             t0 = time.perf_counter()
@@ -333,6 +398,18 @@ def check_parity(wl, results):
     """GPU outputs of the last step against the oracle (same bars as the tests)."""
     import numpy as np
     verdict = {}
+    if isinstance(wl, ScanWorkload):
+        for (op, ex), ref in results.items():
+            got = wl.outs[(op, ex)].cpu().numpy().reshape(ref.out.shape)
+            lo, hi = int(wl.host_off[0]), int(wl.host_off[-1])
+            if op == "sum":
+                g, r = got[lo:hi].astype(np.float64), ref.ref[lo:hi]
+                ok = bool((np.abs(g - r) <= 2.0 ** -24 * np.abs(r) * 1.0001 + 2.0 ** -30 * ref.mag[lo:hi]
+                           + 1e-30).all())
+            else:
+                ok = bool(np.array_equal(got[lo:hi].view(np.uint32), ref.out[lo:hi].view(np.uint32)))
+            verdict[f"{'excl' if ex else 'incl'}_{op}"] = ok
+        return verdict
     if isinstance(wl, RunsWorkload):
         arr, c = results[wl.mode]
         got, gc = wl.outs[wl.mode]
@@ -508,6 +585,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": dk["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": dk["frac"], "traffic": traffic,
                 "kernel": (dominant if dominant.startswith("rle_")
+                           else f"seg_scan_tails ({dominant})" if dominant.endswith("_tails")
                            else f"{getattr(wl, 'kernel_name', 'seg_reduce_pass1')} ({dominant})"),
                 "algorithmic_bytes_per_launch": dk["bytes"], "avg_launch_us": dk["avg_us"],
                 "timing": "kernel-stamped HIP stop events (hipExtLaunchKernel) on the launch stream, end of "
@@ -529,6 +607,11 @@ def main():
         b, bb = sr.scatter(wl.sets[-1][0], wl.sets[-1][1], wl.dim, "max")
         torch.cuda.synchronize()
         repeat_ok = bool(torch.equal(a.view(torch.int32), b.view(torch.int32)) and torch.equal(aa, bb))
+    if isinstance(wl, ScanWorkload) and len(wl.vals) > 1:
+        a = sr.scan(wl.vals[0], wl.off, "sum").clone()
+        b = sr.scan(wl.vals[-1], wl.off, "sum")
+        torch.cuda.synchronize()
+        repeat_ok = bool(torch.equal(a.view(torch.int32), b.view(torch.int32)))
     if isinstance(wl, ReduceWorkload) and len(wl.vals) > 1:
         op = wl.ops[0]
         a, _ = sr.reduce(wl.vals[0], wl.off, op)

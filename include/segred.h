@@ -266,6 +266,42 @@ int segred_scatter_reduce(const void *values, int32_t dtype, int64_t feat, int64
 int segred_offsets_from_index(const int64_t *index, int64_t rows, int64_t dim_size,
                               int64_t *offsets, hipStream_t stream);
 
+/*
+ * segred_scan -- segmented inclusive or exclusive scan over offset-delimited
+ * segments.
+ *
+ * GPUSegmentedScan is named by the luma.gl "GPURunLengthEncode and
+ * GPUUnique" page ("Composition", beside GPUSegmentedReduction); it is read
+ * with the segmented reduction's contract ("GPUSegmentedReduction" page:
+ * segments, dtypes, operations, empty -> 0): for row r of segment s,
+ *   inclusive (exclusive = 0): out[r] = op of values[offsets[s] .. r]
+ *   exclusive (exclusive != 0): out[r] = op of values[offsets[s] .. r-1],
+ *                               0 at the first row of each segment.
+ *
+ *   values        [rows, feat] row-major, 4-byte elements of type `dtype`.
+ *   dtype         SEGRED_U32, SEGRED_I32 or SEGRED_F32.
+ *   feat          features per row, 1 <= feat <= 2^24 (each scanned on its own).
+ *   offsets       int64 [num_segments + 1], nondecreasing (offsets[0] may be > 0).
+ *   num_segments  S >= 0 (0: nothing is written).
+ *   op            SEGRED_SUM, SEGRED_MIN or SEGRED_MAX.
+ *   out           [rows, feat] in the layout of `values` and of its type; only
+ *                 rows in [offsets[0], offsets[S]) are written.  Integer sums
+ *                 wrap modulo 2^32; float sums accumulate in float64 and each
+ *                 output is its prefix rounded to float32 once (results
+ *                 repeat bit for bit); min/max order as in segred_reduce.
+ *   stream        HIP stream the work is ordered on.
+ *
+ * Errors: SEGRED_ERR_INVALID_ARGUMENT for S < 0, feat < 1, an unknown dtype
+ * or op, NULL values/offsets/out with S > 0, misalignment (4 bytes for values
+ * and out, 8 for offsets).  SEGRED_ERR_UNSUPPORTED for SEGRED_MEAN or feat
+ * above 2^24.  SEGRED_ERR_OUT_OF_MEMORY, SEGRED_ERR_HIP as for segred_reduce.
+ * The offsets are not validated (as for segred_reduce); `out` must not
+ * overlap `values` or `offsets`.
+ */
+int segred_scan(const void *values, int32_t dtype, int64_t feat, const int64_t *offsets,
+                int64_t num_segments, int32_t op, int32_t exclusive, void *out,
+                hipStream_t stream);
+
 /* Static, host-side description of a status code (never NULL). */
 const char *segred_status_string(int status);
 
@@ -291,7 +327,8 @@ int64_t segred_get_shares(int32_t dtype, int32_t op, int64_t feat);
  * kernel the library launches carries a HIP event that the runtime stamps
  * when that kernel ends (hipExtLaunchKernel).  segred_timing_read waits for
  * the recorded events and reports, for every streaming kernel (the first
- * kernel of a segred_reduce call, the atomic kernel of segred_scatter_reduce,
+ * kernel of a segred_reduce call, both kernels of segred_scan, the atomic
+ * kernel of segred_scatter_reduce,
  * the histogram of segred_offsets_from_index, the counting and materialising
  * kernels of segred_offsets_from_rle / segred_unique /
  * segred_offsets_from_flags), the time from the end of the launch recorded

@@ -10,6 +10,7 @@ There is no CPU fallback: if the library is missing, calls raise.
     values, lengths, offsets, count = offsets_from_rle(sorted_keys)
     out, arg = scatter(values, index, dim_size, "max")  # unsorted int64 index [N]
     offsets = offsets_from_index(sorted_index, dim_size)
+    prefix = scan(values, offsets, "sum", exclusive=False)  # segmented scan
     values, count = unique(keys)                       # distinct adjacent values
     offsets, count = offsets_from_flags(start_flags)   # uint32 flags, nonzero = start
 """
@@ -64,6 +65,8 @@ def library(path: str | None = None):
             lib.segred_scatter_reduce.restype = ctypes.c_int
             lib.segred_offsets_from_index.argtypes = [vp, i64, i64, vp, vp]
             lib.segred_offsets_from_index.restype = ctypes.c_int
+            lib.segred_scan.argtypes = [vp, i32, i64, vp, i64, i32, i32, vp, vp]
+            lib.segred_scan.restype = ctypes.c_int
             lib.segred_unique.argtypes = [vp, i64, vp, vp, vp]
             lib.segred_unique.restype = ctypes.c_int
             lib.segred_offsets_from_flags.argtypes = [vp, i64, vp, vp, vp]
@@ -255,6 +258,41 @@ def offsets_from_index(index: torch.Tensor, dim_size: int) -> torch.Tensor:
                                                  offsets.data_ptr(), _stream(index.device))
     _check(rc, "segred_offsets_from_index")
     return offsets
+
+
+def scan(values: torch.Tensor, offsets: torch.Tensor, op: str, *, exclusive: bool = False,
+         out: torch.Tensor | None = None) -> torch.Tensor:
+    """Segmented inclusive / exclusive ``op`` ("sum", "min", "max") scan of
+    ``values`` over ``offsets`` (segred_scan).
+
+    Returns ``out`` with the shape and dtype of ``values``; rows outside
+    [offsets[0], offsets[-1]) are left as they were in ``out`` (uninitialised
+    when ``out`` is not given)."""
+    if op not in ("sum", "min", "max"):
+        raise ValueError("op must be one of ['max', 'min', 'sum']")
+    if not (values.is_cuda and offsets.is_cuda) or values.device != offsets.device:
+        raise ValueError("values and offsets must be tensors on the same GPU")
+    if values.dtype not in DTYPES:
+        raise TypeError(f"values dtype {values.dtype} is not uint32, int32 or float32")
+    if offsets.dtype != torch.int64 or offsets.dim() != 1 or offsets.numel() < 1:
+        raise ValueError("offsets must be a 1-D int64 tensor with S + 1 entries")
+    if values.dim() == 0 or not values.is_contiguous() or not offsets.is_contiguous():
+        raise ValueError("values and offsets must be contiguous; values needs a row dimension")
+    feat = 1
+    for d in values.shape[1:]:
+        feat *= d
+    if feat < 1:
+        raise ValueError("values has an empty feature dimension")
+    if out is None:
+        out = torch.empty_like(values)
+    elif out.shape != values.shape or out.dtype != values.dtype or not out.is_contiguous():
+        raise ValueError("out must be contiguous with the shape and dtype of values")
+    s = offsets.numel() - 1
+    with torch.cuda.device(values.device):
+        rc = library().segred_scan(values.data_ptr(), DTYPES[values.dtype], feat, offsets.data_ptr(), s, OPS[op],
+                                   int(bool(exclusive)), out.data_ptr(), _stream(values.device))
+    _check(rc, "segred_scan")
+    return out
 
 
 def unique(keys: torch.Tensor):

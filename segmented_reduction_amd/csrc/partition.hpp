@@ -1,0 +1,216 @@
+// partition.hpp -- merge-path partition of (rows + segment ends) into equal
+// shares, one per wave, found by a workgroup-cooperative search over the
+// offsets.  Shared by the segmented reduction and the segmented scan.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "wave.hpp"
+
+namespace segred {
+
+// Item d is preceded by i(d) = max{ i in [0, S] : key(i) <= d } segment ends,
+// key(i) = offsets[i] - o0 + i (strictly increasing in i).  The four waves
+// of a workgroup own four consecutive shares, so their five boundary
+// diagonals lie close together and the workgroup searches for them jointly:
+//   round A: 1024 evenly spaced offsets (the same for every workgroup, so
+//            they stay cached), which also give o0 and the item count T;
+//   round B: 64 evenly spaced offsets over the range round A leaves for the
+//            workgroup's first and last diagonal;
+//   round C: each wave narrows its own two diagonals with 256-way rounds over
+//            consecutive offsets (one round unless the workgroup's range is
+//            wider than 16K ends).
+// The workgroup-specific loads touch about 64 + 8 * 3 cache lines of the
+// offsets, most of which its waves read again for their segment ends.
+// Every probe is clamped into the array and loaded unconditionally (a load
+// under a branch would be waited for inside the branch).  The key of the
+// last probe at or below a diagonal is kept, which gives offsets[i(d)]
+// without another load.
+
+// A wave's share of the merged (rows + segment ends) sequence: items
+// [d0, d1), i.e. segment ends [i0, i1) and rows [j0, j1) (rows relative to
+// offsets[0]).
+struct Share {
+    int64_t o0, D, d0, d1, i0, j0, i1, j1;
+    int64_t first_row; // first row of segment i0 (relative to offsets[0])
+    int64_t tail_row;  // first row of segment i1 (relative to offsets[0])
+    bool split_head;   // segment i0 ends in the share but began in an earlier one
+    bool has_tail;     // segment i1 has rows in the share and continues past it
+};
+
+// Where d falls among N probes p_k = lo + k * step (k < N - 1) and
+// p_{N-1} = hi whose raw offsets are in s[]: the last probe with key <= d
+// (there is one) and its key; i(d) then lies in [lo', hi'].
+struct Bracket {
+    int64_t lo, hi, klo;
+};
+template <int N>
+__device__ __forceinline__ int64_t probe_pos(int k, int64_t lo, int64_t step, int64_t hi) {
+    return k == N - 1 ? hi : min(lo + (int64_t)k * step, hi);
+}
+template <int N>
+__device__ __forceinline__ Bracket bracket(const int64_t *s, int64_t lo, int64_t step, int64_t hi, int64_t o0,
+                                           int64_t d, int lane) {
+    constexpr int U = N / 64;
+    int cnt = 0;
+    int64_t kk[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int k = u * 64 + lane;
+        kk[u] = s[k] - o0 + probe_pos<N>(k, lo, step, hi);
+        cnt += popc64(ballot(kk[u] <= d));
+    }
+    // cnt >= 1: probe 0 has key <= d
+    const int last = cnt - 1, ul = last >> 6;
+    int64_t klast = kk[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u) klast = ul == u ? kk[u] : klast;
+    Bracket b;
+    b.klo = (int64_t)__builtin_amdgcn_readlane((uint32_t)klast, last & 63) |
+            ((int64_t)__builtin_amdgcn_readlane((uint32_t)((uint64_t)klast >> 32), last & 63) << 32);
+    b.lo = probe_pos<N>(last, lo, step, hi);
+    b.hi = cnt >= N ? hi : probe_pos<N>(cnt, lo, step, hi) - 1;
+    if (b.hi < b.lo) b.hi = b.lo;
+    return b;
+}
+
+constexpr int kProbesA = 1024, kProbesB = 64;
+
+//
+// `wave` is the share index (4 * share block + wave in the workgroup); every
+// wave of the workgroup must call this together (it synchronises).
+//
+// SNAP moves each share boundary d onto the nearer edge of the block of the
+// segment it falls in (block i = segment i's rows and its end item, items
+// [key(i), key(i+1))) when that edge is at most D / 4 items away, so short
+// segments are rarely cut; it is a function of d alone, so the two shares
+// on either side of a boundary agree on it, and it keeps the boundaries in
+// order.
+template <bool SNAP = false>
+__device__ __forceinline__ Share find_share(const int64_t *off, int64_t S, int64_t NW, int64_t wave, int lane,
+                                            int64_t *s_probe /* LDS [kProbesA], workgroup-wide */,
+                                            int64_t min_share = 1) {
+    const int tid = threadIdx.x;
+    const int wid = tid >> 6;
+    const int64_t blk = wave >> 2;  // the workgroup's four shares are 4 * blk .. 4 * blk + 3
+
+    // Round A (4 probes per thread).
+    const int64_t stepA = (S + kProbesA - 2) / (kProbesA - 1);
+#pragma unroll
+    for (int u = 0; u < kProbesA / 256; ++u) {
+        const int k = u * 256 + tid;
+        s_probe[k] = off[probe_pos<kProbesA>(k, 0, stepA, S)];
+    }
+    __syncthreads();
+    const int64_t o0 = s_probe[0];
+    const int64_t T = (s_probe[kProbesA - 1] - o0) + S;
+    // Shares of at least min_share items: small inputs use fewer waves (the
+    // rest get empty shares and only write their header).
+    const int64_t D = max((T + NW - 1) / NW, min_share);
+    const int64_t g0 = min(blk * 4 * D, T), g4 = min((blk * 4 + 4) * D, T);
+    const int64_t d0 = min((blk * 4 + wid) * D, T), d1 = min(d0 + D, T);
+    const Bracket a0 = bracket<kProbesA>(s_probe, 0, stepA, S, o0, g0, lane);
+    const Bracket a4 = bracket<kProbesA>(s_probe, 0, stepA, S, o0, g4, lane);
+    __syncthreads();  // every wave is done with round A
+
+    // Round B over [L, H], which holds i(d) for every diagonal of the group.
+    const int64_t L = a0.lo, H = a4.hi;
+    const int64_t stepB = max((H - L + kProbesB - 2) / (kProbesB - 1), (int64_t)1);
+    if (tid < kProbesB) s_probe[tid] = off[probe_pos<kProbesB>(tid, L, stepB, H)];
+    __syncthreads();
+    Bracket b0 = bracket<kProbesB>(s_probe, L, stepB, H, o0, d0, lane);
+    Bracket b1 = bracket<kProbesB>(s_probe, L, stepB, H, o0, d1, lane);
+    __syncthreads();  // the probe array is free from here on
+
+    // Round C: 256-way rounds on both diagonals of this wave.
+    int64_t lo0 = b0.lo, hi0 = b0.hi, k0lo = b0.klo;
+    int64_t lo1 = b1.lo, hi1 = b1.hi, k1lo = b1.klo;
+    while (lo0 < hi0 || lo1 < hi1) {
+        const int64_t st0 = (hi0 - lo0 + 255) >> 8, st1 = (hi1 - lo1 + 255) >> 8;
+        int64_t k0[4], k1[4];
+        bool ok0[4], ok1[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t j = (int64_t)(u * 64 + lane + 1);
+            const int64_t p0 = lo0 + j * st0, p1 = lo1 + j * st1;
+            ok0[u] = lo0 < hi0 && p0 <= hi0;
+            ok1[u] = lo1 < hi1 && p1 <= hi1;
+            const int64_t q0 = min(p0, S), q1 = min(p1, S);
+            k0[u] = off[q0] - o0 + q0;
+            k1[u] = off[q1] - o0 + q1;
+        }
+        int n0 = 0, n1 = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            n0 += popc64(ballot(ok0[u] && k0[u] <= d0));
+            n1 += popc64(ballot(ok1[u] && k1[u] <= d1));
+        }
+        // key of probe n (1-based), held by lane (n - 1) % 64 in slot (n - 1) / 64
+        auto key_of = [&](int64_t v0, int64_t v1, int64_t v2, int64_t v3, int n)
+            __attribute__((always_inline)) -> int64_t {
+            const int m = n - 1, u = m >> 6;
+            const int64_t v = u == 0 ? v0 : u == 1 ? v1 : u == 2 ? v2 : v3;
+            return (int64_t)__builtin_amdgcn_readlane((uint32_t)v, m & 63) |
+                   ((int64_t)__builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), m & 63) << 32);
+        };
+        if (lo0 < hi0) {
+            if (n0 > 0) k0lo = key_of(k0[0], k0[1], k0[2], k0[3], n0);
+            hi0 = min(hi0, lo0 + (int64_t)(n0 + 1) * st0 - 1);
+            lo0 += (int64_t)n0 * st0;
+        }
+        if (lo1 < hi1) {
+            if (n1 > 0) k1lo = key_of(k1[0], k1[1], k1[2], k1[3], n1);
+            hi1 = min(hi1, lo1 + (int64_t)(n1 + 1) * st1 - 1);
+            lo1 += (int64_t)n1 * st1;
+        }
+    }
+    int64_t e0 = d0, e1 = d1;
+    if constexpr (SNAP) {
+        // key(i + 1) of each boundary's block (block S, the end of the
+        // sequence, is never moved)
+        const int64_t n0 = off[min(lo0 + 1, S)] - o0 + lo0 + 1;
+        const int64_t n1 = off[min(lo1 + 1, S)] - o0 + lo1 + 1;
+        const int64_t slack = D >> 2;
+        auto snap = [&](int64_t d, int64_t i, int64_t klo, int64_t knext, int64_t &e, int64_t &ii, int64_t &kk)
+            __attribute__((always_inline)) {
+            e = d;
+            ii = i;
+            kk = klo;
+            if (i >= S) return;
+            if (d - klo <= slack && d - klo <= knext - d) {
+                e = klo;
+            } else if (knext - d <= slack) {
+                e = knext;
+                ii = i + 1;
+                kk = knext;
+            }
+        };
+        int64_t ii0, kk0, ii1, kk1;
+        snap(d0, lo0, k0lo, n0, e0, ii0, kk0);
+        snap(d1, lo1, k1lo, n1, e1, ii1, kk1);
+        lo0 = ii0;
+        k0lo = kk0;
+        lo1 = ii1;
+        k1lo = kk1;
+    }
+    // Everything here is the same in every lane; saying so lets the compiler
+    // keep it in scalar registers (and build uniform buffer descriptors).
+    Share sh;
+    sh.o0 = readfirst(o0);
+    sh.D = readfirst(D);
+    sh.d0 = readfirst(e0);
+    sh.d1 = readfirst(e1);
+    sh.i0 = readfirst(lo0);
+    sh.j0 = sh.d0 - sh.i0;
+    sh.i1 = readfirst(lo1);
+    sh.j1 = sh.d1 - sh.i1;
+    sh.first_row = readfirst(k0lo) - sh.i0;  // offsets[i0] - o0
+    sh.split_head = sh.i0 < sh.i1 && sh.first_row < sh.j0;
+    sh.tail_row = readfirst(k1lo) - sh.i1;  // offsets[i1] - o0
+    sh.has_tail = sh.i1 < S && sh.tail_row < sh.j1;
+    return sh;
+}
+
+}  // namespace segred

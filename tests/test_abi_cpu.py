@@ -28,7 +28,7 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for required in ("segred_reduce", "segred_offsets_from_rle", "segred_status_string", "segred_scatter_reduce",
-                     "segred_offsets_from_index", "segred_unique", "segred_offsets_from_flags"):
+                     "segred_offsets_from_index", "segred_unique", "segred_offsets_from_flags", "segred_scan"):
         assert required in names
 
 
@@ -169,6 +169,27 @@ def test_offsets_from_index_argument_checks(args, expect):
 def test_unique_and_flags_argument_checks(fn, args, expect):
     lib = _lib()
     assert getattr(lib, fn)(*args, None) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    # (values, dtype, feat, offsets, S, op, exclusive, out) -> status
+    ((FAKE, 2, 1, FAKE, -1, 0, 0, FAKE), 1),           # S < 0
+    ((FAKE, 2, 0, FAKE, 4, 0, 0, FAKE), 1),            # feat < 1
+    ((FAKE, 3, 1, FAKE, 4, 0, 0, FAKE), 1),            # dtype out of range
+    ((FAKE, 2, 1, FAKE, 4, 4, 0, FAKE), 1),            # op out of range
+    ((FAKE, 2, 1, FAKE, 4, 3, 0, FAKE), 2),            # MEAN has no scan
+    ((FAKE, 2, 2 ** 24 + 1, FAKE, 4, 0, 0, FAKE), 2),  # too many features
+    ((None, 2, 1, FAKE, 4, 0, 0, FAKE), 1),
+    ((FAKE, 2, 1, None, 4, 0, 1, FAKE), 1),
+    ((FAKE, 2, 1, FAKE, 4, 0, 1, None), 1),
+    ((FAKE + 2, 2, 1, FAKE, 4, 1, 0, FAKE), 1),
+    ((FAKE, 2, 1, FAKE + 4, 4, 1, 0, FAKE), 1),
+    ((FAKE, 2, 1, FAKE, 4, 2, 0, FAKE + 2), 1),
+    ((None, 2, 1, None, 0, 0, 0, None), 0),            # S == 0 enqueues nothing
+])
+def test_scan_argument_checks(args, expect):
+    lib = _lib()
+    assert lib.segred_scan(*args, None) == expect
 
 
 def test_share_knob_range():
