@@ -63,6 +63,8 @@ def _bind(lib):
     lib.oracle_offsets_from_index.restype = ctypes.c_int
     lib.oracle_scan.argtypes = [vp, i32, i64, vp, i64, i32, i32, vp, vp, vp]
     lib.oracle_scan.restype = ctypes.c_int
+    lib.oracle_lower_bounds.argtypes = [vp, i32, i64, i64, vp, i64, vp, i64, vp, i64, i64, i64, vp, vp, i32]
+    lib.oracle_lower_bounds.restype = ctypes.c_int
     lib.oracle_unique.argtypes = [vp, i64, vp, vp]
     lib.oracle_unique.restype = ctypes.c_int
     lib.oracle_offsets_from_flags.argtypes = [vp, i64, vp, vp]
@@ -159,6 +161,36 @@ def scan(values: np.ndarray, offsets: np.ndarray, op: str, exclusive: bool = Fal
     if rc != 0:
         raise ValueError(f"oracle_scan rejected dtype={dt} op={op} feat={feat} (rc={rc})")
     return Scanned(out, ref, mag)
+
+
+def lower_bounds(values: np.ndarray, queries: np.ndarray, segments: np.ndarray, *, stride: int = 1,
+                 order: np.ndarray | None = None, max_qc: int | None = None, tile: int = 32,
+                 out: np.ndarray | None = None, validation: int = 0, preserve: bool = False,
+                 value_count: int | None = None, lib=None):
+    """Lower bounds of ``queries`` over segmented sorted ``values`` (uint32 or
+    float32, same dtype); ``segments`` int64 [S, 4] of (vo, vc, qo, qc).
+    Returns (out int64 [len(queries)], validation word)."""
+    lib = lib or load()
+    values = np.ascontiguousarray(values)
+    queries = np.ascontiguousarray(queries, dtype=values.dtype)
+    segments = np.ascontiguousarray(segments, dtype=np.int64).reshape(-1, 4)
+    dt = dtype_name(values)
+    if out is None:
+        out = np.full(queries.shape[0], -7, dtype=np.int64)
+    out = np.ascontiguousarray(out, dtype=np.int64)
+    word = np.array([validation], dtype=np.uint32)
+    if order is not None:
+        order = np.ascontiguousarray(order, dtype=np.uint32)
+    if max_qc is None:
+        max_qc = int(segments[:, 3].max()) if segments.shape[0] else 0
+    if value_count is None:
+        value_count = (values.shape[0] + stride - 1) // stride
+    rc = lib.oracle_lower_bounds(_ptr(values), DTYPES[dt], int(value_count), stride, _ptr(order), 0 if order is None else order.shape[0], _ptr(queries),
+                                 queries.shape[0], _ptr(segments), segments.shape[0], int(max_qc), int(tile),
+                                 _ptr(out), _ptr(word), int(bool(preserve)))
+    if rc != 0:
+        raise ValueError(f"oracle_lower_bounds rejected its arguments (rc={rc})")
+    return out, int(word[0])
 
 
 def unique(keys: np.ndarray, lib=None):

@@ -34,6 +34,8 @@
  *     materialises offsets from segment-start flags.
  *   - luma.gl RLE page, "Composition": GPUSegmentedScan beside the
  *     segmented reduction (read as the per-row prefix of the same operation).
+ *   - luma.gl "GPUGallopingSearch": lower bounds of queries over segmented
+ *     sorted values, with its validation word.
  *   - phanerozoic/graph-reduce README, "API" and "Method": the scatter path
  *     reduces every row into the output its index names (the index need not
  *     be sorted), with the same sum / mean / min / max (+ row) semantics;
@@ -54,6 +56,7 @@
  *   - scatter: rows whose index lies outside [0, dim_size) take no part; an
  *     output no row names is empty (0, arg -1, mean 0).
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -298,6 +301,77 @@ int oracle_scan(const void *values, int32_t dtype, int64_t feat, const int64_t *
             }
         }
     }
+    return 0;
+}
+
+/*
+ * oracle_lower_bounds: many lower-bound queries over segmented sorted values
+ * (luma.gl "GPUGallopingSearch": "Overview", "Usage", "Validation").
+ *
+ * The value at search position p is values[p * stride], or, with an order
+ * vector, values[order[p] * stride].  Segment record s is (vo, vc, qo, qc):
+ * value positions [vo, vo + vc) and query positions [qo, qo + qc).  For
+ * query k of the segment, out[qo + k] = the first position p in
+ * [vo, vo + vc) whose value is not less than the query, or vo + vc if
+ * there is none (absolute, in the value / order view).  Comparisons are
+ * unsigned for uint32 and IEEE for float32.  The validation word:
+ *   1  a value range leaves the value view (its segment is not searched),
+ *   2  a query range leaves the query view or exceeds the per-segment
+ *      capacity max_qc (its segment is not searched),
+ *   4  a query is below the one before it in the same tile of T queries
+ *      (its lower bound is still exact),
+ *   8  a float32 query is not finite: that query and the rest of its tile
+ *      are not written.
+ * Without `preserve` the word starts from 0.  Outputs that are not written
+ * keep their contents.
+ */
+int oracle_lower_bounds(const void *values, int32_t dtype, int64_t value_count, int64_t stride,
+                        const uint32_t *order, int64_t order_count, const void *queries, int64_t query_count,
+                        const int64_t *segments, int64_t num_segments, int64_t max_qc, int64_t T,
+                        int64_t *out, uint32_t *validation, int32_t preserve)
+{
+    if ((dtype != ORC_U32 && dtype != ORC_F32) || value_count < 0 || stride < 1 || query_count < 0 ||
+        num_segments < 0 || max_qc < 0 || T < 1 || (order && order_count < 0))
+        return -1;
+    uint32_t word = preserve ? *validation : 0u;
+    const int64_t view = order ? order_count : value_count;
+    for (int64_t s = 0; s < num_segments; ++s) {
+        const int64_t vo = segments[4 * s + 0], vc = segments[4 * s + 1];
+        const int64_t qo = segments[4 * s + 2], qc = segments[4 * s + 3];
+        const int bad_values = vo < 0 || vc < 0 || vo > view || vc > view - vo;
+        const int bad_queries = qo < 0 || qc < 0 || qo > query_count || qc > query_count - qo || qc > max_qc;
+        if (bad_values)
+            word |= 1u;
+        if (bad_queries)
+            word |= 2u;
+        if (bad_values || bad_queries)
+            continue;
+        for (int64_t k = 0; k < qc; ++k) {
+            const uint32_t qb = load_bits(queries, qo + k);
+            if (dtype == ORC_F32 && !isfinite(bits_to_float(qb))) {
+                word |= 8u;
+                k = (k / T + 1) * T - 1; /* the rest of this tile is skipped */
+                continue;
+            }
+            if (k % T != 0) {
+                const uint32_t pb = load_bits(queries, qo + k - 1);
+                const int lower = dtype == ORC_F32 ? (bits_to_float(qb) < bits_to_float(pb)) : (qb < pb);
+                if (lower)
+                    word |= 4u;
+            }
+            int64_t p = vo;
+            while (p < vo + vc) {
+                const int64_t row = order ? (int64_t)order[p] : p;
+                const uint32_t vb = load_bits(values, row * stride);
+                const int less = dtype == ORC_F32 ? (bits_to_float(vb) < bits_to_float(qb)) : (vb < qb);
+                if (!less)
+                    break;
+                ++p;
+            }
+            out[qo + k] = p;
+        }
+    }
+    *validation = word;
     return 0;
 }
 

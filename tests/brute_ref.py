@@ -169,3 +169,11 @@ def scan(rows, offsets, op, kind, feat, exclusive):
                     outs.append((min(col) if op == "min" else max(col)) if col else 0)
             res[r] = (outs, exact if kind == "f32" and op == "sum" else None)
     return res
+
+
+def lower_bound(seq, q):
+    """First index whose element is not less than q (len(seq) if none), by scanning."""
+    for i, v in enumerate(seq):
+        if not v < q:
+            return i
+    return len(seq)

@@ -578,7 +578,117 @@ def pin_scan_library(lib, seed=31):
                 assert np.array_equal(inc.out[hi - 1].view(np.uint32), red.out[s].view(np.uint32)), (kind, op, s)
 
 
+# ---------------------------------------------------------------- lower-bound search
+
+def _lb_case(rng, kind, segs, vmax, qmax, order=False, stride=1):
+    """Sorted value segments (optionally reached through a permutation order
+    vector and a stride) and sorted queries per segment."""
+    vcs = rng.integers(0, vmax + 1, segs)
+    qcs = rng.integers(0, qmax + 1, segs)
+    vo = (np.cumsum(vcs) - vcs).astype(np.int64)
+    qo = (np.cumsum(qcs) - qcs).astype(np.int64)
+    nv, nq = int(vcs.sum()), int(qcs.sum())
+    if kind == "f32":
+        pool = rng.standard_normal(nv).astype(np.float32)
+        pool[rng.random(nv) < 0.3] = np.float32(0.5)  # duplicates
+        qs = rng.standard_normal(nq).astype(np.float32) * np.float32(1.3)
+        qs[rng.random(nq) < 0.2] = np.float32(0.5)
+    else:
+        pool = rng.integers(0, 50, nv).astype(np.uint32)
+        pool[rng.random(nv) < 0.1] = np.uint32(0xFFFFFFF0)
+        qs = rng.integers(0, 52, nq).astype(np.uint32)
+        qs[rng.random(nq) < 0.05] = np.uint32(0xFFFFFFFF)
+    for s in range(segs):
+        pool[vo[s]:vo[s] + vcs[s]].sort()
+        qs[qo[s]:qo[s] + qcs[s]].sort()
+    seg = np.stack([vo, vcs, qo, qcs], axis=1).astype(np.int64)
+    ordv = None
+    stored = pool
+    if order:
+        perm = rng.permutation(nv).astype(np.uint32)  # stored row of search position p
+        stored = np.empty_like(pool)
+        stored[perm] = pool
+        ordv = perm
+    if stride > 1:
+        wide = np.zeros(nv * stride, dtype=pool.dtype)
+        wide[::stride] = stored
+        stored = wide
+    return stored, qs, seg, ordv, pool
+
+
+def pin_lower_bounds_library(lib, seed=37):
+    """Every answer equals numpy.searchsorted(side='left') on its segment and
+    bisect.bisect_left, directly, through an order vector, and strided."""
+    import bisect
+    rng = np.random.default_rng(seed)
+    for trial in range(60):
+        kind = ("u32", "f32")[trial % 2]
+        order, stride = bool(trial % 3 == 1), (1, 1, 3)[trial % 3]
+        stored, qs, seg, ordv, pool = _lb_case(rng, kind, int(rng.integers(1, 12)), 60, 70, order, stride)
+        out, word = oracle.lower_bounds(stored, qs, seg, stride=stride, order=ordv,
+                                        value_count=pool.shape[0] if stride > 1 else None, lib=lib)
+        assert word == 0, trial
+        for vo, vc, qo, qc in seg.tolist():
+            v = pool[vo:vo + vc]
+            want = vo + np.searchsorted(v, qs[qo:qo + qc], side="left")
+            assert np.array_equal(out[qo:qo + qc], want), (trial, kind, order, stride)
+            vl = v.tolist()
+            for k in range(qc):
+                assert out[qo + k] == vo + bisect.bisect_left(vl, qs[qo + k].item())
+
+
+def pin_lower_bounds_brute(lib, seed=41):
+    """Tiny cases against the scan-from-the-left definition (brute_ref)."""
+    rng = np.random.default_rng(seed)
+    for trial in range(150):
+        kind = ("u32", "f32")[trial % 2]
+        stored, qs, seg, _, pool = _lb_case(rng, kind, int(rng.integers(0, 5)), 9, 9)
+        out, word = oracle.lower_bounds(stored, qs, seg, tile=int(rng.integers(1, 5)), lib=lib)
+        for vo, vc, qo, qc in seg.tolist():
+            for k in range(qc):
+                assert out[qo + k] == vo + brute_ref.lower_bound(pool[vo:vo + vc].tolist(), qs[qo + k].item())
+
+
+def pin_lower_bounds_validation(lib):
+    """The validation word of the galloping-search page ('Validation'), bit by
+    bit, on constructed inputs."""
+    v = np.arange(10, dtype=np.float32)
+    q = np.array([2.5, 1.0, 7.0, 3.0, np.nan, 4.0, 5.0, 8.0, 9.5, np.inf], dtype=np.float32)
+    # bit 4: a query below its predecessor inside a tile; the answer stays exact
+    out, w = oracle.lower_bounds(v, q[:4], np.array([[0, 10, 0, 4]]), tile=4, lib=lib)
+    assert w == 4 and out.tolist() == [3, 1, 7, 3]
+    # ... but not across a tile boundary (tiles of 1 and of 2 here)
+    out, w = oracle.lower_bounds(v, q[:2], np.array([[0, 10, 0, 2]]), tile=1, lib=lib)
+    assert w == 0 and out.tolist() == [3, 1]
+    out, w = oracle.lower_bounds(v, q[1:3], np.array([[0, 10, 0, 2]]), tile=1, lib=lib)
+    assert w == 0
+    # bit 8: a non-finite query stops the rest of its tile; the next tile runs
+    out, w = oracle.lower_bounds(v, q[3:10], np.array([[0, 10, 0, 7]]), tile=3, lib=lib)
+    assert w == 8 and out.tolist() == [3, -7, -7, 5, 8, 10, -7]
+    # bit 1: value range outside the view; bit 2: query range outside, or above capacity
+    out, w = oracle.lower_bounds(v, q[:3], np.array([[5, 6, 0, 3]]), lib=lib)
+    assert w == 1 and (out == -7).all()
+    out, w = oracle.lower_bounds(v, q[:3], np.array([[0, 10, 1, 3]]), lib=lib)
+    assert w == 2 and (out == -7).all()
+    out, w = oracle.lower_bounds(v, q[:3], np.array([[0, 10, 0, 3]]), max_qc=2, lib=lib)
+    assert w == 2 and (out == -7).all()
+    out, w = oracle.lower_bounds(v, q[:3], np.array([[-1, 2, 0, 3], [0, 10, 0, 1]]), lib=lib)
+    assert w == 1 and out.tolist() == [3, -7, -7]
+    # empty segments are valid; preserve ORs into the old word
+    out, w = oracle.lower_bounds(v, q[:1], np.array([[4, 0, 0, 1], [0, 0, 1, 0]]), validation=16, lib=lib)
+    assert w == 0 and out.tolist() == [4]
+    out, w = oracle.lower_bounds(v, q[:2], np.array([[0, 10, 0, 2]]), tile=2, validation=16, preserve=True, lib=lib)
+    assert w == 20
+    # uint32 compares unsigned
+    vu = np.array([1, 5, 0x80000000, 0xFFFFFFFF], dtype=np.uint32)
+    out, w = oracle.lower_bounds(vu, np.array([0x7FFFFFFF, 0xFFFFFFFF], np.uint32), np.array([[0, 4, 0, 2]]), lib=lib)
+    assert w == 0 and out.tolist() == [2, 3]
+
+
 ALL_PINS = [
+    pin_lower_bounds_library,
+    pin_lower_bounds_brute,
+    pin_lower_bounds_validation,
     pin_scan_against_printed_reduction,
     pin_scan_brute,
     pin_scan_library,

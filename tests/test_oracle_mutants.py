@@ -69,6 +69,15 @@ MUTANTS = [
     ("scan_feature_stride_dropped", "const int64_t o = r * feat + f;\n                const uint32_t b",
      "const int64_t o = r + f;\n                const uint32_t b"),
     ("scan_int_sum_overwrites", "run_int += b;", "run_int = b;"),
+    ("lb_upper_bound", "(bits_to_float(vb) < bits_to_float(qb)) : (vb < qb)",
+     "(bits_to_float(vb) <= bits_to_float(qb)) : (vb <= qb)"),
+    ("lb_signed_compare", ": (vb < qb);", ": ((int32_t)vb < (int32_t)qb);"),
+    ("lb_relative_position", "out[qo + k] = p;", "out[qo + k] = p - vo;"),
+    ("lb_order_ignored", "const int64_t row = order ? (int64_t)order[p] : p;", "const int64_t row = p;"),
+    ("lb_stride_ignored", "load_bits(values, row * stride);", "load_bits(values, row);"),
+    ("lb_decrease_across_tiles", "if (k % T != 0) {", "if (k != 0) {"),
+    ("lb_no_tile_stop", "k = (k / T + 1) * T - 1; /* the rest of this tile is skipped */", "/* no stop */"),
+    ("lb_capacity_ignored", " || qc > max_qc;", ";"),
     ("rle_length_off_by_one", "(uint32_t)(offsets[r + 1] - offsets[r])", "(uint32_t)(offsets[r + 1] - offsets[r] - 1)"),
 ]
 
