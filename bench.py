@@ -38,7 +38,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["segmented_reduction_amd/csrc/reduce.hip", "segmented_reduction_amd/csrc/wave.hpp",
                   "segmented_reduction_amd/csrc/rle.hip", "segmented_reduction_amd/csrc/keys.hpp",
                   "segmented_reduction_amd/csrc/scan.hpp", "segmented_reduction_amd/csrc/scatter.hip",
-                  "segmented_reduction_amd/csrc/partition.hpp", "segmented_reduction_amd/csrc/segscan.hip"]
+                  "segmented_reduction_amd/csrc/partition.hpp", "segmented_reduction_amd/csrc/segscan.hip",
+                  "segmented_reduction_amd/csrc/galloping.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -241,6 +242,44 @@ class ScanWorkload(Workload):
         return self.rows * self.feat * len(self.ops)
 
 
+class SearchWorkload(Workload):
+    """Lower-bound queries over segmented sorted float32 values, one search
+    call per step (galloping search with the page's defaults)."""
+
+    kernel_name = "gallop_kernel"
+
+    def __init__(self, cfg, copies, sr, torch):
+        self.sr, self.torch, self.cfg = sr, torch, cfg
+        v = torch.from_numpy(cfg["values"]).cuda()
+        q = torch.from_numpy(cfg["queries"]).cuda()
+        sg = torch.from_numpy(cfg["segments"]).cuda()
+        self.sets = [(v, q)] + [(v.clone(), q.clone()) for _ in range(copies - 1)]
+        self.seg = sg
+        self.nq, self.S = int(q.numel()), int(sg.shape[0])
+        self.out = torch.empty(self.nq, dtype=torch.int64, device=v.device)
+        self.val = torch.zeros(1, dtype=torch.int32, device=v.device).view(torch.uint32)
+        self.calls = [("search", None)]
+        self.kernels_per_step = 2  # clear the validation word, search
+        self.outs = {}
+
+    def step(self, i):
+        v, q = self.sets[i % len(self.sets)]
+        self.outs["search"] = self.sr.galloping_search(
+            v, q, self.seg, max_query_count=self.cfg["max_query_count"],
+            queries_per_tile=self.cfg["queries_per_tile"], out=self.out, validation=self.val)
+
+    def call_bytes(self, label):
+        """Each query read and its answer written once, plus the records and
+        the validation word; the value probes come on top (mostly cache hits)."""
+        return self.nq * (4 + 8) + self.S * 32 + 4
+
+    def bytes_per_step(self):
+        return self.call_bytes("search")
+
+    def elems_per_step(self):
+        return self.nq
+
+
 class RunsWorkload(Workload):
     """The RLE's relatives on the same 16M Zipf keys: the distinct adjacent
     values (unique) or the offsets of the run-start flags (flags)."""
@@ -302,6 +341,9 @@ DESCRIPTIONS = {
             "normal(0,1), 10,000 segments (multinomial, mean 100); inclusive sum and exclusive max per row",
     "scan1d": "segmented scan over the heavy-skew input: 50M f32 uniform[0,1) in 1M segments (Pareto 1.5, one "
               "5M-row segment, 10% empty); inclusive sum and exclusive min per element",
+    "search": "lower-bound (galloping) search: 8,192 segments of sorted f32 time stamps (0..4,096 each, "
+              "16.7M values) and sorted queries (0..2,049 each, 8.4M), maximumQueryCount 2049, 32 queries per "
+              "tile; Gelem/s counts queries",
     "scatter": "scatter path: 1,000,000 rows x F=64 f32 normal(0,1) in edge order, unsorted int64 destination "
                "index uniform over 10,000 outputs; atomic scatter sum and scatter max+argmax",
     "scatter16": "scatter path: 1,000,000 rows x F=16 f32 normal(0,1) in edge order, unsorted int64 "
@@ -314,6 +356,9 @@ def build_workload(name, sr, torch):
     if name == "rle":
         cfg = W.rle_keys()
         return RleWorkload(cfg, copies=4, sr=sr, torch=torch), cfg
+    if name == "search":
+        cfg = W.search()
+        return SearchWorkload(cfg, copies=2, sr=sr, torch=torch), cfg
     if name in ("scan", "scan1d"):
         cfg = W.message() if name == "scan" else W.skew()
         calls = [("sum", False), ("max", True)] if name == "scan" else [("sum", False), ("min", True)]
@@ -346,6 +391,31 @@ def cpu_baseline(wl, name, budget_s):
     t = 0.0
     reps = 0
     results = {}
+    if isinstance(wl, SearchWorkload):
+        cfg = wl.cfg
+        seg = cfg["segments"]
+        done_q = 0
+        s = 0
+        while s < seg.shape[0] and (s == 0 or t < budget_s):
+            e = min(s + 128, seg.shape[0])
+            a0, b0 = int(seg[s, 0]), int(seg[s, 2])
+            a1, b1 = int(seg[e - 1, 0] + seg[e - 1, 1]), int(seg[e - 1, 2] + seg[e - 1, 3])
+            sub = seg[s:e].copy()
+            sub[:, 0] -= a0
+            sub[:, 2] -= b0
+            t0 = time.perf_counter()
+            out, word = oracle.lower_bounds(cfg["values"][a0:a1], cfg["queries"][b0:b1], sub,
+                                            max_qc=cfg["max_query_count"], tile=cfg["queries_per_tile"], lib=lib)
+            t += time.perf_counter() - t0
+            results.setdefault("search", []).append((b0, b1, a0, out, word))
+            done_q += b1 - b0
+            s = e
+        reps = 1
+        sample = f"first {s} of {seg.shape[0]} segments ({done_q} queries)"
+        qps = done_q / t
+        return {"value": round(qps * wl.call_bytes("search") / wl.nq / 1e9, 4), "unit": "GB/s", "cores": 1,
+                "kind": "oracle", "sample": sample, "seconds": round(t, 2),
+                "gelem_per_s": round(qps / 1e9, 6)}, results
     if isinstance(wl, ScanWorkload):
         while reps == 0 or (t < budget_s and reps < 50):
             t0 = time.perf_counter()
@@ -398,6 +468,14 @@ def check_parity(wl, results):
     """GPU outputs of the last step against the oracle (same bars as the tests)."""
     import numpy as np
     verdict = {}
+    if isinstance(wl, SearchWorkload):
+        out, val = wl.outs["search"]
+        out = out.cpu().numpy()
+        ok = int(val.cpu().view(torch_int32()).item()) == 0
+        for b0, b1, a0, ref, word in results["search"]:
+            ok = ok and word == 0 and np.array_equal(out[b0:b1] - a0, ref)
+        verdict["search_sampled"] = bool(ok)
+        return verdict
     if isinstance(wl, ScanWorkload):
         for (op, ex), ref in results.items():
             got = wl.outs[(op, ex)].cpu().numpy().reshape(ref.out.shape)
@@ -465,6 +543,11 @@ def check_parity(wl, results):
             ok = bool((np.abs(got.astype(np.float64) - ref.ref) <= tol).all())
         verdict[op] = bool(ok)
     return verdict
+
+
+def torch_int32():
+    import torch
+    return torch.int32
 
 
 def load_traffic(name, dominant_label, src_hash):
@@ -630,7 +713,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"rle": "u32/i32", "unique": "u32", "flags": "u32"}.get(args.config, "f32"),
+        "dtype": {"rle": "u32/i32", "unique": "u32", "flags": "u32", "search": "f32 (int64 positions)"}.get(
+            args.config, "f32"),
         "data": "synthetic (seeded numpy generators, workloads.py)",
         "config": {"workload": DESCRIPTIONS[args.config], "name": cfg.get("name", args.config),
                    "input_copies_rotated": len(getattr(wl, "vals", getattr(wl, "sets", getattr(wl, "inputs",

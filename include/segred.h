@@ -302,6 +302,60 @@ int segred_scan(const void *values, int32_t dtype, int64_t feat, const int64_t *
                 int64_t num_segments, int32_t op, int32_t exclusive, void *out,
                 hipStream_t stream);
 
+/*
+ * segred_galloping_search -- many lower-bound queries over segmented sorted
+ * values.
+ *
+ * Defined by the luma.gl "GPUGallopingSearch" page ("Overview", "Usage",
+ * "Validation", "Cost model"): segment record s = (vo, vc, qo, qc) names
+ * value positions [vo, vo + vc) and query positions [qo, qo + qc);
+ * out[qo + k] = the first position p in [vo, vo + vc) whose value is not
+ * less than query k, or vo + vc when there is none -- an absolute position
+ * in the value view, or in the order view when `value_order` is given.
+ * Queries are processed in tiles of `queries_per_tile` per segment; each
+ * tile seeds with a full search and gallops from answer to answer.
+ *
+ *   values           device array; value i is values[i * value_stride]
+ *                    (a strided column), i < value_count.  SEGRED_U32
+ *                    (unsigned order) or SEGRED_F32 (IEEE order); each value
+ *                    segment must be sorted ascending (caller's invariant).
+ *   value_order      uint32 [order_count] or NULL: search position p means
+ *                    value row value_order[p] (every entry < value_count,
+ *                    the caller's invariant; an entry past it reads as a
+ *                    value above every query, without a fault).
+ *   queries          [query_count] of the values' type; ascending inside a
+ *                    tile for the fast path.
+ *   segments         int64 [num_segments][4] records (vo, vc, qo, qc), read
+ *                    on the device.
+ *   max_query_count  per-segment query capacity the launch covers.
+ *   queries_per_tile T >= 1 (the page's default is 32).
+ *   out              int64 [query_count]; positions not answered (see
+ *                    validation) keep their contents.
+ *   validation       one uint32 on the device, cleared first unless
+ *                    preserve_validation is nonzero, then OR-ed with:
+ *                    1 a value range leaves its view (segment skipped),
+ *                    2 a query range leaves the query view or qc exceeds
+ *                      max_query_count (segment skipped),
+ *                    4 a query is below its predecessor in its tile (it is
+ *                      answered by a full search: still exact),
+ *                    8 a float32 query is not finite (it and the rest of
+ *                      its tile are not written).
+ *   stream           HIP stream the work is ordered on.
+ *
+ * Errors: SEGRED_ERR_INVALID_ARGUMENT for an unknown dtype, negative counts,
+ * value_stride < 1, queries_per_tile < 1, NULL or misaligned arrays that are
+ * needed (4 bytes for values, order, queries and validation; 8 for segments
+ * and out).  SEGRED_ERR_UNSUPPORTED for SEGRED_I32 (the page searches
+ * float32 or uint32) or more than 2^31 workgroups.  SEGRED_ERR_HIP if a
+ * launch fails.
+ */
+int segred_galloping_search(const void *values, int32_t dtype, int64_t value_count, int64_t value_stride,
+                            const uint32_t *value_order, int64_t order_count,
+                            const void *queries, int64_t query_count,
+                            const int64_t *segments, int64_t num_segments, int64_t max_query_count,
+                            int32_t queries_per_tile, int64_t *out, uint32_t *validation,
+                            int32_t preserve_validation, hipStream_t stream);
+
 /* Static, host-side description of a status code (never NULL). */
 const char *segred_status_string(int status);
 
@@ -328,7 +382,8 @@ int64_t segred_get_shares(int32_t dtype, int32_t op, int64_t feat);
  * when that kernel ends (hipExtLaunchKernel).  segred_timing_read waits for
  * the recorded events and reports, for every streaming kernel (the first
  * kernel of a segred_reduce call, both kernels of segred_scan, the atomic
- * kernel of segred_scatter_reduce,
+ * kernel of segred_scatter_reduce, the search kernel of
+ * segred_galloping_search,
  * the histogram of segred_offsets_from_index, the counting and materialising
  * kernels of segred_offsets_from_rle / segred_unique /
  * segred_offsets_from_flags), the time from the end of the launch recorded

@@ -11,6 +11,7 @@ There is no CPU fallback: if the library is missing, calls raise.
     out, arg = scatter(values, index, dim_size, "max")  # unsorted int64 index [N]
     offsets = offsets_from_index(sorted_index, dim_size)
     prefix = scan(values, offsets, "sum", exclusive=False)  # segmented scan
+    pos, word = galloping_search(values, queries, segments)  # lower bounds per segment
     values, count = unique(keys)                       # distinct adjacent values
     offsets, count = offsets_from_flags(start_flags)   # uint32 flags, nonzero = start
 """
@@ -67,6 +68,9 @@ def library(path: str | None = None):
             lib.segred_offsets_from_index.restype = ctypes.c_int
             lib.segred_scan.argtypes = [vp, i32, i64, vp, i64, i32, i32, vp, vp]
             lib.segred_scan.restype = ctypes.c_int
+            lib.segred_galloping_search.argtypes = [vp, i32, i64, i64, vp, i64, vp, i64, vp, i64, i64, i32, vp,
+                                                    vp, i32, vp]
+            lib.segred_galloping_search.restype = ctypes.c_int
             lib.segred_unique.argtypes = [vp, i64, vp, vp, vp]
             lib.segred_unique.restype = ctypes.c_int
             lib.segred_offsets_from_flags.argtypes = [vp, i64, vp, vp, vp]
@@ -293,6 +297,48 @@ def scan(values: torch.Tensor, offsets: torch.Tensor, op: str, *, exclusive: boo
                                    int(bool(exclusive)), out.data_ptr(), _stream(values.device))
     _check(rc, "segred_scan")
     return out
+
+
+def galloping_search(values: torch.Tensor, queries: torch.Tensor, segments: torch.Tensor, *,
+                     value_order: torch.Tensor | None = None, value_stride: int = 1, value_count: int | None = None,
+                     max_query_count: int | None = None, queries_per_tile: int = 32,
+                     out: torch.Tensor | None = None, validation: torch.Tensor | None = None,
+                     preserve_validation: bool = False):
+    """Lower bounds of ``queries`` over segmented sorted ``values``
+    (segred_galloping_search).  ``values`` and ``queries`` are uint32 or
+    float32 GPU tensors of one dtype; ``segments`` int64 [S, 4] records
+    (vo, vc, qo, qc) on the GPU.  ``max_query_count`` defaults to the
+    queries' length (no host read of the records).  Returns (out int64
+    [len(queries)], validation uint32 [1]), both on the GPU."""
+    if values.dtype not in (torch.uint32, torch.float32) or queries.dtype != values.dtype:
+        raise TypeError("values and queries must both be uint32 or both float32")
+    for t in (values, queries, segments):
+        if not t.is_cuda or t.device != values.device or not t.is_contiguous():
+            raise ValueError("values, queries and segments must be contiguous tensors on one GPU")
+    if segments.dtype != torch.int64 or segments.dim() != 2 or segments.shape[1] != 4:
+        raise ValueError("segments must be an int64 [S, 4] tensor")
+    if value_order is not None and (value_order.dtype != torch.uint32 or not value_order.is_cuda
+                                    or value_order.device != values.device or not value_order.is_contiguous()):
+        raise ValueError("value_order must be a contiguous uint32 tensor on the values' GPU")
+    n = values.numel()
+    vcount = value_count if value_count is not None else (n + value_stride - 1) // value_stride
+    qn = queries.numel()
+    mq = qn if max_query_count is None else int(max_query_count)
+    dev = values.device
+    if out is None:
+        out = torch.empty(qn, dtype=torch.int64, device=dev)
+    if validation is None:
+        validation = torch.zeros(1, dtype=torch.int32, device=dev).view(torch.uint32)
+    with torch.cuda.device(dev):
+        rc = library().segred_galloping_search(
+            values.data_ptr() if n else None, DTYPES[values.dtype], vcount, value_stride,
+            value_order.data_ptr() if value_order is not None else None,
+            value_order.numel() if value_order is not None else 0,
+            queries.data_ptr() if qn else None, qn, segments.data_ptr() if segments.numel() else None,
+            segments.shape[0], mq, queries_per_tile, out.data_ptr() if qn else None, validation.data_ptr(),
+            int(bool(preserve_validation)), _stream(dev))
+    _check(rc, "segred_galloping_search")
+    return out, validation
 
 
 def unique(keys: torch.Tensor):

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIB_DIR, "libsegred.so")
-SOURCES = ["api.hip", "reduce.hip", "rle.hip", "scatter.hip", "segscan.hip"]
+SOURCES = ["api.hip", "reduce.hip", "rle.hip", "scatter.hip", "segscan.hip", "galloping.hip"]
 ARCH = os.environ.get("SEGRED_OFFLOAD_ARCH", "gfx950")
 
 

@@ -1,0 +1,300 @@
+// galloping.hip -- many lower-bound queries over segmented sorted values
+// (luma.gl "GPUGallopingSearch": "Overview", "Usage", "Validation", "Cost
+// model").
+//
+// Segment record s = (vo, vc, qo, qc): value positions [vo, vo + vc) (of the
+// value view, or of the order view when an order vector is given: position
+// p then means row order[p]), query positions [qo, qo + qc).  out[qo + k] is
+// the first position p in [vo, vo + vc) whose value is not less than query
+// k, or vo + vc.  The queries of a segment are cut into tiles of T; each
+// (segment, tile) pair is one lane and independent of the others, as on the
+// page: the tile's first query (and any query below its predecessor) is
+// found by a full search of the segment, every later query by galloping
+// forward from the previous answer, then a bounded search, then a linear
+// scan once at most 16 values remain.
+//
+// For gfx950 each of those steps issues its probes together instead of one
+// after another, because a probe is a memory round trip: the gallop loads
+// the 16 values after the previous answer (one 64-byte run) and 6
+// exponential probes up to 1023 positions on in one round; a bounded
+// search splits its range 16 ways per round (15 probes loaded together); the
+// final linear scan loads its <= 16 values at once and takes the first one
+// not below the query.  The next query is loaded while the current one is
+// searched.  The answer is the same lower bound; only the number of
+// dependent round trips shrinks.
+//
+// Validation word (OR of): 1 a value range leaves its view, 2 a query range
+// leaves the query view or exceeds the per-segment capacity (neither
+// segment is searched), 4 a query below its predecessor in a tile (answered
+// by a full search, still exact), 8 a non-finite float32 query (it and the
+// rest of its tile are not written).  Bits are set with an atomic OR, whose
+// result does not depend on arrival order; each lane ORs once.
+#include "internal.hpp"
+#include "keys.hpp"
+#include "wave.hpp"
+
+namespace segred {
+
+struct GArgs {
+    const uint32_t *values;  // element bits; value i at values[i * stride]
+    int64_t value_count, stride;
+    const uint32_t *order;   // [order_count] rows of the search positions, or null
+    int64_t order_count;
+    const uint32_t *queries;  // [query_count]
+    int64_t query_count;
+    const int64_t *segments;  // [S][4]
+    int64_t S, max_qc, T, tiles;  // tiles per segment = ceil(max_qc / T)
+    int64_t *out;                 // [query_count]
+    uint32_t *validation;
+};
+
+constexpr int kGThreads = 256;
+
+__global__ __launch_bounds__(64) void gallop_clear(uint32_t *w) {
+    if (threadIdx.x == 0) *w = 0u;
+}
+
+template <int DT, bool ORDER>
+struct Probe {
+    const uint32_t *values;
+    const uint32_t *order;
+    int64_t value_count, stride;
+    // Value bits at search position p (p inside the validated range).  A row
+    // past the value view (a broken order vector, which the caller must
+    // prevent) reads as a value no query is above, without touching memory.
+    __device__ __forceinline__ uint32_t at(int64_t p) const {
+        int64_t row = p;
+        if constexpr (ORDER) row = (int64_t)order[p];
+        if (row >= value_count) return DT == DT_F32 ? 0x7FC00000u : 0xFFFFFFFFu;
+        return values[row * stride];
+    }
+    // The 16 values at positions a .. a+15 (entries at or past `end` are not
+    // used).  A plain column (no order vector, stride 1) whose window lies
+    // inside the segment is read with four 16-byte loads (the address is
+    // only 4-byte aligned, which the type says).
+    __device__ __forceinline__ void window16(int64_t a, int64_t end, uint32_t (&w)[16]) const {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));
+        if (!ORDER && stride == 1 && a + 16 <= end) {
+            const u32x4 *p = reinterpret_cast<const u32x4 *>(values + a);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const u32x4 v = p[j];
+                w[4 * j] = v.x;
+                w[4 * j + 1] = v.y;
+                w[4 * j + 2] = v.z;
+                w[4 * j + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) w[j] = a + j < end ? at(a + j) : 0u;
+        }
+    }
+    // value < query, in the value type (IEEE for float32, unsigned for uint32)
+    static __device__ __forceinline__ bool less(uint32_t v, uint32_t q) {
+        if constexpr (DT == DT_F32) return __uint_as_float(v) < __uint_as_float(q);
+        else return v < q;
+    }
+};
+
+// Lower bound of q in [lo, hi), knowing every position before lo is below q
+// and (when hi is not the segment end) position hi is not.  16-way rounds
+// while more than 16 positions remain, then one round over the rest.
+template <int DT, bool ORDER>
+__device__ __forceinline__ int64_t bounded(const Probe<DT, ORDER> &pr, int64_t lo, int64_t hi, uint32_t q) {
+    while (hi - lo > 16) {
+        const int64_t n = hi - lo;
+        int64_t pos[15];
+        uint32_t v[15];
+#pragma unroll
+        for (int j = 0; j < 15; ++j) pos[j] = lo + (n * (j + 1)) / 16;  // strictly inside [lo, hi)
+#pragma unroll
+        for (int j = 0; j < 15; ++j) v[j] = pr.at(pos[j]);
+        int64_t nlo = lo, nhi = hi;
+        bool found = false;
+#pragma unroll
+        for (int j = 0; j < 15; ++j) {
+            if (!found) {
+                if (Probe<DT, ORDER>::less(v[j], q)) {
+                    nlo = pos[j] + 1;
+                } else {
+                    nhi = pos[j];
+                    found = true;
+                }
+            }
+        }
+        lo = nlo;
+        hi = nhi;
+    }
+    // linear finish: the first of the <= 16 remaining values not below q
+    uint32_t v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = lo + j < hi ? pr.at(lo + j) : 0u;
+    int64_t lb = hi;
+#pragma unroll
+    for (int j = 15; j >= 0; --j)
+        if (lo + j < hi && !Probe<DT, ORDER>::less(v[j], q)) lb = lo + j;
+    return lb;
+}
+
+// Gallop from position a (every position before a is below q): one round
+// loads the 16 positions a .. a+15 together with 6 exponential probes at
+// a+31, a+63, ... a+1023, so any answer within about a thousand positions is
+// bracketed by a single round trip (the lanes of a wave search in lockstep,
+// so a wave waits for its slowest lane: every query should cost the same few
+// rounds).  If all are below q, the next round starts at a+1024 with a
+// window and probes 64 times coarser.  A bracket is finished by `bounded`.
+template <int DT, bool ORDER>
+__device__ __forceinline__ int64_t gallop(const Probe<DT, ORDER> &pr, int64_t a, int64_t end, uint32_t q) {
+    int64_t base = a;
+    int64_t scale = 1;
+    for (;;) {
+        if (base >= end) return end;
+        uint32_t w[16], e[6];
+        if (scale == 1) {
+            pr.window16(base, end, w);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) w[j] = base + j * scale < end ? pr.at(base + j * scale) : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+            const int64_t p = base + ((int64_t)32 << i) * scale - 1;
+            e[i] = p < end ? pr.at(p) : 0u;
+        }
+        if (scale == 1) {
+            // dense window: the first of base .. base+15 not below q is the
+            // answer; past the end of the segment, the end is
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                if (base + j >= end) return end;
+                if (!Probe<DT, ORDER>::less(w[j], q)) return base + j;
+            }
+        } else {
+            // sparse window: bracket the answer between two samples (or
+            // between the last sample and the end of the segment)
+            int64_t prev = base - 1;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int64_t p = base + j * scale;
+                if (p >= end) return bounded(pr, prev + 1, end, q);
+                if (!Probe<DT, ORDER>::less(w[j], q)) return bounded(pr, prev + 1, p, q);
+                prev = p;
+            }
+        }
+        // the window is below q; take the first exponential probe not below
+        int64_t prev = base + 15 * scale;
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+            const int64_t p = base + ((int64_t)32 << i) * scale - 1;
+            if (p >= end) return bounded(pr, prev + 1, end, q);
+            if (!Probe<DT, ORDER>::less(e[i], q)) return bounded(pr, prev + 1, p, q);
+            prev = p;
+        }
+        base = prev + 1;
+        scale *= 64;  // farther probes next round
+    }
+}
+
+template <int DT, bool ORDER>
+__global__ __launch_bounds__(kGThreads) void gallop_kernel(const GArgs a) {
+    const int64_t id = (int64_t)blockIdx.x * kGThreads + threadIdx.x;
+    const int64_t s = id / a.tiles, t = id - s * a.tiles;
+    if (s >= a.S) return;
+    const int64_t vo = a.segments[4 * s + 0], vc = a.segments[4 * s + 1];
+    const int64_t qo = a.segments[4 * s + 2], qc = a.segments[4 * s + 3];
+    const int64_t view = ORDER ? a.order_count : a.value_count;
+    const bool bad_v = vo < 0 || vc < 0 || vo > view || vc > view - vo;
+    const bool bad_q = qo < 0 || qc < 0 || qo > a.query_count || qc > a.query_count - qo || qc > a.max_qc;
+    uint32_t bits = 0;
+    if (bad_v || bad_q) {
+        if (t == 0) {
+            bits = (bad_v ? 1u : 0u) | (bad_q ? 2u : 0u);
+            __hip_atomic_fetch_or(a.validation, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return;
+    }
+    const int64_t k0 = t * a.T;
+    if (k0 >= qc) return;
+    const int64_t k1 = min(k0 + a.T, qc);
+    const Probe<DT, ORDER> pr{a.values, a.order, a.value_count, a.stride};
+    const int64_t end = vo + vc;
+    int64_t lb = vo;
+    uint32_t prevq = 0;
+    uint32_t qn = a.queries[qo + k0];
+    for (int64_t k = k0; k < k1; ++k) {
+        const uint32_t q = qn;
+        if (k + 1 < k1) qn = a.queries[qo + k + 1];  // next query in flight during this search
+        if (DT == DT_F32 && !isfinite(__uint_as_float(q))) {
+            bits |= 8u;
+            break;  // the rest of the tile is not written
+        }
+        bool full = k == k0;
+        if (!full && Probe<DT, ORDER>::less(q, prevq)) {
+            bits |= 4u;
+            full = true;
+        }
+        lb = full ? bounded(pr, vo, end, q) : gallop(pr, lb, end, q);
+        a.out[qo + k] = lb;
+        prevq = q;
+    }
+    if (bits) __hip_atomic_fetch_or(a.validation, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int DT>
+static int gallop_launch(const GArgs &a, hipStream_t st) {
+    const int64_t lanes = a.S * a.tiles;
+    const int64_t wgs = (lanes + kGThreads - 1) / kGThreads;
+    if (wgs > INT32_MAX) return SEGRED_ERR_UNSUPPORTED;
+    if (wgs == 0) return SEGRED_OK;
+    if (a.order)
+        hipExtLaunchKernelGGL((gallop_kernel<DT, true>), dim3((unsigned)wgs), dim3(kGThreads), 0, st, nullptr,
+                              timing_stop(true), 0, a);
+    else
+        hipExtLaunchKernelGGL((gallop_kernel<DT, false>), dim3((unsigned)wgs), dim3(kGThreads), 0, st, nullptr,
+                              timing_stop(true), 0, a);
+    return hipGetLastError() == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
+}
+
+}  // namespace segred
+
+using namespace segred;
+
+extern "C" int segred_galloping_search(const void *values, int32_t dtype, int64_t value_count, int64_t value_stride,
+                                       const uint32_t *value_order, int64_t order_count, const void *queries,
+                                       int64_t query_count, const int64_t *segments, int64_t num_segments,
+                                       int64_t max_query_count, int32_t queries_per_tile, int64_t *out,
+                                       uint32_t *validation, int32_t preserve_validation, hipStream_t stream) {
+    if (dtype < SEGRED_U32 || dtype > SEGRED_F32) return SEGRED_ERR_INVALID_ARGUMENT;
+    if (dtype == SEGRED_I32) return SEGRED_ERR_UNSUPPORTED;
+    if (value_count < 0 || value_stride < 1 || query_count < 0 || num_segments < 0 || max_query_count < 0 ||
+        queries_per_tile < 1 || (value_order && order_count < 0))
+        return SEGRED_ERR_INVALID_ARGUMENT;
+    if (value_count > 0 && value_stride > INT64_MAX / value_count) return SEGRED_ERR_INVALID_ARGUMENT;
+    if (!validation || (num_segments > 0 && !segments) || (value_count > 0 && !values) ||
+        (query_count > 0 && (!queries || !out)))
+        return SEGRED_ERR_INVALID_ARGUMENT;
+    if (!aligned(validation, 4) || (values && !aligned(values, 4)) || (queries && !aligned(queries, 4)) ||
+        (value_order && !aligned(value_order, 4)) || (segments && !aligned(segments, 8)) ||
+        (out && !aligned(out, 8)))
+        return SEGRED_ERR_INVALID_ARGUMENT;
+    if (!preserve_validation) {
+        hipExtLaunchKernelGGL(gallop_clear, dim3(1), dim3(64), 0, stream, nullptr, timing_stop(false), 0, validation);
+        if (hipGetLastError() != hipSuccess) return SEGRED_ERR_HIP;
+    }
+    GArgs a{};
+    a.values = static_cast<const uint32_t *>(values);
+    a.value_count = value_count;
+    a.stride = value_stride;
+    a.order = value_order;
+    a.order_count = value_order ? order_count : 0;
+    a.queries = static_cast<const uint32_t *>(queries);
+    a.query_count = query_count;
+    a.segments = segments;
+    a.S = num_segments;
+    a.max_qc = max_query_count;
+    a.T = queries_per_tile;
+    a.tiles = max_query_count > 0 ? (max_query_count + queries_per_tile - 1) / queries_per_tile : 1;
+    a.out = out;
+    a.validation = validation;
+    return dtype == SEGRED_F32 ? gallop_launch<DT_F32>(a, stream) : gallop_launch<DT_U32>(a, stream);
+}

@@ -28,7 +28,8 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for required in ("segred_reduce", "segred_offsets_from_rle", "segred_status_string", "segred_scatter_reduce",
-                     "segred_offsets_from_index", "segred_unique", "segred_offsets_from_flags", "segred_scan"):
+                     "segred_offsets_from_index", "segred_unique", "segred_offsets_from_flags", "segred_scan",
+                     "segred_galloping_search"):
         assert required in names
 
 
@@ -192,6 +193,26 @@ def test_scan_argument_checks(args, expect):
     assert lib.segred_scan(*args, None) == expect
 
 
+def _gs(**kw):
+    args = dict(values=FAKE, dtype=2, value_count=10, stride=1, order=None, order_count=0, queries=FAKE,
+                query_count=4, segments=FAKE, S=1, max_qc=4, T=32, out=FAKE, validation=FAKE, preserve=0)
+    args.update(kw)
+    return tuple(args.values())
+
+
+@pytest.mark.parametrize("args,expect", [
+    (_gs(dtype=3), 1), (_gs(dtype=1), 2),               # unknown dtype; int32 is not searched
+    (_gs(value_count=-1), 1), (_gs(stride=0), 1), (_gs(query_count=-1), 1), (_gs(S=-1), 1),
+    (_gs(max_qc=-1), 1), (_gs(T=0), 1), (_gs(order=FAKE, order_count=-1), 1),
+    (_gs(validation=None), 1), (_gs(segments=None), 1), (_gs(values=None), 1), (_gs(queries=None), 1),
+    (_gs(out=None), 1), (_gs(values=FAKE + 2), 1), (_gs(queries=FAKE + 2), 1), (_gs(segments=FAKE + 4), 1),
+    (_gs(out=FAKE + 4), 1), (_gs(validation=FAKE + 2), 1), (_gs(order=FAKE + 2, order_count=3), 1),
+])
+def test_galloping_argument_checks(args, expect):
+    lib = _lib()
+    assert lib.segred_galloping_search(*args, None) == expect
+
+
 def test_share_knob_range():
     lib = _lib()
     assert lib.segred_set_shares(-1) == 1
@@ -224,13 +245,14 @@ def test_kernel_sources_have_no_atomics_or_foreign_backends():
     """No atomics on global memory in the segmented and RLE paths (results are
     combined in a fixed order instead) and no CUDA/Triton/dual-platform code
     in the library sources.  The scatter path (scatter.hip) is atomic by
-    definition and is the one file exempt.  Elsewhere the one atomic allowed
+    definition, and the lower-bound search (galloping.hip) sets validation
+    bits with an atomic OR; those two files are exempt.  Elsewhere the one atomic allowed
     is the wave-scope LDS bit-OR helper `lds_or` (it sets flag bits, so
     arrival order cannot change a result)."""
     device_atomic = re.compile(r"\batomic[A-Z]\w*\s*\(|__hip_atomic|__atomic_\w+\s*\(|\bunsafeAtomic")
     allowed = "__hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT)"
     seen_allowed = 0
-    atomic_files = {"scatter.hip"}
+    atomic_files = {"scatter.hip", "galloping.hip"}
     for name in os.listdir(CSRC):
         code = re.sub(r"//[^\n]*", "", open(os.path.join(CSRC, name)).read())
         for bad in ("cuda", "triton", "__hip_platform"):

@@ -77,3 +77,15 @@ def test_scatter_case_orders():
     assert (np.diff(idx) == 0).mean() > 0.8
     idx, _ = W.scatter_case(5, 100, 7, order="one")
     assert (idx == 0).all()
+
+
+def test_search_shape():
+    c = W.search()
+    v, q, seg = c["values"], c["queries"], c["segments"]
+    assert seg.shape == (8192, 4) and seg.dtype == np.int64
+    assert v.dtype == np.float32 and q.dtype == np.float32
+    assert seg[:, 1].sum() == v.size and seg[:, 3].sum() == q.size and seg[:, 3].max() <= 2049
+    for vo, vc, qo, qc in seg[::97]:
+        assert (np.diff(v[vo:vo + vc]) >= 0).all() and (np.diff(q[qo:qo + qc]) >= 0).all()
+        if vc:
+            assert v[vo] > 0

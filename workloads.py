@@ -25,6 +25,13 @@ Configurations (sizes are decimal unless written as powers of two):
   powerlaw  2,000,000 nodes, 32,000,000 destination-sorted edges, in-degree
             Lomax/Pareto-II (alpha = 2) capped at 200,000 with one hub of
             exactly 200,000, F = 32 float32 normal(0, 1).
+  search    lower-bound queries over segmented sorted values, shaped like the
+            galloping-search page's uses (sampled time domains, repeated
+            threshold lookup) with its Usage defaults (maximumQueryCount
+            2049, 32 queries per tile): 8,192 segments, each a float32 time
+            axis of uniform[0, 4096] stamps (cumulative exponential gaps),
+            and uniform[0, 2049] sorted queries drawn over the segment's time
+            span widened by 5 % on both sides.
   scatter   the message rows in edge order: 1,000,000 rows x F float32
             normal(0, 1) with an int64 destination index drawn uniformly over
             10,000 outputs, unsorted (the graph-reduce README's scatter_*
@@ -151,8 +158,31 @@ def scatter(seed=0, feat=64, rows=1_000_000, dim=10_000):
             "f32": values}
 
 
+def search(seed=0, segments=8_192, max_values=4_096, max_queries=2_049):
+    rng = np.random.default_rng(seed)
+    vcs = rng.integers(0, max_values + 1, segments)
+    qcs = rng.integers(0, max_queries + 1, segments)
+    nv, nq = int(vcs.sum()), int(qcs.sum())
+    gaps = rng.exponential(1.0, nv).astype(np.float32)
+    values = np.empty(nv, dtype=np.float32)
+    queries = np.empty(nq, dtype=np.float32)
+    vo = np.cumsum(vcs) - vcs
+    qo = np.cumsum(qcs) - qcs
+    u = rng.random(nq)
+    for s in range(segments):
+        v = np.cumsum(gaps[vo[s]:vo[s] + vcs[s]], dtype=np.float64)
+        values[vo[s]:vo[s] + vcs[s]] = v.astype(np.float32)
+        span = float(v[-1]) if vcs[s] else 1.0
+        lo, hi = -0.05 * span, 1.05 * span
+        queries[qo[s]:qo[s] + qcs[s]] = np.sort(lo + (hi - lo) * u[qo[s]:qo[s] + qcs[s]]).astype(np.float32)
+    # (rounding a nondecreasing float64 sum to float32 keeps it nondecreasing)
+    segs = np.stack([vo, vcs, qo, qcs], axis=1).astype(np.int64)
+    return {"name": f"search-{segments // 1024}Kseg", "values": values, "queries": queries,
+            "segments": segs, "max_query_count": max_queries, "queries_per_tile": 32}
+
+
 CONFIGS = {"small": small, "message": message, "rle": rle_keys, "skew": skew, "powerlaw": powerlaw,
-           "scatter": scatter}
+           "scatter": scatter, "search": search}
 
 
 # ---------------------------------------------------------------- test-sized cases
