@@ -35,16 +35,27 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 MALL_BYTES = 256 << 20
 METRIC = "effective HBM GB/s (+% of peak) and Gelem/s for CSR segmented reduce, 1 GPU"
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["segmented_reduction_amd/csrc/reduce.hip", "segmented_reduction_amd/csrc/wave.hpp",
-                  "segmented_reduction_amd/csrc/rle.hip", "segmented_reduction_amd/csrc/keys.hpp",
-                  "segmented_reduction_amd/csrc/scan.hpp", "segmented_reduction_amd/csrc/scatter.hip",
-                  "segmented_reduction_amd/csrc/partition.hpp", "segmented_reduction_amd/csrc/segscan.hip",
-                  "segmented_reduction_amd/csrc/galloping.hip"]
+# Kernel sources behind each workload: the HBM-traffic figures in
+# profiles/traffic.json are keyed by a hash of these files and ignored once
+# any of them changes.
+_C = "segmented_reduction_amd/csrc/"
+_REDUCE = [_C + f for f in ("reduce.hip", "partition.hpp", "keys.hpp", "wave.hpp")]
+KERNEL_SOURCES = {
+    "reduce": _REDUCE,
+    "rle": _REDUCE + [_C + "rle.hip", _C + "scan.hpp"],
+    "runs": [_C + "rle.hip", _C + "scan.hpp", _C + "wave.hpp"],
+    "scatter": [_C + f for f in ("scatter.hip", "keys.hpp", "scan.hpp", "wave.hpp")],
+    "scan": [_C + f for f in ("segscan.hip", "partition.hpp", "keys.hpp", "wave.hpp")],
+    "search": [_C + f for f in ("galloping.hip", "keys.hpp", "wave.hpp")],
+}
+CONFIG_SOURCES = {"small": "reduce", "message": "reduce", "skew": "reduce", "powerlaw": "reduce", "rle": "rle",
+                  "unique": "runs", "flags": "runs", "scatter": "scatter", "scatter16": "scatter", "scan": "scan",
+                  "scan1d": "scan", "search": "search"}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(config: str = "message") -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[CONFIG_SOURCES[config]]:
         with open(os.path.join(ROOT, p), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -663,7 +674,7 @@ def main():
                           "frac": round(b / (avg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
     dk = kernels[dominant]
-    src_hash = kernel_source_hash()
+    src_hash = kernel_source_hash(args.config)
     traffic = load_traffic(args.config, dominant, src_hash)
     roofline = {"bound": "hbm", "achieved": dk["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": dk["frac"], "traffic": traffic,
