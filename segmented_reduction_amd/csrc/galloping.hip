@@ -19,9 +19,12 @@
 // exponential probes up to 1023 positions on in one round; a bounded
 // search splits its range 16 ways per round (15 probes loaded together); the
 // final linear scan loads its <= 16 values at once and takes the first one
-// not below the query.  The next query is loaded while the current one is
-// searched.  The answer is the same lower bound; only the number of
-// dependent round trips shrinks.
+// not below the query.  The exponential probes join the first window only
+// for a lane whose previous gap was wider than the window (each probe is a
+// cache line of its own).  The next query is loaded while the current one is
+// searched, and answers are stored four at a time.  The answer is the same
+// lower bound; only the number of dependent round trips and the memory
+// traffic shrink.
 //
 // Validation word (OR of): 1 a value range leaves its view, 2 a query range
 // leaves the query view or exceeds the per-segment capacity (neither
@@ -144,23 +147,29 @@ __device__ __forceinline__ int64_t bounded(const Probe<DT, ORDER> &pr, int64_t l
 // rounds).  If all are below q, the next round starts at a+1024 with a
 // window and probes 64 times coarser.  A bracket is finished by `bounded`.
 template <int DT, bool ORDER>
-__device__ __forceinline__ int64_t gallop(const Probe<DT, ORDER> &pr, int64_t a, int64_t end, uint32_t q) {
+__device__ __forceinline__ int64_t gallop(const Probe<DT, ORDER> &pr, int64_t a, int64_t end, uint32_t q,
+                                          bool wide) {
     int64_t base = a;
     int64_t scale = 1;
     for (;;) {
         if (base >= end) return end;
         uint32_t w[16], e[6];
+        auto load_probes = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 6; ++i) {
+                const int64_t p = base + ((int64_t)32 << i) * scale - 1;
+                e[i] = p < end ? pr.at(p) : 0u;
+            }
+        };
         if (scale == 1) {
             pr.window16(base, end, w);
         } else {
 #pragma unroll
             for (int j = 0; j < 16; ++j) w[j] = base + j * scale < end ? pr.at(base + j * scale) : 0u;
         }
-#pragma unroll
-        for (int i = 0; i < 6; ++i) {
-            const int64_t p = base + ((int64_t)32 << i) * scale - 1;
-            e[i] = p < end ? pr.at(p) : 0u;
-        }
+        // the exponential probes ride along with the first window only when
+        // this lane's last gap was wide (they cost a cache line each)
+        if (wide || scale != 1) load_probes();
         if (scale == 1) {
             // dense window: the first of base .. base+15 not below q is the
             // answer; past the end of the segment, the end is
@@ -181,6 +190,7 @@ __device__ __forceinline__ int64_t gallop(const Probe<DT, ORDER> &pr, int64_t a,
                 prev = p;
             }
         }
+        if (!wide && scale == 1) load_probes();
         // the window is below q; take the first exponential probe not below
         int64_t prev = base + 15 * scale;
 #pragma unroll
@@ -221,7 +231,13 @@ __global__ __launch_bounds__(kGThreads) void gallop_kernel(const GArgs a) {
     int64_t lb = vo;
     uint32_t prevq = 0;
     uint32_t qn = a.queries[qo + k0];
-    for (int64_t k = k0; k < k1; ++k) {
+    bool wide = true;
+    // answers go out four at a time (32 contiguous bytes per lane rather than
+    // 8-byte pieces spread over the search)
+    int64_t held[4];
+    int nheld = 0;
+    int64_t k = k0;
+    for (; k < k1; ++k) {
         const uint32_t q = qn;
         if (k + 1 < k1) qn = a.queries[qo + k + 1];  // next query in flight during this search
         if (DT == DT_F32 && !isfinite(__uint_as_float(q))) {
@@ -233,10 +249,21 @@ __global__ __launch_bounds__(kGThreads) void gallop_kernel(const GArgs a) {
             bits |= 4u;
             full = true;
         }
-        lb = full ? bounded(pr, vo, end, q) : gallop(pr, lb, end, q);
-        a.out[qo + k] = lb;
+        const int64_t nlb = full ? bounded(pr, vo, end, q) : gallop(pr, lb, end, q, wide);
+        wide = full || nlb - lb > 16;
+        lb = nlb;
         prevq = q;
+        held[nheld++ & 3] = lb;
+        if (nheld == 4) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a.out[qo + k - 3 + j] = held[j];
+            nheld = 0;
+        }
     }
+    // the answers still held belong to the queries just before k
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+        if (j < nheld) a.out[qo + k - nheld + j] = held[j];
     if (bits) __hip_atomic_fetch_or(a.validation, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
