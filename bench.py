@@ -101,11 +101,16 @@ class ReduceWorkload(Workload):
         self.calls = [(op, op) for op in ops]
         self.kernels_per_step = 2 * len(ops)  # two kernels per call
         self.ncalls = 0
+        # outputs allocated once, as a caller reusing buffers would
+        shape = (self.segs,) + tuple(self.host_vals.shape[1:])
+        self.out_buf = {op: torch.empty(shape, dtype=torch.float32, device=dev_vals.device) for op in ops}
+        self.arg_buf = {op: torch.empty(shape, dtype=torch.int64, device=dev_vals.device)
+                        for op in ops if op in ("min", "max")}
 
     def step(self, i):
         for j, op in enumerate(self.ops):
             v = self.vals[(i * len(self.ops) + j) % len(self.vals)]
-            self.outs[op] = self.sr.reduce(v, self.off, op)
+            self.outs[op] = self.sr.reduce(v, self.off, op, out=self.out_buf[op], arg=self.arg_buf.get(op))
 
     def call_bytes(self, op):
         return reduce_bytes(self.rows, self.feat, self.segs, op)
