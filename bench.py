@@ -49,7 +49,8 @@ KERNEL_SOURCES = {
     "search": [_C + f for f in ("galloping.hip", "keys.hpp", "wave.hpp")],
 }
 CONFIG_SOURCES = {"small": "reduce", "message": "reduce", "skew": "reduce", "powerlaw": "reduce", "rle": "rle",
-                  "unique": "runs", "flags": "runs", "scatter": "scatter", "scatter16": "scatter", "scan": "scan",
+                  "unique": "runs", "flags": "runs", "scatter": "scatter", "scatter16": "scatter", "scatter100": "scatter",
+                  "scan": "scan",
                   "scan1d": "scan", "search": "search"}
 
 
@@ -364,6 +365,8 @@ DESCRIPTIONS = {
                "index uniform over 10,000 outputs; atomic scatter sum and scatter max+argmax",
     "scatter16": "scatter path: 1,000,000 rows x F=16 f32 normal(0,1) in edge order, unsorted int64 "
                  "destination index uniform over 10,000 outputs; atomic scatter sum and scatter max+argmax",
+    "scatter100": "scatter path, few outputs: 1,000,000 rows x F=16 f32 normal(0,1), unsorted int64 destination "
+                  "index uniform over 100 outputs (private LDS copies per workgroup); scatter sum and max+argmax",
 }
 
 
@@ -384,8 +387,8 @@ def build_workload(name, sr, torch):
     if name in ("unique", "flags"):
         cfg = W.rle_keys()
         return RunsWorkload(cfg, name, copies=4, sr=sr, torch=torch), cfg
-    if name in ("scatter", "scatter16"):
-        cfg = W.scatter(feat=64 if name == "scatter" else 16)
+    if name in ("scatter", "scatter16", "scatter100"):
+        cfg = W.scatter(feat=64 if name == "scatter" else 16, dim=100 if name == "scatter100" else 10_000)
         nbytes = cfg["f32"].nbytes + cfg["index"].nbytes
         copies = max(1, min(4, -(-4 * MALL_BYTES // nbytes)))
         return ScatterWorkload(cfg, ["sum", "max"], copies, sr, torch), cfg

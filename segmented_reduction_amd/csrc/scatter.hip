@@ -24,8 +24,19 @@
 // two neighbours share an index), so a sorted or clustered index sends one
 // atomic per run rather than one per row.
 //
+// With few outputs (they fit 32 KB of LDS) and many rows per output, each
+// workgroup accumulates into a private LDS copy, stores it to its own
+// scratch slot, and a fold kernel combines the copies in a fixed order with
+// plain stores (scatter_private, scatter_private_fold).  Sums of rows with
+// >= 2 features use one copy per wave and no atomics at all, so they repeat
+// bit for bit; 1-D sums and min/max use LDS atomics (min/max are exact
+// anyway).
+//
 // Rows whose index lies outside [0, dim_size) are skipped: they take part in
 // no output (and no memory outside the outputs is touched for them).
+#include <algorithm>
+#include <map>
+
 #include "internal.hpp"
 #include "keys.hpp"
 #include "scan.hpp"
@@ -48,6 +59,10 @@ struct ScArgs {
     uint32_t *out;           // [dim, F]: sums (SUM, MEAN)
     uint64_t *words;         // [dim, F]: packed key/row words (MIN, MAX)
     uint32_t *counts;        // [dim]: rows per output (MEAN)
+    uint32_t *priv;          // [priv_grid][cells] private copies (32- or 64-bit cells), then [priv_grid][dim] counts
+    int64_t priv_grid;       // workgroups of the private path, 0 for the element-atomic path
+    int priv_waves;          // private path with one copy per wave (float sums of >= 8 features)
+    int priv_lds;            // LDS bytes per workgroup of the private path
 };
 
 // Packed word of (key, row): the integer max of MAX words is the largest key
@@ -161,6 +176,207 @@ __global__ __launch_bounds__(kScThreads) void scatter_kernel(ScArgs a) {
                 if (f == 0)
                     __hip_atomic_fetch_add(a.counts + s[u], cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
+        }
+    }
+}
+
+// Few outputs: each workgroup accumulates into its own copy of the outputs
+// in LDS (LDS atomics, resolved inside the CU) and stores that copy to its
+// scratch slot.  Used when the outputs fit kPrivBytes and the rows are many
+// times the output cells (the page's contended case: many rows into a few
+// hundred outputs, where element atomics to the same few addresses
+// serialise at the memory side).  The LDS is sized per launch (priv_lds),
+// so small output sets leave room for more workgroups per CU.
+constexpr int kPrivBytes = 32768;
+constexpr int kLdsPerCu = 163840;  // 160 KB of LDS per compute unit
+constexpr int kWgPerCu = 8;        // 32 waves per CU in workgroups of 4 waves
+
+//
+// WAVES (float sums with rows of >= 8 features): each wave keeps a copy of
+// its own and adds with a plain read-modify-write, one row group of the step
+// after another (at most 8 turns), so no two lanes touch a cell at once and
+// no LDS float atomic (several times slower than the integer ones here) is
+// needed; the four copies are added in wave order at the end, so the
+// workgroup's partial sums have a fixed order.  Integer sums keep the LDS
+// atomics, which are exact in any order and faster than the turns.
+template <int DT, int OP, bool WAVES>
+__global__ __launch_bounds__(kScThreads) void scatter_private(ScArgs a) {
+    constexpr bool kWord = OP == OP_MIN || OP == OP_MAX;
+    static_assert(!(WAVES && kWord), "per-wave copies are for sums");
+    extern __shared__ __attribute__((aligned(16))) uint64_t s_priv[];  // priv_lds bytes
+    uint64_t *c64 = s_priv;
+    uint32_t *c32 = reinterpret_cast<uint32_t *>(s_priv);
+    const int64_t cells = a.dim * a.F;
+    constexpr int kCopies = WAVES ? kScThreads / 64 : 1;
+    uint32_t *cnt = c32 + (kWord ? 2 * cells : kCopies * cells);  // MEAN: rows per output
+    const int tid = threadIdx.x;
+    for (int64_t i = tid; i < kCopies * cells; i += kScThreads) {
+        if constexpr (kWord) c64[i] = kEmptyWord<OP>;
+        else c32[i] = 0u;
+    }
+    if constexpr (OP == OP_MEAN)
+        for (int64_t i = tid; i < a.dim; i += kScThreads) cnt[i] = 0u;
+    __syncthreads();
+
+    const int lane = tid & 63;
+    const int lg = a.lg;
+    const int64_t G = 64 >> lg;
+    const int sub = lane & ((1 << lg) - 1);
+    const int64_t stride = (int64_t)gridDim.x * (kScThreads / 64) * kScSteps * G;
+    for (int64_t qbase = ((int64_t)blockIdx.x * (kScThreads / 64) + (tid >> 6)) * kScSteps * G; qbase < a.items;
+         qbase += stride) {
+        int64_t s[kScSteps], fe[kScSteps], row[kScSteps];
+        uint32_t x[kScSteps];
+#pragma unroll
+        for (int u = 0; u < kScSteps; ++u) {
+            int64_t q = qbase + u * G + (lane >> lg);
+            int64_t r = q, f = sub;
+            if (a.chunks > 1) {
+                q = readfirst(q);  // one item per wave step (64 lanes per item)
+                r = q / a.chunks;
+                f = (q - r * a.chunks) * 64 + lane;
+            }
+            const bool live = q < a.items && f < a.F;
+            s[u] = live ? a.index[r] : -1;
+            x[u] = live ? a.values[r * a.F + f] : 0u;
+            fe[u] = f;
+            row[u] = r;
+        }
+        if constexpr (WAVES) {
+            uint32_t *mine = c32 + (tid >> 6) * cells;
+            const int grp = lane >> lg;
+#pragma unroll
+            for (int u = 0; u < kScSteps; ++u) {
+                const bool act = s[u] >= 0 && s[u] < a.dim;
+                const int64_t cell = s[u] * a.F + fe[u];
+                for (int gg = 0; gg < (int)G; ++gg) {
+                    if (grp == gg && act) {
+                        if constexpr (DT == DT_F32)
+                            mine[cell] = __float_as_uint(__uint_as_float(mine[cell]) + __uint_as_float(x[u]));
+                        else
+                            mine[cell] += x[u];
+                    }
+                    // keep the groups' turns apart: a group reads the cells
+                    // the previous group of this wave has just written
+                    asm volatile("" ::: "memory");
+                }
+                if constexpr (OP == OP_MEAN) {
+                    if (act && fe[u] == 0)
+                        __hip_atomic_fetch_add(cnt + s[u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                }
+            }
+            continue;
+        }
+#pragma unroll
+        for (int u = 0; u < kScSteps; ++u) {
+            if (s[u] < 0 || s[u] >= a.dim) continue;
+            const int64_t cell = s[u] * a.F + fe[u];
+            if constexpr (OP == OP_MAX) {
+                __hip_atomic_fetch_max(c64 + cell, pack<OP>(okey<DT>(x[u]), row[u]), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+            } else if constexpr (OP == OP_MIN) {
+                __hip_atomic_fetch_min(c64 + cell, pack<OP>(okey<DT>(x[u]), row[u]), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+            } else if constexpr (DT == DT_F32) {
+                __hip_atomic_fetch_add(reinterpret_cast<float *>(c32) + cell, __uint_as_float(x[u]), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+            } else {
+                __hip_atomic_fetch_add(c32 + cell, x[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+            if constexpr (OP == OP_MEAN) {
+                if (fe[u] == 0) __hip_atomic_fetch_add(cnt + s[u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        }
+    }
+    __syncthreads();
+    // the workgroup's copy goes to its own scratch slot with plain stores
+    // (global atomics from every workgroup into the same few outputs would
+    // serialise at the memory side); scatter_private_fold combines them
+    if constexpr (kWord) {
+        uint64_t *dst = reinterpret_cast<uint64_t *>(a.priv) + blockIdx.x * cells;
+        for (int64_t i = tid; i < cells; i += kScThreads) dst[i] = c64[i];
+    } else if constexpr (WAVES) {
+        uint32_t *dst = a.priv + blockIdx.x * cells;
+        for (int64_t i = tid; i < cells; i += kScThreads) {
+            if constexpr (DT == DT_F32) {
+                float v = __uint_as_float(c32[i]);
+#pragma unroll
+                for (int c = 1; c < kCopies; ++c) v += __uint_as_float(c32[c * cells + i]);
+                dst[i] = __float_as_uint(v);
+            } else {
+                uint32_t v = c32[i];
+#pragma unroll
+                for (int c = 1; c < kCopies; ++c) v += c32[c * cells + i];
+                dst[i] = v;
+            }
+        }
+    } else {
+        uint32_t *dst = a.priv + blockIdx.x * cells;
+        for (int64_t i = tid; i < cells; i += kScThreads) dst[i] = c32[i];
+    }
+    if constexpr (OP == OP_MEAN) {
+        uint32_t *dst = a.priv + gridDim.x * cells + blockIdx.x * a.dim;
+        for (int64_t i = tid; i < a.dim; i += kScThreads) dst[i] = cnt[i];
+    }
+}
+
+// Fold the nwg private copies of each output cell and store the result (no
+// atomics: each cell has one owner).  One wave per cell: lane l takes copies
+// l, l + 64, ... in order, then the lanes combine in a fixed tree, so the
+// fold order is fixed.  The MEAN counts are folded the same way, one wave per
+// output.
+template <int DT, int OP>
+__global__ __launch_bounds__(kScThreads) void scatter_private_fold(ScArgs a, int64_t nwg) {
+    constexpr bool kWord = OP == OP_MIN || OP == OP_MAX;
+    const int lane = threadIdx.x & 63;
+    const int64_t cells = a.dim * a.F;
+    const int64_t w = (int64_t)blockIdx.x * (kScThreads / 64) + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * (kScThreads / 64);
+    for (int64_t i = w; i < cells; i += nwaves) {
+        if constexpr (kWord) {
+            const uint64_t *src = reinterpret_cast<const uint64_t *>(a.priv);
+            uint64_t acc = kEmptyWord<OP>;
+            for (int64_t g = lane; g < nwg; g += 64) {
+                const uint64_t v = src[g * cells + i];
+                acc = OP == OP_MAX ? (v > acc ? v : acc) : (v < acc ? v : acc);
+            }
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                const uint64_t v = lane_get(acc, (lane + o) & 63);
+                if (lane < o) acc = OP == OP_MAX ? (v > acc ? v : acc) : (v < acc ? v : acc);
+            }
+            if (lane == 0) a.words[i] = acc;
+        } else if constexpr (DT == DT_F32) {
+            float acc = 0.0f;
+            for (int64_t g = lane; g < nwg; g += 64) acc += __uint_as_float(a.priv[g * cells + i]);
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                const float v = lane_get(acc, (lane + o) & 63);
+                if (lane < o) acc += v;
+            }
+            if (lane == 0) a.out[i] = __float_as_uint(acc);
+        } else {
+            uint32_t acc = 0u;
+            for (int64_t g = lane; g < nwg; g += 64) acc += a.priv[g * cells + i];
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                const uint32_t v = lane_get(acc, (lane + o) & 63);
+                if (lane < o) acc += v;
+            }
+            if (lane == 0) a.out[i] = acc;
+        }
+    }
+    if constexpr (OP == OP_MEAN) {
+        const uint32_t *src = a.priv + nwg * cells;
+        for (int64_t i = w; i < a.dim; i += nwaves) {
+            uint32_t n = 0u;
+            for (int64_t g = lane; g < nwg; g += 64) n += src[g * a.dim + i];
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                const uint32_t v = lane_get(n, (lane + o) & 63);
+                if (lane < o) n += v;
+            }
+            if (lane == 0) a.counts[i] = n;
         }
     }
 }
@@ -299,6 +515,25 @@ __global__ __launch_bounds__(kCountThreads) void count_apply(int64_t *counts, in
     }
 }
 
+// Compute units of the current device (cached per device; 256 if the query
+// fails).
+static int64_t device_cus() {
+    static std::mutex mu;
+    static std::map<int, int64_t> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(dev);
+    if (it != cache.end()) return it->second;
+    int cus = 0;
+    const int64_t n = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0
+                          ? cus
+                          : 256;
+    (void)hipGetLastError();
+    cache[dev] = n;
+    return n;
+}
+
 template <int DT, int OP>
 int scatter_launch(const ScArgs &a, int64_t *arg, hipStream_t st) {
     const int64_t per_wave = (int64_t)kScSteps * (64 >> a.lg);
@@ -306,7 +541,29 @@ int scatter_launch(const ScArgs &a, int64_t *arg, hipStream_t st) {
     const int64_t wgs = (waves + kScThreads / 64 - 1) / (kScThreads / 64);
     if (wgs > INT32_MAX) return SEGRED_ERR_UNSUPPORTED;
     hipError_t e = hipSuccess;
-    if (wgs > 0) {
+    if (a.priv_grid > 0) {
+        const int64_t cells = a.dim * a.F;
+        const unsigned lds = (unsigned)a.priv_lds;
+        if constexpr (DT == DT_F32 && (OP == OP_SUM || OP == OP_MEAN)) {
+            if (a.priv_waves)
+                hipExtLaunchKernelGGL((scatter_private<DT, OP, true>), dim3((unsigned)a.priv_grid), dim3(kScThreads),
+                                      lds, st, nullptr, timing_stop(true), 0, a);
+            else
+                hipExtLaunchKernelGGL((scatter_private<DT, OP, false>), dim3((unsigned)a.priv_grid), dim3(kScThreads),
+                                      lds, st, nullptr, timing_stop(true), 0, a);
+        } else {
+            hipExtLaunchKernelGGL((scatter_private<DT, OP, false>), dim3((unsigned)a.priv_grid), dim3(kScThreads), lds,
+                                  st, nullptr, timing_stop(true), 0, a);
+        }
+        e = hipGetLastError();
+        if (e == hipSuccess) {
+            // one wave per output cell
+            const unsigned fg = (unsigned)std::max<int64_t>(1, std::min<int64_t>((cells + 3) / 4, 8192));
+            hipExtLaunchKernelGGL((scatter_private_fold<DT, OP>), dim3(fg), dim3(kScThreads), 0, st, nullptr,
+                                  timing_stop(false), 0, a, a.priv_grid);
+            e = hipGetLastError();
+        }
+    } else if (wgs > 0) {
         if (a.lg == 0)
             hipExtLaunchKernelGGL((scatter_kernel<DT, OP, true>), dim3((unsigned)wgs), dim3(kScThreads), 0, st,
                                   nullptr, timing_stop(true), 0, a);
@@ -379,11 +636,33 @@ extern "C" int segred_scatter_reduce(const void *values, int32_t dtype, int64_t 
     size_t need = 0;
     if ((op == SEGRED_MIN || op == SEGRED_MAX) && !arg) need = (size_t)cells * 8;
     if (op == SEGRED_MEAN) need = (size_t)dim_size * 4;
+    need = (need + 255) & ~size_t(255);
+    // Few outputs: private LDS copies when they fit and there are at least
+    // 16 x 64 elements per output cell.  Grid: at most one workgroup per 8
+    // elements per cell (the copies then add at most an eighth of the input
+    // bytes, written once and read once by the fold), at most one per item
+    // range of the element-atomic grid, and no more than fit the chip at once.
+    const bool word_op = op == SEGRED_MIN || op == SEGRED_MAX;
+    const int64_t count_bytes = op == SEGRED_MEAN ? dim_size * 4 : 0;
+    const int64_t priv_bytes = cells * (word_op ? 8 : 4) + count_bytes;
+    const int64_t elems = rows * feat;
+    if (priv_bytes <= kPrivBytes && elems >= 16 * 64 * cells) {
+        const bool waves = dtype == SEGRED_F32 && (op == SEGRED_SUM || op == SEGRED_MEAN) && lg >= 3 &&
+                           cells * 4 * (kScThreads / 64) + count_bytes <= kPrivBytes;
+        a.priv_waves = waves ? 1 : 0;
+        a.priv_lds = (int)(waves ? cells * 4 * (kScThreads / 64) + count_bytes : priv_bytes);
+        const int64_t per_wave = (int64_t)kScSteps * (64 >> lg);
+        const int64_t wgs = ((a.items + per_wave - 1) / per_wave + kScThreads / 64 - 1) / (kScThreads / 64);
+        const int64_t resident = (int64_t)device_cus() * std::min<int64_t>(kWgPerCu, kLdsPerCu / a.priv_lds);
+        a.priv_grid = std::max<int64_t>(1, std::min<int64_t>({wgs, elems / (8 * cells), resident}));
+    }
+    const size_t priv_need = (size_t)(a.priv_grid * priv_bytes);
     ScratchLease scratch;
-    if (need > 0) {
-        const int rc = scratch_acquire(scratch, need, stream);
+    if (need + priv_need > 0) {
+        const int rc = scratch_acquire(scratch, need + priv_need, stream);
         if (rc != SEGRED_OK) return rc;
     }
+    if (priv_need > 0) a.priv = reinterpret_cast<uint32_t *>(static_cast<char *>(scratch.ptr) + need);
     if (op == SEGRED_MIN || op == SEGRED_MAX) {
         a.words = arg ? reinterpret_cast<uint64_t *>(arg) : static_cast<uint64_t *>(scratch.ptr);
         const uint64_t empty = op == SEGRED_MAX ? kEmptyWord<OP_MAX> : kEmptyWord<OP_MIN>;

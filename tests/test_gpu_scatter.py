@@ -204,6 +204,46 @@ def test_scatter_repeatability():
         _check(index, vf, 100, "sum", what=f"float repeat {rep}")
 
 
+# ---------------------------------------------------------------- few outputs (private LDS copies)
+
+PRIVATE = [
+    # (seed, rows, dim, feat, order, out_of_range): at least 1,024 elements per output cell
+    (51, 120_000, 1, 1, "random", 0.0),
+    (52, 150_000, 100, 1, "random", 0.1),
+    (53, 200_000, 7, 3, "runs", 0.02),
+    (54, 110_000, 100, 8, "random", 0.0),
+    (55, 105_000, 60, 16, "sorted", 0.05),
+    (56, 70_000, 3, 100, "random", 0.0),
+]
+
+
+@pytest.mark.parametrize("kind", ["f32", "i32", "u32"])
+@pytest.mark.parametrize("case", PRIVATE, ids=lambda c: f"r{c[1]}-d{c[2]}-f{c[3]}-{c[4]}")
+def test_scatter_few_outputs(case, kind):
+    """Many rows into few outputs: each workgroup reduces into a private copy
+    in LDS (one copy per wave for float sums of >= 8 features), stores it to
+    its own scratch slot, and a fold kernel combines the copies."""
+    seed, rows, dim, feat, order, oor = case
+    index, vals = W.scatter_case(seed, rows, dim, feat=feat, dtype=kind, order=order, out_of_range=oor,
+                                 values="ties" if kind != "f32" else "normal")
+    for op in _ops(kind):
+        _check(index, vals, dim, op, what=f"few outputs seed={seed}")
+
+
+@pytest.mark.parametrize("feat", [8, 16, 100])
+def test_scatter_few_outputs_float_sums_repeat(feat):
+    """Float sums into few outputs with >= 8 features add in a fixed order
+    (per-wave copies, then the copies in wave and workgroup order): two calls
+    give the same bits, for sum and mean."""
+    index, vals = W.scatter_case(60 + feat, 200_000, 16, feat=feat, dtype="f32", order="random", out_of_range=0.01)
+    for op in ("sum", "mean"):
+        gu.say(f"scatter few-output repeat F={feat} {op}")
+        a, _ = _run(vals, index, 16, op, want_arg=False)
+        b, _ = _run(vals, index, 16, op, want_arg=False)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+        _assert_scatter(vals, index, 16, op, a, None, what=f"few-output repeat F={feat}")
+
+
 # ---------------------------------------------------------------- index -> offsets
 
 OFFSET_CASES = [

@@ -154,7 +154,8 @@ def scatter(seed=0, feat=64, rows=1_000_000, dim=10_000):
     rng = np.random.default_rng(seed)
     index = rng.integers(0, dim, rows, dtype=np.int64)
     values = rng.standard_normal((rows, feat), dtype=np.float32)
-    return {"name": f"scatter-{rows // 1_000_000}Mx{feat}-{dim // 1000}Kdst", "index": index, "dim": dim,
+    tag = f"{dim // 1000}K" if dim >= 1000 else str(dim)
+    return {"name": f"scatter-{rows // 1_000_000}Mx{feat}-{tag}dst", "index": index, "dim": dim,
             "f32": values}
 
 
