@@ -59,7 +59,8 @@ struct ScArgs {
     uint32_t *out;           // [dim, F]: sums (SUM, MEAN)
     uint64_t *words;         // [dim, F]: packed key/row words (MIN, MAX)
     uint32_t *counts;        // [dim]: rows per output (MEAN)
-    uint32_t *priv;          // [priv_grid][cells] private copies (32- or 64-bit cells), then [priv_grid][dim] counts
+    uint32_t *priv;          // [priv_grid][T] private copies: cells (32- or 64-bit), then for MEAN dim counts
+    uint32_t *part;          // [<= 64][T] partial folds of the copies (when priv_grid > 64)
     int64_t priv_grid;       // workgroups of the private path, 0 for the element-atomic path
     int priv_waves;          // private path with one copy per wave (float sums of >= 8 features)
     int priv_lds;            // LDS bytes per workgroup of the private path
@@ -296,7 +297,7 @@ __global__ __launch_bounds__(kScThreads) void scatter_private(ScArgs a) {
         uint64_t *dst = reinterpret_cast<uint64_t *>(a.priv) + blockIdx.x * cells;
         for (int64_t i = tid; i < cells; i += kScThreads) dst[i] = c64[i];
     } else if constexpr (WAVES) {
-        uint32_t *dst = a.priv + blockIdx.x * cells;
+        uint32_t *dst = a.priv + blockIdx.x * (cells + (OP == OP_MEAN ? a.dim : 0));
         for (int64_t i = tid; i < cells; i += kScThreads) {
             if constexpr (DT == DT_F32) {
                 float v = __uint_as_float(c32[i]);
@@ -311,22 +312,69 @@ __global__ __launch_bounds__(kScThreads) void scatter_private(ScArgs a) {
             }
         }
     } else {
-        uint32_t *dst = a.priv + blockIdx.x * cells;
+        uint32_t *dst = a.priv + blockIdx.x * (cells + (OP == OP_MEAN ? a.dim : 0));
         for (int64_t i = tid; i < cells; i += kScThreads) dst[i] = c32[i];
     }
     if constexpr (OP == OP_MEAN) {
-        uint32_t *dst = a.priv + gridDim.x * cells + blockIdx.x * a.dim;
+        uint32_t *dst = a.priv + blockIdx.x * (cells + a.dim) + cells;
         for (int64_t i = tid; i < a.dim; i += kScThreads) dst[i] = cnt[i];
     }
 }
 
-// Fold the nwg private copies of each output cell and store the result (no
-// atomics: each cell has one owner).  One wave per cell: lane l takes copies
-// l, l + 64, ... in order, then the lanes combine in a fixed tree, so the
-// fold order is fixed.  The MEAN counts are folded the same way, one wave per
-// output.
+// Folding the copies.  A workgroup's copy is one row of T columns: the
+// output cells (32-bit sums or 64-bit MIN/MAX words), then for MEAN the row
+// counts of the dim outputs.  With more than 64 copies, scatter_private_fold_a
+// first adds consecutive ranges of `per` copies into 64 partial rows or fewer
+// (one wave per 64 columns and range, lanes over consecutive columns, so the
+// loads are coalesced); scatter_private_fold_b then folds the remaining rows
+// of each cell (one wave per cell, lane l takes rows l, l + 64, ... in order,
+// then a fixed tree) and writes the final value: the sum, the mean, or the
+// unpacked MIN/MAX value and row.  Every order is fixed, so float sums repeat
+// bit for bit.
 template <int DT, int OP>
-__global__ __launch_bounds__(kScThreads) void scatter_private_fold(ScArgs a, int64_t nwg) {
+__device__ __forceinline__ uint32_t fold_add(uint32_t acc, uint32_t v, bool count_col) {
+    if constexpr (DT == DT_F32) {
+        if (!count_col) return __float_as_uint(__uint_as_float(acc) + __uint_as_float(v));
+    }
+    return acc + v;
+}
+
+template <int OP>
+__device__ __forceinline__ uint64_t fold_word(uint64_t acc, uint64_t v) {
+    return OP == OP_MAX ? (v > acc ? v : acc) : (v < acc ? v : acc);
+}
+
+template <int DT, int OP>
+__global__ __launch_bounds__(kScThreads) void scatter_private_fold_a(ScArgs a, int64_t nwg, int64_t T, int64_t per,
+                                                                     int64_t nparts, uint32_t *part) {
+    constexpr bool kWord = OP == OP_MIN || OP == OP_MAX;
+    const int lane = threadIdx.x & 63;
+    const int64_t cells = a.dim * a.F;
+    const int64_t cgroups = (T + 63) / 64;
+    const int64_t units = cgroups * nparts;
+    for (int64_t u = (int64_t)blockIdx.x * (kScThreads / 64) + (threadIdx.x >> 6); u < units;
+         u += (int64_t)gridDim.x * (kScThreads / 64)) {
+        const int64_t ch = u / cgroups;
+        const int64_t c = (u - ch * cgroups) * 64 + lane;
+        if (c >= T) continue;
+        const int64_t g0 = ch * per, g1 = g0 + per < nwg ? g0 + per : nwg;
+        if constexpr (kWord) {
+            const uint64_t *src = reinterpret_cast<const uint64_t *>(a.priv);
+            uint64_t acc = kEmptyWord<OP>;
+            for (int64_t g = g0; g < g1; ++g) acc = fold_word<OP>(acc, src[g * T + c]);
+            reinterpret_cast<uint64_t *>(part)[ch * T + c] = acc;
+        } else {
+            const bool count_col = c >= cells;
+            uint32_t acc = 0u;
+            for (int64_t g = g0; g < g1; ++g) acc = fold_add<DT, OP>(acc, a.priv[g * T + c], count_col);
+            part[ch * T + c] = acc;
+        }
+    }
+}
+
+template <int DT, int OP>
+__global__ __launch_bounds__(kScThreads) void scatter_private_fold_b(ScArgs a, const uint32_t *src, int64_t n,
+                                                                     int64_t T, int64_t *arg) {
     constexpr bool kWord = OP == OP_MIN || OP == OP_MAX;
     const int lane = threadIdx.x & 63;
     const int64_t cells = a.dim * a.F;
@@ -334,49 +382,41 @@ __global__ __launch_bounds__(kScThreads) void scatter_private_fold(ScArgs a, int
     const int64_t nwaves = (int64_t)gridDim.x * (kScThreads / 64);
     for (int64_t i = w; i < cells; i += nwaves) {
         if constexpr (kWord) {
-            const uint64_t *src = reinterpret_cast<const uint64_t *>(a.priv);
+            const uint64_t *s64 = reinterpret_cast<const uint64_t *>(src);
             uint64_t acc = kEmptyWord<OP>;
-            for (int64_t g = lane; g < nwg; g += 64) {
-                const uint64_t v = src[g * cells + i];
-                acc = OP == OP_MAX ? (v > acc ? v : acc) : (v < acc ? v : acc);
-            }
+            for (int64_t g = lane; g < n; g += 64) acc = fold_word<OP>(acc, s64[g * T + i]);
 #pragma unroll
             for (int o = 32; o >= 1; o >>= 1) {
                 const uint64_t v = lane_get(acc, (lane + o) & 63);
-                if (lane < o) acc = OP == OP_MAX ? (v > acc ? v : acc) : (v < acc ? v : acc);
+                if (lane < o) acc = fold_word<OP>(acc, v);
             }
-            if (lane == 0) a.words[i] = acc;
-        } else if constexpr (DT == DT_F32) {
-            float acc = 0.0f;
-            for (int64_t g = lane; g < nwg; g += 64) acc += __uint_as_float(a.priv[g * cells + i]);
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                const float v = lane_get(acc, (lane + o) & 63);
-                if (lane < o) acc += v;
+            if (lane == 0) {
+                const bool empty = acc == kEmptyWord<OP>;
+                const uint32_t code = (uint32_t)acc;
+                a.out[i] = empty ? 0u : okey_inv<DT>((uint32_t)(acc >> 32));
+                if (arg) arg[i] = empty ? -1 : (int64_t)(OP == OP_MAX ? ~code : code);
             }
-            if (lane == 0) a.out[i] = __float_as_uint(acc);
         } else {
             uint32_t acc = 0u;
-            for (int64_t g = lane; g < nwg; g += 64) acc += a.priv[g * cells + i];
+            for (int64_t g = lane; g < n; g += 64) acc = fold_add<DT, OP>(acc, src[g * T + i], false);
 #pragma unroll
             for (int o = 32; o >= 1; o >>= 1) {
                 const uint32_t v = lane_get(acc, (lane + o) & 63);
-                if (lane < o) acc += v;
+                if (lane < o) acc = fold_add<DT, OP>(acc, v, false);
             }
-            if (lane == 0) a.out[i] = acc;
-        }
-    }
-    if constexpr (OP == OP_MEAN) {
-        const uint32_t *src = a.priv + nwg * cells;
-        for (int64_t i = w; i < a.dim; i += nwaves) {
-            uint32_t n = 0u;
-            for (int64_t g = lane; g < nwg; g += 64) n += src[g * a.dim + i];
+            if constexpr (OP == OP_MEAN) {
+                const int64_t col = cells + i / a.F;
+                uint32_t cnt = 0u;
+                for (int64_t g = lane; g < n; g += 64) cnt += src[g * T + col];
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                const uint32_t v = lane_get(n, (lane + o) & 63);
-                if (lane < o) n += v;
+                for (int o = 32; o >= 1; o >>= 1) {
+                    const uint32_t v = lane_get(cnt, (lane + o) & 63);
+                    if (lane < o) cnt += v;
+                }
+                if (lane == 0) a.out[i] = cnt ? __float_as_uint(__uint_as_float(acc) / (float)cnt) : 0u;
+            } else {
+                if (lane == 0) a.out[i] = acc;
             }
-            if (lane == 0) a.counts[i] = n;
         }
     }
 }
@@ -556,13 +596,27 @@ int scatter_launch(const ScArgs &a, int64_t *arg, hipStream_t st) {
                                   st, nullptr, timing_stop(true), 0, a);
         }
         e = hipGetLastError();
+        const int64_t T = cells + (OP == OP_MEAN ? a.dim : 0);
+        const uint32_t *rows = a.priv;
+        int64_t n = a.priv_grid;
+        if (e == hipSuccess && n > 64) {
+            const int64_t per = (n + 63) / 64, nparts = (n + per - 1) / per;
+            const int64_t units = (T + 63) / 64 * nparts;
+            const unsigned ga = (unsigned)std::max<int64_t>(1, std::min<int64_t>((units + 3) / 4, 8192));
+            hipExtLaunchKernelGGL((scatter_private_fold_a<DT, OP>), dim3(ga), dim3(kScThreads), 0, st, nullptr,
+                                  timing_stop(false), 0, a, n, T, per, nparts, a.part);
+            e = hipGetLastError();
+            rows = a.part;
+            n = nparts;
+        }
         if (e == hipSuccess) {
             // one wave per output cell
             const unsigned fg = (unsigned)std::max<int64_t>(1, std::min<int64_t>((cells + 3) / 4, 8192));
-            hipExtLaunchKernelGGL((scatter_private_fold<DT, OP>), dim3(fg), dim3(kScThreads), 0, st, nullptr,
-                                  timing_stop(false), 0, a, a.priv_grid);
+            hipExtLaunchKernelGGL((scatter_private_fold_b<DT, OP>), dim3(fg), dim3(kScThreads), 0, st, nullptr,
+                                  timing_stop(false), 0, a, rows, n, T, arg);
             e = hipGetLastError();
         }
+        return e == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
     } else if (wgs > 0) {
         if (a.lg == 0)
             hipExtLaunchKernelGGL((scatter_kernel<DT, OP, true>), dim3((unsigned)wgs), dim3(kScThreads), 0, st,
@@ -631,12 +685,6 @@ extern "C" int segred_scatter_reduce(const void *values, int32_t dtype, int64_t 
     const int64_t cells = dim_size * feat;
     int64_t *arg = (op == SEGRED_MIN || op == SEGRED_MAX) ? arg_out : nullptr;
 
-    // MIN/MAX words live in arg_out when the caller gives it (8 bytes per
-    // cell, unpacked in place), else in scratch; MEAN counts in scratch.
-    size_t need = 0;
-    if ((op == SEGRED_MIN || op == SEGRED_MAX) && !arg) need = (size_t)cells * 8;
-    if (op == SEGRED_MEAN) need = (size_t)dim_size * 4;
-    need = (need + 255) & ~size_t(255);
     // Few outputs: private LDS copies when they fit and there are at least
     // 16 x 64 elements per output cell.  Grid: at most one workgroup per 8
     // elements per cell (the copies then add at most an eighth of the input
@@ -644,7 +692,7 @@ extern "C" int segred_scatter_reduce(const void *values, int32_t dtype, int64_t 
     // range of the element-atomic grid, and no more than fit the chip at once.
     const bool word_op = op == SEGRED_MIN || op == SEGRED_MAX;
     const int64_t count_bytes = op == SEGRED_MEAN ? dim_size * 4 : 0;
-    const int64_t priv_bytes = cells * (word_op ? 8 : 4) + count_bytes;
+    const int64_t priv_bytes = cells * (word_op ? 8 : 4) + count_bytes;  // one copy: T columns
     const int64_t elems = rows * feat;
     if (priv_bytes <= kPrivBytes && elems >= 16 * 64 * cells) {
         const bool waves = dtype == SEGRED_F32 && (op == SEGRED_SUM || op == SEGRED_MEAN) && lg >= 3 &&
@@ -656,14 +704,30 @@ extern "C" int segred_scatter_reduce(const void *values, int32_t dtype, int64_t 
         const int64_t resident = (int64_t)device_cus() * std::min<int64_t>(kWgPerCu, kLdsPerCu / a.priv_lds);
         a.priv_grid = std::max<int64_t>(1, std::min<int64_t>({wgs, elems / (8 * cells), resident}));
     }
-    const size_t priv_need = (size_t)(a.priv_grid * priv_bytes);
+
+    // The private path writes every output itself (its fold stores each
+    // cell).  The element-atomic path accumulates into zeroed outputs: MIN/MAX
+    // words live in arg_out when the caller gives it (8 bytes per cell,
+    // unpacked in place), else in scratch; MEAN counts in scratch.
+    size_t need = 0;
+    if (a.priv_grid == 0) {
+        if (word_op && !arg) need = (size_t)cells * 8;
+        if (op == SEGRED_MEAN) need = (size_t)dim_size * 4;
+    }
+    need = (need + 255) & ~size_t(255);
+    const size_t copies = (size_t)(a.priv_grid * priv_bytes);
+    const size_t parts = a.priv_grid > 64 ? (size_t)(64 * priv_bytes) : 0;
+    const size_t priv_need = copies + ((parts + 255) & ~size_t(255));
     ScratchLease scratch;
     if (need + priv_need > 0) {
         const int rc = scratch_acquire(scratch, need + priv_need, stream);
         if (rc != SEGRED_OK) return rc;
     }
-    if (priv_need > 0) a.priv = reinterpret_cast<uint32_t *>(static_cast<char *>(scratch.ptr) + need);
-    if (op == SEGRED_MIN || op == SEGRED_MAX) {
+    if (a.priv_grid > 0) {
+        char *base = static_cast<char *>(scratch.ptr) + need;
+        a.priv = reinterpret_cast<uint32_t *>(base);
+        a.part = reinterpret_cast<uint32_t *>(base + ((copies + 255) & ~size_t(255)));
+    } else if (word_op) {
         a.words = arg ? reinterpret_cast<uint64_t *>(arg) : static_cast<uint64_t *>(scratch.ptr);
         const uint64_t empty = op == SEGRED_MAX ? kEmptyWord<OP_MAX> : kEmptyWord<OP_MIN>;
         hipExtLaunchKernelGGL(scatter_init, dim3(fill_grid(cells)), dim3(kScThreads), 0, stream, nullptr,
