@@ -178,7 +178,7 @@ class ScatterWorkload(Workload):
 
     kernel_name = "scatter_kernel"
 
-    def __init__(self, cfg, ops, copies, sr, torch):
+    def __init__(self, cfg, ops, copies, sr, torch, private=False):
         self.sr, self.torch = sr, torch
         self.cfg = cfg
         self.host_vals, self.host_index, self.dim = cfg["f32"], cfg["index"], int(cfg["dim"])
@@ -190,8 +190,13 @@ class ScatterWorkload(Workload):
         self.sets = [(v, i)] + [(v.clone(), i.clone()) for _ in range(copies - 1)]
         self.vals = [x[0] for x in self.sets]
         self.calls = [(op, op) for op in ops]
-        # init + scatter (+ finish for min/max/mean; + a second init for mean)
-        self.kernels_per_step = sum({"sum": 2, "min": 3, "max": 3, "mean": 4}[op] for op in ops)
+        if private:
+            # few outputs: private-copy kernel and the two fold stages per call
+            self.kernel_name = "scatter_private"
+            self.kernels_per_step = 3 * len(ops)
+        else:
+            # init + scatter (+ finish for min/max/mean; + a second init for mean)
+            self.kernels_per_step = sum({"sum": 2, "min": 3, "max": 3, "mean": 4}[op] for op in ops)
         self.outs = {}
 
     def step(self, i):
@@ -391,7 +396,7 @@ def build_workload(name, sr, torch):
         cfg = W.scatter(feat=64 if name == "scatter" else 16, dim=100 if name == "scatter100" else 10_000)
         nbytes = cfg["f32"].nbytes + cfg["index"].nbytes
         copies = max(1, min(4, -(-4 * MALL_BYTES // nbytes)))
-        return ScatterWorkload(cfg, ["sum", "max"], copies, sr, torch), cfg
+        return ScatterWorkload(cfg, ["sum", "max"], copies, sr, torch, private=name == "scatter100"), cfg
     gen = {"small": W.small, "message": W.message, "skew": W.skew, "powerlaw": W.powerlaw}[name]
     cfg = gen()
     ops = {"small": ["sum", "min", "max", "mean"], "message": ["sum", "max"], "skew": ["sum", "min"],

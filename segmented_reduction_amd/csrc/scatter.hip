@@ -191,6 +191,7 @@ __global__ __launch_bounds__(kScThreads) void scatter_kernel(ScArgs a) {
 constexpr int kPrivBytes = 32768;
 constexpr int kLdsPerCu = 163840;  // 160 KB of LDS per compute unit
 constexpr int kWgPerCu = 8;        // 32 waves per CU in workgroups of 4 waves
+constexpr int kPrivSteps = 8;      // wave steps whose loads are issued together
 
 //
 // WAVES (float sums with rows of >= 8 features): each wave keeps a copy of
@@ -223,13 +224,13 @@ __global__ __launch_bounds__(kScThreads) void scatter_private(ScArgs a) {
     const int lg = a.lg;
     const int64_t G = 64 >> lg;
     const int sub = lane & ((1 << lg) - 1);
-    const int64_t stride = (int64_t)gridDim.x * (kScThreads / 64) * kScSteps * G;
-    for (int64_t qbase = ((int64_t)blockIdx.x * (kScThreads / 64) + (tid >> 6)) * kScSteps * G; qbase < a.items;
+    const int64_t stride = (int64_t)gridDim.x * (kScThreads / 64) * kPrivSteps * G;
+    for (int64_t qbase = ((int64_t)blockIdx.x * (kScThreads / 64) + (tid >> 6)) * kPrivSteps * G; qbase < a.items;
          qbase += stride) {
-        int64_t s[kScSteps], fe[kScSteps], row[kScSteps];
-        uint32_t x[kScSteps];
+        int64_t s[kPrivSteps], fe[kPrivSteps], row[kPrivSteps];
+        uint32_t x[kPrivSteps];
 #pragma unroll
-        for (int u = 0; u < kScSteps; ++u) {
+        for (int u = 0; u < kPrivSteps; ++u) {
             int64_t q = qbase + u * G + (lane >> lg);
             int64_t r = q, f = sub;
             if (a.chunks > 1) {
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(kScThreads) void scatter_private(ScArgs a) {
             uint32_t *mine = c32 + (tid >> 6) * cells;
             const int grp = lane >> lg;
 #pragma unroll
-            for (int u = 0; u < kScSteps; ++u) {
+            for (int u = 0; u < kPrivSteps; ++u) {
                 const bool act = s[u] >= 0 && s[u] < a.dim;
                 const int64_t cell = s[u] * a.F + fe[u];
                 for (int gg = 0; gg < (int)G; ++gg) {
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(kScThreads) void scatter_private(ScArgs a) {
             continue;
         }
 #pragma unroll
-        for (int u = 0; u < kScSteps; ++u) {
+        for (int u = 0; u < kPrivSteps; ++u) {
             if (s[u] < 0 || s[u] >= a.dim) continue;
             const int64_t cell = s[u] * a.F + fe[u];
             if constexpr (OP == OP_MAX) {
@@ -358,15 +359,33 @@ __global__ __launch_bounds__(kScThreads) void scatter_private_fold_a(ScArgs a, i
         const int64_t c = (u - ch * cgroups) * 64 + lane;
         if (c >= T) continue;
         const int64_t g0 = ch * per, g1 = g0 + per < nwg ? g0 + per : nwg;
+        // loads in batches of 8 ahead of the in-order combine
+        constexpr int kB = 8;
         if constexpr (kWord) {
             const uint64_t *src = reinterpret_cast<const uint64_t *>(a.priv);
             uint64_t acc = kEmptyWord<OP>;
-            for (int64_t g = g0; g < g1; ++g) acc = fold_word<OP>(acc, src[g * T + c]);
+            int64_t g = g0;
+            for (; g + kB <= g1; g += kB) {
+                uint64_t v[kB];
+#pragma unroll
+                for (int k = 0; k < kB; ++k) v[k] = src[(g + k) * T + c];
+#pragma unroll
+                for (int k = 0; k < kB; ++k) acc = fold_word<OP>(acc, v[k]);
+            }
+            for (; g < g1; ++g) acc = fold_word<OP>(acc, src[g * T + c]);
             reinterpret_cast<uint64_t *>(part)[ch * T + c] = acc;
         } else {
             const bool count_col = c >= cells;
             uint32_t acc = 0u;
-            for (int64_t g = g0; g < g1; ++g) acc = fold_add<DT, OP>(acc, a.priv[g * T + c], count_col);
+            int64_t g = g0;
+            for (; g + kB <= g1; g += kB) {
+                uint32_t v[kB];
+#pragma unroll
+                for (int k = 0; k < kB; ++k) v[k] = a.priv[(g + k) * T + c];
+#pragma unroll
+                for (int k = 0; k < kB; ++k) acc = fold_add<DT, OP>(acc, v[k], count_col);
+            }
+            for (; g < g1; ++g) acc = fold_add<DT, OP>(acc, a.priv[g * T + c], count_col);
             part[ch * T + c] = acc;
         }
     }
@@ -686,23 +705,28 @@ extern "C" int segred_scatter_reduce(const void *values, int32_t dtype, int64_t 
     int64_t *arg = (op == SEGRED_MIN || op == SEGRED_MAX) ? arg_out : nullptr;
 
     // Few outputs: private LDS copies when they fit and there are at least
-    // 16 x 64 elements per output cell.  Grid: at most one workgroup per 8
-    // elements per cell (the copies then add at most an eighth of the input
-    // bytes, written once and read once by the fold), at most one per item
-    // range of the element-atomic grid, and no more than fit the chip at once.
+    // 128 elements per output cell.  Float sums of >= 8 features take it
+    // only with one copy per wave: their LDS float atomics run at a fixed
+    // rate below that of global atomics spread over thousands of cells.
+    // Grid: one workgroup per CU at least, more while the copies stay under
+    // an eighth of the input bytes (they are written once and read once by
+    // the fold), at most one per item range of the element-atomic grid and
+    // no more than fit the chip at once.
     const bool word_op = op == SEGRED_MIN || op == SEGRED_MAX;
     const int64_t count_bytes = op == SEGRED_MEAN ? dim_size * 4 : 0;
     const int64_t priv_bytes = cells * (word_op ? 8 : 4) + count_bytes;  // one copy: T columns
     const int64_t elems = rows * feat;
-    if (priv_bytes <= kPrivBytes && elems >= 16 * 64 * cells) {
-        const bool waves = dtype == SEGRED_F32 && (op == SEGRED_SUM || op == SEGRED_MEAN) && lg >= 3 &&
-                           cells * 4 * (kScThreads / 64) + count_bytes <= kPrivBytes;
+    const bool float_sum = dtype == SEGRED_F32 && (op == SEGRED_SUM || op == SEGRED_MEAN);
+    const bool waves = float_sum && lg >= 3 && cells * 4 * (kScThreads / 64) + count_bytes <= kPrivBytes;
+    if (priv_bytes <= kPrivBytes && elems >= 128 * cells && (waves || !float_sum || lg < 3)) {
         a.priv_waves = waves ? 1 : 0;
         a.priv_lds = (int)(waves ? cells * 4 * (kScThreads / 64) + count_bytes : priv_bytes);
         const int64_t per_wave = (int64_t)kScSteps * (64 >> lg);
         const int64_t wgs = ((a.items + per_wave - 1) / per_wave + kScThreads / 64 - 1) / (kScThreads / 64);
-        const int64_t resident = (int64_t)device_cus() * std::min<int64_t>(kWgPerCu, kLdsPerCu / a.priv_lds);
-        a.priv_grid = std::max<int64_t>(1, std::min<int64_t>({wgs, elems / (8 * cells), resident}));
+        const int64_t cus = device_cus();
+        const int64_t resident = cus * std::min<int64_t>(kWgPerCu, kLdsPerCu / a.priv_lds);
+        a.priv_grid = std::max<int64_t>(
+            1, std::min<int64_t>({wgs, resident, std::max<int64_t>(cus, elems / (8 * cells))}));
     }
 
     // The private path writes every output itself (its fold stores each
