@@ -207,13 +207,17 @@ def test_scatter_repeatability():
 # ---------------------------------------------------------------- few outputs (private LDS copies)
 
 PRIVATE = [
-    # (seed, rows, dim, feat, order, out_of_range): at least 1,024 elements per output cell
+    # (seed, rows, dim, feat, order, out_of_range): many elements per output cell
     (51, 120_000, 1, 1, "random", 0.0),
     (52, 150_000, 100, 1, "random", 0.1),
     (53, 200_000, 7, 3, "runs", 0.02),
     (54, 110_000, 100, 8, "random", 0.0),
     (55, 105_000, 60, 16, "sorted", 0.05),
     (56, 70_000, 3, 100, "random", 0.0),
+    # >= 128 elements per cell, at least one workgroup per CU
+    (57, 200_000, 1000, 1, "sorted", 0.0),
+    (58, 300_000, 1000, 4, "random", 0.05),
+    (59, 600_000, 500, 8, "runs", 0.0),  # float sums: global atomics (no per-wave copies); others private
 ]
 
 
