@@ -268,7 +268,7 @@ class SearchWorkload(Workload):
     """Lower-bound queries over segmented sorted float32 values, one search
     call per step (galloping search with the page's defaults)."""
 
-    kernel_name = "gallop_kernel"
+    kernel_name = "gallop_staged"
 
     def __init__(self, cfg, copies, sr, torch):
         self.sr, self.torch, self.cfg = sr, torch, cfg

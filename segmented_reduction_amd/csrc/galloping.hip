@@ -13,6 +13,17 @@
 // forward from the previous answer, then a bounded search, then a linear
 // scan once at most 16 values remain.
 //
+// Two kernels compute those answers.  When a record has at most 256 tiles
+// (ceil(max_query_count / T) <= 256), gallop_staged gives each record a
+// workgroup: a record of at most 4,096 values is copied into LDS once, and
+// each thread answers whole queries (consecutive threads on consecutive
+// queries) by a binary search in LDS, so every memory access is coalesced
+// and no probe leaves the CU.  A lower bound is the same whichever search
+// finds it, so the tile rules are kept query by query (bit 4 below); only a
+// record with a non-finite query goes tile by tile, since such a query ends
+// its tile.  Otherwise gallop_kernel runs one lane per (record, tile) with
+// the page's steps below.
+//
 // For gfx950 each of those steps issues its probes together instead of one
 // after another, because a probe is a memory round trip: the gallop loads
 // the 16 values after the previous answer (one 64-byte run) and 6
@@ -99,11 +110,26 @@ struct Probe {
     }
 };
 
+// A record's values staged in LDS: search position p is s_vals[p - vo].
+constexpr int kStageValues = 4096;  // 16 KB per workgroup
+
+template <int DT>
+struct LdsProbe {
+    const uint32_t *vals;
+    int64_t vo;
+    __device__ __forceinline__ uint32_t at(int64_t p) const { return vals[p - vo]; }
+    __device__ __forceinline__ void window16(int64_t a, int64_t end, uint32_t (&w)[16]) const {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) w[j] = a + j < end ? vals[a + j - vo] : 0u;
+    }
+    static __device__ __forceinline__ bool less(uint32_t v, uint32_t q) { return Probe<DT, false>::less(v, q); }
+};
+
 // Lower bound of q in [lo, hi), knowing every position before lo is below q
 // and (when hi is not the segment end) position hi is not.  16-way rounds
 // while more than 16 positions remain, then one round over the rest.
-template <int DT, bool ORDER>
-__device__ __forceinline__ int64_t bounded(const Probe<DT, ORDER> &pr, int64_t lo, int64_t hi, uint32_t q) {
+template <class P>
+__device__ __forceinline__ int64_t bounded(const P &pr, int64_t lo, int64_t hi, uint32_t q) {
     while (hi - lo > 16) {
         const int64_t n = hi - lo;
         int64_t pos[15];
@@ -117,7 +143,7 @@ __device__ __forceinline__ int64_t bounded(const Probe<DT, ORDER> &pr, int64_t l
 #pragma unroll
         for (int j = 0; j < 15; ++j) {
             if (!found) {
-                if (Probe<DT, ORDER>::less(v[j], q)) {
+                if (P::less(v[j], q)) {
                     nlo = pos[j] + 1;
                 } else {
                     nhi = pos[j];
@@ -135,7 +161,7 @@ __device__ __forceinline__ int64_t bounded(const Probe<DT, ORDER> &pr, int64_t l
     int64_t lb = hi;
 #pragma unroll
     for (int j = 15; j >= 0; --j)
-        if (lo + j < hi && !Probe<DT, ORDER>::less(v[j], q)) lb = lo + j;
+        if (lo + j < hi && !P::less(v[j], q)) lb = lo + j;
     return lb;
 }
 
@@ -146,9 +172,8 @@ __device__ __forceinline__ int64_t bounded(const Probe<DT, ORDER> &pr, int64_t l
 // so a wave waits for its slowest lane: every query should cost the same few
 // rounds).  If all are below q, the next round starts at a+1024 with a
 // window and probes 64 times coarser.  A bracket is finished by `bounded`.
-template <int DT, bool ORDER>
-__device__ __forceinline__ int64_t gallop(const Probe<DT, ORDER> &pr, int64_t a, int64_t end, uint32_t q,
-                                          bool wide) {
+template <class P>
+__device__ __forceinline__ int64_t gallop(const P &pr, int64_t a, int64_t end, uint32_t q, bool wide) {
     int64_t base = a;
     int64_t scale = 1;
     for (;;) {
@@ -176,7 +201,7 @@ __device__ __forceinline__ int64_t gallop(const Probe<DT, ORDER> &pr, int64_t a,
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 if (base + j >= end) return end;
-                if (!Probe<DT, ORDER>::less(w[j], q)) return base + j;
+                if (!P::less(w[j], q)) return base + j;
             }
         } else {
             // sparse window: bracket the answer between two samples (or
@@ -186,7 +211,7 @@ __device__ __forceinline__ int64_t gallop(const Probe<DT, ORDER> &pr, int64_t a,
             for (int j = 0; j < 16; ++j) {
                 const int64_t p = base + j * scale;
                 if (p >= end) return bounded(pr, prev + 1, end, q);
-                if (!Probe<DT, ORDER>::less(w[j], q)) return bounded(pr, prev + 1, p, q);
+                if (!P::less(w[j], q)) return bounded(pr, prev + 1, p, q);
                 prev = p;
             }
         }
@@ -197,7 +222,7 @@ __device__ __forceinline__ int64_t gallop(const Probe<DT, ORDER> &pr, int64_t a,
         for (int i = 0; i < 6; ++i) {
             const int64_t p = base + ((int64_t)32 << i) * scale - 1;
             if (p >= end) return bounded(pr, prev + 1, end, q);
-            if (!Probe<DT, ORDER>::less(e[i], q)) return bounded(pr, prev + 1, p, q);
+            if (!P::less(e[i], q)) return bounded(pr, prev + 1, p, q);
             prev = p;
         }
         base = prev + 1;
@@ -205,29 +230,11 @@ __device__ __forceinline__ int64_t gallop(const Probe<DT, ORDER> &pr, int64_t a,
     }
 }
 
-template <int DT, bool ORDER>
-__global__ __launch_bounds__(kGThreads) void gallop_kernel(const GArgs a) {
-    const int64_t id = (int64_t)blockIdx.x * kGThreads + threadIdx.x;
-    const int64_t s = id / a.tiles, t = id - s * a.tiles;
-    if (s >= a.S) return;
-    const int64_t vo = a.segments[4 * s + 0], vc = a.segments[4 * s + 1];
-    const int64_t qo = a.segments[4 * s + 2], qc = a.segments[4 * s + 3];
-    const int64_t view = ORDER ? a.order_count : a.value_count;
-    const bool bad_v = vo < 0 || vc < 0 || vo > view || vc > view - vo;
-    const bool bad_q = qo < 0 || qc < 0 || qo > a.query_count || qc > a.query_count - qo || qc > a.max_qc;
+// Queries k0 .. k1-1 of a record (one tile): returns the validation bits.
+template <int DT, class P>
+__device__ __forceinline__ uint32_t search_tile(const GArgs &a, const P &pr, int64_t vo, int64_t end, int64_t qo,
+                                                int64_t k0, int64_t k1) {
     uint32_t bits = 0;
-    if (bad_v || bad_q) {
-        if (t == 0) {
-            bits = (bad_v ? 1u : 0u) | (bad_q ? 2u : 0u);
-            __hip_atomic_fetch_or(a.validation, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        return;
-    }
-    const int64_t k0 = t * a.T;
-    if (k0 >= qc) return;
-    const int64_t k1 = min(k0 + a.T, qc);
-    const Probe<DT, ORDER> pr{a.values, a.order, a.value_count, a.stride};
-    const int64_t end = vo + vc;
     int64_t lb = vo;
     uint32_t prevq = 0;
     uint32_t qn = a.queries[qo + k0];
@@ -245,7 +252,7 @@ __global__ __launch_bounds__(kGThreads) void gallop_kernel(const GArgs a) {
             break;  // the rest of the tile is not written
         }
         bool full = k == k0;
-        if (!full && Probe<DT, ORDER>::less(q, prevq)) {
+        if (!full && P::less(q, prevq)) {
             bits |= 4u;
             full = true;
         }
@@ -264,15 +271,186 @@ __global__ __launch_bounds__(kGThreads) void gallop_kernel(const GArgs a) {
 #pragma unroll
     for (int j = 0; j < 3; ++j)
         if (j < nheld) a.out[qo + k - nheld + j] = held[j];
+    return bits;
+}
+
+// Lower bound of q over a whole record: a plain binary search in LDS (one
+// read per step; the waves resident on a CU hide its latency), the 16-way
+// rounds of `bounded` through memory.
+template <int DT>
+__device__ __forceinline__ int64_t record_lower_bound(const LdsProbe<DT> &pr, int64_t vo, int64_t end, uint32_t q) {
+    uint32_t lo = 0, n = (uint32_t)(end - vo);  // at most kStageValues
+    while (n > 0) {
+        const uint32_t half = n >> 1;
+        if (LdsProbe<DT>::less(pr.vals[lo + half], q)) {
+            lo += half + 1;
+            n -= half + 1;
+        } else {
+            n = half;
+        }
+    }
+    return vo + lo;
+}
+
+template <int DT, bool ORDER>
+__device__ __forceinline__ int64_t record_lower_bound(const Probe<DT, ORDER> &pr, int64_t vo, int64_t end,
+                                                      uint32_t q) {
+    return bounded(pr, vo, end, q);
+}
+
+// Every query of a record, consecutive threads on consecutive queries
+// (coalesced loads and stores): a search of the whole record each, bit 4 for
+// a query below its predecessor in the same tile.
+template <int DT, class P>
+__device__ __forceinline__ uint32_t answer_queries(const GArgs &a, const P &pr, int64_t vo, int64_t end, int64_t qo,
+                                                   int64_t qc) {
+    uint32_t bits = 0;
+    auto query = [&](int64_t k) __attribute__((always_inline)) { return a.queries[qo + k]; };
+    // position of query k in its tile, stepped along with k
+    const int64_t step = kGThreads % a.T;
+    int64_t in_tile = (int64_t)threadIdx.x % a.T;
+    for (int64_t k = threadIdx.x; k < qc; k += kGThreads) {
+        const uint32_t q = query(k);
+        if (in_tile != 0 && P::less(q, query(k - 1))) bits |= 4u;
+        a.out[qo + k] = record_lower_bound<DT>(pr, vo, end, q);
+        in_tile += step;
+        if (in_tile >= a.T) in_tile -= a.T;
+    }
+    return bits;
+}
+
+// A record with a non-finite query: one lane per tile, queries in order; a
+// non-finite query sets bit 8 and ends its tile (it and the rest are not
+// written), a query below its predecessor sets bit 4.  Each answer is the
+// same whole-record lower bound.
+template <int DT, class P>
+__device__ __forceinline__ uint32_t answer_tiles(const GArgs &a, const P &pr, int64_t vo, int64_t end, int64_t qo,
+                                                 int64_t qc) {
+    uint32_t bits = 0;
+    const int64_t ntiles = (qc + a.T - 1) / a.T;
+    for (int64_t t = threadIdx.x; t < ntiles; t += kGThreads) {
+        const int64_t k0 = t * a.T, k1 = min(k0 + a.T, qc);
+        uint32_t prevq = 0;
+        for (int64_t k = k0; k < k1; ++k) {
+            const uint32_t q = a.queries[qo + k];
+            if (DT == DT_F32 && !isfinite(__uint_as_float(q))) {
+                bits |= 8u;
+                break;
+            }
+            if (k != k0 && P::less(q, prevq)) bits |= 4u;
+            a.out[qo + k] = record_lower_bound<DT>(pr, vo, end, q);
+            prevq = q;
+        }
+    }
+    return bits;
+}
+
+// Record checks (bits 1 and 2); true when the record may be searched.
+__device__ __forceinline__ bool record_ok(const GArgs &a, bool order, int64_t vo, int64_t vc, int64_t qo, int64_t qc,
+                                          uint32_t &bits) {
+    const int64_t view = order ? a.order_count : a.value_count;
+    const bool bad_v = vo < 0 || vc < 0 || vo > view || vc > view - vo;
+    const bool bad_q = qo < 0 || qc < 0 || qo > a.query_count || qc > a.query_count - qo || qc > a.max_qc;
+    bits = (bad_v ? 1u : 0u) | (bad_q ? 2u : 0u);
+    return bits == 0;
+}
+
+// One lane per (record, tile): for records with more tiles than a workgroup
+// has lanes.
+template <int DT, bool ORDER>
+__global__ __launch_bounds__(kGThreads) void gallop_kernel(const GArgs a) {
+    const int64_t id = (int64_t)blockIdx.x * kGThreads + threadIdx.x;
+    const int64_t s = id / a.tiles, t = id - s * a.tiles;
+    if (s >= a.S) return;
+    const int64_t vo = a.segments[4 * s + 0], vc = a.segments[4 * s + 1];
+    const int64_t qo = a.segments[4 * s + 2], qc = a.segments[4 * s + 3];
+    uint32_t bits = 0;
+    if (!record_ok(a, ORDER, vo, vc, qo, qc, bits)) {
+        if (t == 0) __hip_atomic_fetch_or(a.validation, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    const int64_t k0 = t * a.T;
+    if (k0 >= qc) return;
+    const Probe<DT, ORDER> pr{a.values, a.order, a.value_count, a.stride};
+    bits = search_tile<DT>(a, pr, vo, vo + vc, qo, k0, min(k0 + a.T, qc));
+    if (bits) __hip_atomic_fetch_or(a.validation, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One workgroup per record.  A record of at most kStageValues values and at
+// most 64 values per query is first copied into LDS (coalesced loads,
+// once); then each thread answers whole queries, consecutive threads on
+// consecutive queries, so query loads and answer stores are coalesced, and
+// every probe is an LDS read.  The answers are the lower bounds, the same
+// whatever search finds them; the tile rules still hold query by query: a
+// query below its predecessor in the same tile sets bit 4.  A record with a
+// non-finite float32 query (bit 8: the rest of its tile is not written) and
+// every record that is not staged go tile by tile, one lane per tile.
+template <int DT, bool ORDER>
+__global__ __launch_bounds__(kGThreads) void gallop_staged(const GArgs a) {
+    __shared__ uint32_t s_vals[kStageValues];
+    const int64_t s = blockIdx.x;
+    const int64_t vo = a.segments[4 * s + 0], vc = a.segments[4 * s + 1];
+    const int64_t qo = a.segments[4 * s + 2], qc = a.segments[4 * s + 3];
+    uint32_t bits = 0;
+    if (!record_ok(a, ORDER, vo, vc, qo, qc, bits)) {
+        if (threadIdx.x == 0) __hip_atomic_fetch_or(a.validation, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    const Probe<DT, ORDER> pr{a.values, a.order, a.value_count, a.stride};
+    const int64_t end = vo + vc;
+    const bool stage = vc <= kStageValues;  // the same for the whole workgroup
+    // every load of the staging (and of the non-finite check of the first
+    // kStageValues queries) issued before the first LDS store
+    constexpr int kPer = kStageValues / kGThreads;
+    uint32_t v[kPer], w[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int64_t i = u * kGThreads + threadIdx.x;
+        v[u] = stage && i < vc ? pr.at(vo + i) : 0u;
+        w[u] = i < qc ? a.queries[qo + i] : 0u;
+    }
+    bool nonfinite = false;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int64_t i = u * kGThreads + threadIdx.x;
+        if (stage && i < vc) s_vals[i] = v[u];
+        if constexpr (DT == DT_F32) nonfinite |= i < qc && !isfinite(__uint_as_float(w[u]));
+    }
+    if constexpr (DT == DT_F32)
+        for (int64_t k = kStageValues + threadIdx.x; k < qc; k += kGThreads)
+            nonfinite |= !isfinite(__uint_as_float(a.queries[qo + k]));
+    const bool by_tile = __syncthreads_or(nonfinite) != 0;  // also orders the LDS stores before the searches
+    if (!by_tile) {
+        if (stage)
+            bits |= answer_queries<DT>(a, LdsProbe<DT>{s_vals, vo}, vo, end, qo, qc);
+        else
+            bits |= answer_queries<DT>(a, pr, vo, end, qo, qc);
+    } else {
+        if (stage)
+            bits |= answer_tiles<DT>(a, LdsProbe<DT>{s_vals, vo}, vo, end, qo, qc);
+        else
+            bits |= answer_tiles<DT>(a, pr, vo, end, qo, qc);
+    }
     if (bits) __hip_atomic_fetch_or(a.validation, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int DT>
 static int gallop_launch(const GArgs &a, hipStream_t st) {
+    if (a.S == 0) return SEGRED_OK;
+    if (a.tiles <= kGThreads) {
+        // a workgroup per record (its tiles fit the workgroup's lanes)
+        if (a.S > INT32_MAX) return SEGRED_ERR_UNSUPPORTED;
+        if (a.order)
+            hipExtLaunchKernelGGL((gallop_staged<DT, true>), dim3((unsigned)a.S), dim3(kGThreads), 0, st, nullptr,
+                                  timing_stop(true), 0, a);
+        else
+            hipExtLaunchKernelGGL((gallop_staged<DT, false>), dim3((unsigned)a.S), dim3(kGThreads), 0, st, nullptr,
+                                  timing_stop(true), 0, a);
+        return hipGetLastError() == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
+    }
     const int64_t lanes = a.S * a.tiles;
     const int64_t wgs = (lanes + kGThreads - 1) / kGThreads;
     if (wgs > INT32_MAX) return SEGRED_ERR_UNSUPPORTED;
-    if (wgs == 0) return SEGRED_OK;
     if (a.order)
         hipExtLaunchKernelGGL((gallop_kernel<DT, true>), dim3((unsigned)wgs), dim3(kGThreads), 0, st, nullptr,
                               timing_stop(true), 0, a);

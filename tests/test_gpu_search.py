@@ -111,6 +111,25 @@ def test_decreasing_and_nonfinite_in_bulk():
     _check(stored, qs, seg, what="bulk diagnostics", tile=8)
 
 
+def test_many_queries_per_record():
+    """Records with more queries than one staging batch (4,096): answered
+    query by query, and with a NaN past that batch, tile by tile (the NaN's
+    tile stops there, bit 8)."""
+    rng = np.random.default_rng(31)
+    v = np.sort(rng.standard_normal(3000)).astype(np.float32)
+    q = np.concatenate([np.sort(rng.standard_normal(6000) * 1.2), np.sort(rng.standard_normal(4500))]).astype(np.float32)
+    seg = np.array([[0, 3000, 0, 6000], [100, 2500, 6000, 4500]])  # query ranges must not overlap
+    _check(v, q, seg, what="many queries", tile=32)
+    q2 = q.copy()
+    q2[4600] = np.nan
+    q2[6000 + 4200] = np.inf
+    _check(v, q2, seg, what="many queries, NaN past the batch", tile=32)
+    vu = np.sort(rng.integers(0, 2 ** 32, 5000, dtype=np.uint64)).astype(np.uint32)
+    qu = np.sort(rng.integers(0, 2 ** 32, 9000, dtype=np.uint64)).astype(np.uint32)
+    _check(vu, qu, np.array([[0, 5000, 0, 9000], [7, 4000, 9000, 0]]), what="many queries u32, 5,000 values",
+           tile=64)
+
+
 def test_search_config_full_size():
     """The bench's workload at full size: every answer satisfies the lower
     bound property on the sorted segments (any size), and 96 sampled segments
