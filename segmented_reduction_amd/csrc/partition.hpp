@@ -12,7 +12,12 @@
 namespace segred {
 
 // Item d is preceded by i(d) = max{ i in [0, S] : key(i) <= d } segment ends,
-// key(i) = offsets[i] - o0 + i (strictly increasing in i).  The four waves
+// key(i) = offsets[i] - o0 + CW * i (strictly increasing in i).  CW is the
+// weight of a segment end in rows: with CW = 1 every row and every end is
+// one item; a larger CW counts an end as CW items (an end costs more than a
+// row when rows are single values), and a diagonal that falls inside an
+// end's weight is moved back to just before that end (the end goes to the
+// next share), so shares still split the merged sequence at valid points.  The four waves
 // of a workgroup own four consecutive shares, so their five boundary
 // diagonals lie close together and the workgroup searches for them jointly:
 //   round A: 1024 evenly spaced offsets (the same for every workgroup, so
@@ -33,7 +38,8 @@ namespace segred {
 // [d0, d1), i.e. segment ends [i0, i1) and rows [j0, j1) (rows relative to
 // offsets[0]).
 struct Share {
-    int64_t o0, D, d0, d1, i0, j0, i1, j1;
+    int64_t o0, D, d0, d1, i0, j0, i1, j1;  // D in weighted items; d0 = i0 + j0, d1 = i1 + j1 (unweighted)
+    int64_t cw;                             // weight of a segment end
     int64_t first_row; // first row of segment i0 (relative to offsets[0])
     int64_t tail_row;  // first row of segment i1 (relative to offsets[0])
     bool split_head;   // segment i0 ends in the share but began in an earlier one
@@ -50,7 +56,7 @@ template <int N>
 __device__ __forceinline__ int64_t probe_pos(int k, int64_t lo, int64_t step, int64_t hi) {
     return k == N - 1 ? hi : min(lo + (int64_t)k * step, hi);
 }
-template <int N>
+template <int N, int CW = 1>
 __device__ __forceinline__ Bracket bracket(const int64_t *s, int64_t lo, int64_t step, int64_t hi, int64_t o0,
                                            int64_t d, int lane) {
     constexpr int U = N / 64;
@@ -59,7 +65,7 @@ __device__ __forceinline__ Bracket bracket(const int64_t *s, int64_t lo, int64_t
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int k = u * 64 + lane;
-        kk[u] = s[k] - o0 + probe_pos<N>(k, lo, step, hi);
+        kk[u] = s[k] - o0 + CW * probe_pos<N>(k, lo, step, hi);
         cnt += popc64(ballot(kk[u] <= d));
     }
     // cnt >= 1: probe 0 has key <= d
@@ -88,10 +94,11 @@ constexpr int kProbesA = 1024, kProbesB = 64;
 // segments are rarely cut; it is a function of d alone, so the two shares
 // on either side of a boundary agree on it, and it keeps the boundaries in
 // order.
-template <bool SNAP = false>
+template <bool SNAP = false, int CW = 1>
 __device__ __forceinline__ Share find_share(const int64_t *off, int64_t S, int64_t NW, int64_t wave, int lane,
                                             int64_t *s_probe /* LDS [kProbesA], workgroup-wide */,
                                             int64_t min_share = 1) {
+    static_assert(!(SNAP && CW != 1), "snapping is defined for unit weights");
     const int tid = threadIdx.x;
     const int wid = tid >> 6;
     const int64_t blk = wave >> 2;  // the workgroup's four shares are 4 * blk .. 4 * blk + 3
@@ -105,14 +112,14 @@ __device__ __forceinline__ Share find_share(const int64_t *off, int64_t S, int64
     }
     __syncthreads();
     const int64_t o0 = s_probe[0];
-    const int64_t T = (s_probe[kProbesA - 1] - o0) + S;
+    const int64_t T = (s_probe[kProbesA - 1] - o0) + CW * S;
     // Shares of at least min_share items: small inputs use fewer waves (the
     // rest get empty shares and only write their header).
     const int64_t D = max((T + NW - 1) / NW, min_share);
     const int64_t g0 = min(blk * 4 * D, T), g4 = min((blk * 4 + 4) * D, T);
     const int64_t d0 = min((blk * 4 + wid) * D, T), d1 = min(d0 + D, T);
-    const Bracket a0 = bracket<kProbesA>(s_probe, 0, stepA, S, o0, g0, lane);
-    const Bracket a4 = bracket<kProbesA>(s_probe, 0, stepA, S, o0, g4, lane);
+    const Bracket a0 = bracket<kProbesA, CW>(s_probe, 0, stepA, S, o0, g0, lane);
+    const Bracket a4 = bracket<kProbesA, CW>(s_probe, 0, stepA, S, o0, g4, lane);
     __syncthreads();  // every wave is done with round A
 
     // Round B over [L, H], which holds i(d) for every diagonal of the group.
@@ -120,8 +127,8 @@ __device__ __forceinline__ Share find_share(const int64_t *off, int64_t S, int64
     const int64_t stepB = max((H - L + kProbesB - 2) / (kProbesB - 1), (int64_t)1);
     if (tid < kProbesB) s_probe[tid] = off[probe_pos<kProbesB>(tid, L, stepB, H)];
     __syncthreads();
-    Bracket b0 = bracket<kProbesB>(s_probe, L, stepB, H, o0, d0, lane);
-    Bracket b1 = bracket<kProbesB>(s_probe, L, stepB, H, o0, d1, lane);
+    Bracket b0 = bracket<kProbesB, CW>(s_probe, L, stepB, H, o0, d0, lane);
+    Bracket b1 = bracket<kProbesB, CW>(s_probe, L, stepB, H, o0, d1, lane);
     __syncthreads();  // the probe array is free from here on
 
     // Round C: 256-way rounds on both diagonals of this wave.
@@ -138,8 +145,8 @@ __device__ __forceinline__ Share find_share(const int64_t *off, int64_t S, int64
             ok0[u] = lo0 < hi0 && p0 <= hi0;
             ok1[u] = lo1 < hi1 && p1 <= hi1;
             const int64_t q0 = min(p0, S), q1 = min(p1, S);
-            k0[u] = off[q0] - o0 + q0;
-            k1[u] = off[q1] - o0 + q1;
+            k0[u] = off[q0] - o0 + CW * q0;
+            k1[u] = off[q1] - o0 + CW * q1;
         }
         int n0 = 0, n1 = 0;
 #pragma unroll
@@ -195,20 +202,29 @@ __device__ __forceinline__ Share find_share(const int64_t *off, int64_t S, int64
         lo1 = ii1;
         k1lo = kk1;
     }
+    // rows before each boundary; a weighted diagonal inside an end's weight
+    // stops at the last row of that end's segment
+    int64_t r0 = e0 - CW * lo0, r1 = e1 - CW * lo1;
+    if constexpr (CW != 1) {
+        const int64_t n0 = off[min(lo0 + 1, S)] - o0, n1 = off[min(lo1 + 1, S)] - o0;
+        if (lo0 < S) r0 = min(r0, n0);
+        if (lo1 < S) r1 = min(r1, n1);
+    }
     // Everything here is the same in every lane; saying so lets the compiler
     // keep it in scalar registers (and build uniform buffer descriptors).
     Share sh;
+    sh.cw = CW;
     sh.o0 = readfirst(o0);
     sh.D = readfirst(D);
-    sh.d0 = readfirst(e0);
-    sh.d1 = readfirst(e1);
     sh.i0 = readfirst(lo0);
-    sh.j0 = sh.d0 - sh.i0;
+    sh.j0 = readfirst(r0);
+    sh.d0 = sh.i0 + sh.j0;
     sh.i1 = readfirst(lo1);
-    sh.j1 = sh.d1 - sh.i1;
-    sh.first_row = readfirst(k0lo) - sh.i0;  // offsets[i0] - o0
+    sh.j1 = readfirst(r1);
+    sh.d1 = sh.i1 + sh.j1;
+    sh.first_row = readfirst(k0lo) - CW * sh.i0;  // offsets[i0] - o0
     sh.split_head = sh.i0 < sh.i1 && sh.first_row < sh.j0;
-    sh.tail_row = readfirst(k1lo) - sh.i1;  // offsets[i1] - o0
+    sh.tail_row = readfirst(k1lo) - CW * sh.i1;  // offsets[i1] - o0
     sh.has_tail = sh.i1 < S && sh.tail_row < sh.j1;
     return sh;
 }
