@@ -230,7 +230,8 @@ __device__ __forceinline__ int64_t gallop(const P &pr, int64_t a, int64_t end, u
     }
 }
 
-// Queries k0 .. k1-1 of a record (one tile): returns the validation bits.
+// Queries k0 .. k1-1 of a record (one tile), the page's steps: returns the
+// validation bits.  Used by gallop_kernel.
 template <int DT, class P>
 __device__ __forceinline__ uint32_t search_tile(const GArgs &a, const P &pr, int64_t vo, int64_t end, int64_t qo,
                                                 int64_t k0, int64_t k1) {
@@ -305,13 +306,13 @@ template <int DT, class P>
 __device__ __forceinline__ uint32_t answer_queries(const GArgs &a, const P &pr, int64_t vo, int64_t end, int64_t qo,
                                                    int64_t qc) {
     uint32_t bits = 0;
-    auto query = [&](int64_t k) __attribute__((always_inline)) { return a.queries[qo + k]; };
+    const uint32_t *qs = a.queries + qo;
     // position of query k in its tile, stepped along with k
     const int64_t step = kGThreads % a.T;
     int64_t in_tile = (int64_t)threadIdx.x % a.T;
     for (int64_t k = threadIdx.x; k < qc; k += kGThreads) {
-        const uint32_t q = query(k);
-        if (in_tile != 0 && P::less(q, query(k - 1))) bits |= 4u;
+        const uint32_t q = qs[k];
+        if (in_tile != 0 && P::less(q, qs[k - 1])) bits |= 4u;
         a.out[qo + k] = record_lower_bound<DT>(pr, vo, end, q);
         in_tile += step;
         if (in_tile >= a.T) in_tile -= a.T;
@@ -376,15 +377,15 @@ __global__ __launch_bounds__(kGThreads) void gallop_kernel(const GArgs a) {
     if (bits) __hip_atomic_fetch_or(a.validation, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One workgroup per record.  A record of at most kStageValues values and at
-// most 64 values per query is first copied into LDS (coalesced loads,
-// once); then each thread answers whole queries, consecutive threads on
-// consecutive queries, so query loads and answer stores are coalesced, and
-// every probe is an LDS read.  The answers are the lower bounds, the same
-// whatever search finds them; the tile rules still hold query by query: a
-// query below its predecessor in the same tile sets bit 4.  A record with a
-// non-finite float32 query (bit 8: the rest of its tile is not written) and
-// every record that is not staged go tile by tile, one lane per tile.
+// One workgroup per record.  A record of at most kStageValues values is
+// first copied into LDS (coalesced loads, once); then each thread answers
+// whole queries, consecutive threads on consecutive queries, so query loads
+// and answer stores are coalesced, and every probe is an LDS read (a larger
+// record is searched through memory, query by query).  The answers are the
+// lower bounds, the same whatever search finds them; the tile rules still
+// hold query by query: a query below its predecessor in the same tile sets
+// bit 4.  A record with a non-finite float32 query (bit 8: the rest of its
+// tile is not written) goes tile by tile, one lane per tile.
 template <int DT, bool ORDER>
 __global__ __launch_bounds__(kGThreads) void gallop_staged(const GArgs a) {
     __shared__ uint32_t s_vals[kStageValues];
