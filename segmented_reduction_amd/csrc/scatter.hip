@@ -24,13 +24,16 @@
 // two neighbours share an index), so a sorted or clustered index sends one
 // atomic per run rather than one per row.
 //
-// With few outputs (they fit 32 KB of LDS) and many rows per output, each
-// workgroup accumulates into a private LDS copy, stores it to its own
-// scratch slot, and a fold kernel combines the copies in a fixed order with
-// plain stores (scatter_private, scatter_private_fold).  Sums of rows with
-// >= 2 features use one copy per wave and no atomics at all, so they repeat
-// bit for bit; 1-D sums and min/max use LDS atomics (min/max are exact
-// anyway).
+// With few outputs (one copy fits 32 KB of LDS) and at least 128 rows x
+// features per output cell, each workgroup accumulates into a private LDS
+// copy, stores it to its own scratch slot, and two fold kernels combine the
+// copies in a fixed order with plain stores and write the final values
+// (scatter_private, scatter_private_fold_a/_b).  Float sums of rows with
+// >= 8 features use one copy per wave and no atomics at all, so they repeat
+// bit for bit; float sums of wider rows whose wave copies do not fit stay on
+// the element-atomic path (LDS float atomics are slower than global ones
+// spread over many cells); other sums and min/max use LDS atomics (integer
+// sums and min/max are exact in any order).
 //
 // Rows whose index lies outside [0, dim_size) are skipped: they take part in
 // no output (and no memory outside the outputs is touched for them).
@@ -293,7 +296,7 @@ __global__ __launch_bounds__(kScThreads) void scatter_private(ScArgs a) {
     __syncthreads();
     // the workgroup's copy goes to its own scratch slot with plain stores
     // (global atomics from every workgroup into the same few outputs would
-    // serialise at the memory side); scatter_private_fold combines them
+    // serialise at the memory side); scatter_private_fold_a/_b combine them
     if constexpr (kWord) {
         uint64_t *dst = reinterpret_cast<uint64_t *>(a.priv) + blockIdx.x * cells;
         for (int64_t i = tid; i < cells; i += kScThreads) dst[i] = c64[i];
