@@ -217,17 +217,26 @@ int segred_reduce_device_count(const void *values, int32_t dtype, int64_t feat,
  *              element is written.  An output no row reaches gets 0.
  *              Integer SUM wraps modulo 2^32 and is exact; MIN/MAX use the
  *              same order as segred_reduce and are exact.  Float SUM and MEAN
- *              are float32 atomic additions in arrival order: the result can
- *              differ in its last bits from run to run (error at most
- *              (n - 1) * 2^-24 * sum|x| for an output of n rows, to first
- *              order; MEAN adds one rounding of the division).  Use
- *              segred_reduce on destination-sorted rows for a reproducible
- *              sum.
+ *              are float32 additions (error at most (n - 1) * 2^-24 *
+ *              sum|x| for an output of n rows, to first order, in any order;
+ *              MEAN adds one rounding of the division).  They add in arrival
+ *              order, so the last bits can differ from run to run, except on
+ *              the few-output path with feat >= 8 (below), which adds in a
+ *              fixed order.  Use segred_reduce on destination-sorted rows for
+ *              a reproducible sum in every case.
  *   arg_out    int64 [dim_size, feat] or NULL; MIN/MAX only: the row that
  *              produced the value, the lowest such row on ties, -1 for an
  *              output no row reaches.  When given, it also serves as the
  *              call's working memory for the packed words.
  *   stream     HIP stream the work is ordered on.
+ *
+ * Paths: with many outputs, one global atomic per element (as in "Method").
+ * When one copy of the outputs fits 32 KB (4 or 8 bytes per cell, plus 4 per
+ * output for MEAN) and there are at least 128 rows x features per cell,
+ * each workgroup reduces its rows into a private copy in LDS and the copies
+ * are folded in a fixed order; float SUM/MEAN with feat >= 8 take this path
+ * only when one copy per wave fits (4 copies).  That path keeps up to one
+ * 32 KB copy per resident workgroup in the stream's scratch (tens of MB).
  *
  * Errors: SEGRED_ERR_INVALID_ARGUMENT for rows < 0, dim_size < 0, feat < 1,
  * an unknown dtype or op, a NULL values/index with rows > 0 or out with
@@ -381,8 +390,8 @@ int64_t segred_get_shares(int32_t dtype, int32_t op, int64_t feat);
  * kernel the library launches carries a HIP event that the runtime stamps
  * when that kernel ends (hipExtLaunchKernel).  segred_timing_read waits for
  * the recorded events and reports, for every streaming kernel (the first
- * kernel of a segred_reduce call, both kernels of segred_scan, the atomic
- * kernel of segred_scatter_reduce, the search kernel of
+ * kernel of a segred_reduce call, both kernels of segred_scan, the atomic or
+ * private-copy kernel of segred_scatter_reduce, the search kernel of
  * segred_galloping_search,
  * the histogram of segred_offsets_from_index, the counting and materialising
  * kernels of segred_offsets_from_rle / segred_unique /
