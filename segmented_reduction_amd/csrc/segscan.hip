@@ -98,12 +98,16 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int idx) {
 // past it; bit 1: that segment starts inside the share.
 constexpr int kRec = 8;
 
+// The shares are sized by the main kernel's occupancy (up to 8 waves per
+// SIMD); the tails kernel is held to the same (64 registers, smaller load
+// batches) so that all its shares run in one round rather than two.
 template <int DT, int OP, int L>
-__global__ __launch_bounds__(256) void seg_scan_tails(const ScanArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8)))
+void seg_scan_tails(const ScanArgs a) {
     using O = ScanOp<DT, OP>;
     using acc_t = typename O::acc_t;
     constexpr int G = 64 / L;
-    constexpr int U = L == 1 ? 8 : 32;
+    constexpr int U = L == 1 ? 4 : 16;
     __shared__ int64_t s_probe[kProbesA];
     const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t sblocks = a.NW / 4;
