@@ -7,11 +7,13 @@
 // offsets[r] = start, lengths[r] = next start - start, offsets[count] = n.
 //
 // Three launches, no atomics: (1) each tile of 4096 keys counts its run
-// starts and notes its first one; (2) one workgroup scans the tile counts
-// (run index of each tile's first start) and the first starts from the right
-// (the start that follows each tile); (3) each tile ranks its starts in
-// position order through LDS and writes values, offsets and lengths with
-// consecutive lanes on consecutive runs.
+// starts, notes its first one and stores its start bits (one 64-bit ballot
+// per wave and step, 512 bytes per tile); (2) one workgroup scans the tile
+// counts (run index of each tile's first start) and the first starts from
+// the right (the start that follows each tile); (3) each tile ranks its
+// starts in position order from the stored bits (the keys are not read
+// again) and writes values, offsets and lengths with consecutive lanes on
+// consecutive runs, loading a key only where a run starts.
 //
 // The same three launches serve two relatives, chosen by a mode: the
 // distinct adjacent values alone (same page, "GPUUnique": RLE's equality and
@@ -82,9 +84,15 @@ __device__ __forceinline__ void load_tile(const uint32_t *keys, int64_t n, int64
     }
 }
 
+// Start bits of a tile: word (u, w) = the ballot of wave w at step u
+// (bit l: position tile_start + u * 256 + w * 64 + l starts a run).
+__device__ __forceinline__ int64_t mask_word(int64_t tile, int u, int w) {
+    return (tile * kRleKeysPerThread + u) * 4 + w;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kRleThreads) void rle_count(const uint32_t *keys, int64_t n, int64_t *tile_count,
-                                                         int64_t *tile_first) {
+                                                         int64_t *tile_first, uint64_t *tile_mask) {
     __shared__ int64_t s_cnt[4];
     __shared__ int64_t s_first[4];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -92,12 +100,15 @@ __global__ __launch_bounds__(kRleThreads) void rle_count(const uint32_t *keys, i
     TileKeys t;
     load_tile<MODE>(keys, n, start, tid, t);
     int64_t cnt = 0, first = INT64_MAX;
+    uint64_t mine = 0;  // lane u keeps step u's ballot
 #pragma unroll
     for (int u = 0; u < kRleKeysPerThread; ++u) {
         const uint64_t m = ballot(t.head[u]);
         cnt += popc64(m);
         if (m && first == INT64_MAX) first = start + u * kRleThreads + wid * 64 + (int)__builtin_ctzll(m);
+        if (lane == u) mine = m;
     }
+    if (lane < kRleKeysPerThread) tile_mask[mask_word(blockIdx.x, lane, wid)] = mine;
     if (lane == 0) {
         s_cnt[wid] = cnt;
         s_first[wid] = first;
@@ -210,19 +221,19 @@ __global__ __launch_bounds__(kScanThreads) void rle_scan(int64_t tiles, int64_t 
 template <int MODE>
 __global__ __launch_bounds__(kRleThreads) void rle_materialize(const uint32_t *keys, int64_t n,
                                                                const int64_t *tile_base, const int64_t *tile_next,
-                                                               uint32_t *values, uint32_t *lengths,
-                                                               int64_t *offsets) {
+                                                               const uint64_t *tile_mask, uint32_t *values,
+                                                               uint32_t *lengths, int64_t *offsets) {
     __shared__ uint32_t s_pos[kRleTile];
-    __shared__ uint32_t s_key[kRleTile];
     __shared__ int s_wc[kRleKeysPerThread][4];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int64_t start = (int64_t)blockIdx.x * kRleTile;
-    TileKeys t;
-    load_tile<MODE>(keys, n, start, tid, t);
     uint64_t m[kRleKeysPerThread];
+    bool head[kRleKeysPerThread];
+#pragma unroll
+    for (int u = 0; u < kRleKeysPerThread; ++u) m[u] = tile_mask[mask_word(blockIdx.x, u, wid)];
 #pragma unroll
     for (int u = 0; u < kRleKeysPerThread; ++u) {
-        m[u] = ballot(t.head[u]);
+        head[u] = (m[u] >> lane) & 1ull;
         if (lane == 0) s_wc[u][wid] = popc64(m[u]);
     }
     __syncthreads();
@@ -236,10 +247,9 @@ __global__ __launch_bounds__(kRleThreads) void rle_materialize(const uint32_t *k
             before += w < wid ? s_wc[u][w] : 0;
             all += s_wc[u][w];
         }
-        if (t.head[u]) {
+        if (head[u]) {
             const int rank = base + before + popc64(m[u] & below);
             s_pos[rank] = (uint32_t)(u * kRleThreads + tid);
-            s_key[rank] = t.k[u];
         }
         base += all;
     }
@@ -249,7 +259,7 @@ __global__ __launch_bounds__(kRleThreads) void rle_materialize(const uint32_t *k
     const int64_t next = MODE == MODE_RLE ? tile_next[blockIdx.x] : 0;
     for (int q = tid; q < cnt; q += kRleThreads) {
         const int64_t pos = start + s_pos[q];
-        if (MODE != MODE_FLAGS) values[rb + q] = s_key[q];
+        if (MODE != MODE_FLAGS) values[rb + q] = keys[pos];
         if (MODE != MODE_UNIQUE) offsets[rb + q] = pos;
         if (MODE == MODE_RLE) {
             const int64_t npos = q + 1 < cnt ? start + s_pos[q + 1] : next;
@@ -270,22 +280,24 @@ int rle_launch(const uint32_t *keys, int64_t n, uint32_t *values, uint32_t *leng
                int64_t *count, hipStream_t stream) {
     const int64_t tiles = (n + kRleTile - 1) / kRleTile;
     ScratchLease scratch;
-    int rc = scratch_acquire(scratch, (size_t)std::max<int64_t>(tiles, 1) * 4 * sizeof(int64_t), stream);
+    const size_t words = (size_t)std::max<int64_t>(tiles, 1) * (4 + kRleKeysPerThread * 4);
+    int rc = scratch_acquire(scratch, words * sizeof(int64_t), stream);
     if (rc != SEGRED_OK) return rc;
     int64_t *tcount = static_cast<int64_t *>(scratch.ptr);
     int64_t *tfirst = tcount + tiles;
     int64_t *tbase = tfirst + tiles;
     int64_t *tnext = tbase + tiles;
+    uint64_t *tmask = reinterpret_cast<uint64_t *>(tnext + tiles);  // [tiles][16][4] start bits
 
     if (tiles > 0)
         hipExtLaunchKernelGGL(rle_count<MODE>, dim3((unsigned)tiles), dim3(kRleThreads), 0, stream, nullptr,
-                              timing_stop(true), 0, keys, n, tcount, tfirst);
+                              timing_stop(true), 0, keys, n, tcount, tfirst, tmask);
     hipExtLaunchKernelGGL(rle_scan<MODE>, dim3(1), dim3(kScanThreads), 0, stream, nullptr, timing_stop(false), 0,
                           tiles, n, (const int64_t *)tcount, (const int64_t *)tfirst, tbase, tnext, count, offsets);
     if (tiles > 0)
         hipExtLaunchKernelGGL(rle_materialize<MODE>, dim3((unsigned)tiles), dim3(kRleThreads), 0, stream, nullptr,
-                              timing_stop(true), 0, keys, n, (const int64_t *)tbase, (const int64_t *)tnext, values,
-                              lengths, offsets);
+                              timing_stop(true), 0, keys, n, (const int64_t *)tbase, (const int64_t *)tnext,
+                              (const uint64_t *)tmask, values, lengths, offsets);
     return hipGetLastError() == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
 }
 
