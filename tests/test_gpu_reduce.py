@@ -244,3 +244,26 @@ def test_one_dimensional_chunk_edges(kind):
             gu.say(f"chunk edges kind={kind} op={op} shares={shares}")
             out, arg = gu.run_gpu(vals, off, op, shares=shares)
             gu.assert_parity(vals, off, op, out, arg, orc=orc, what=f"chunk edges shares={shares}")
+
+
+@pytest.mark.parametrize("kind", ["i32", "f32"])
+def test_one_dimensional_weighted_shares(kind):
+    """The 1-D kernel weighs a segment end as 8 rows in its shares: share
+    boundaries then fall inside long stretches of empty segments (each is 8
+    items with no rows), inside stretches of one-row segments and inside long
+    segments, and each must stop at a point of the merged sequence.  Many
+    share counts move the boundaries across all three."""
+    rng = np.random.default_rng(91)
+    lengths = np.concatenate([
+        [50_000], np.zeros(40_000, np.int64), [3], np.ones(30_000, np.int64), np.zeros(7, np.int64),
+        rng.integers(0, 4, 20_000), [120_000], np.zeros(25_000, np.int64), rng.integers(1, 60, 2_000)])
+    off = np.concatenate([[5], 5 + np.cumsum(lengths)]).astype(np.int64)  # offsets[0] > 0
+    rows = int(off[-1])
+    vals = {"f32": rng.standard_normal(rows, dtype=np.float32),
+            "i32": rng.integers(-1000, 1000, rows, dtype=np.int32)}[kind]
+    for op in ("sum", "min", "max"):
+        orc = oracle.reduce(vals, off, op)
+        for shares in (None, 4, 36, 412, 4096):
+            gu.say(f"weighted shares kind={kind} op={op} shares={shares}")
+            out, arg = gu.run_gpu(vals, off, op, shares=shares)
+            gu.assert_parity(vals, off, op, out, arg, orc=orc, what=f"weighted shares={shares}")
