@@ -157,3 +157,20 @@ def test_search_config_full_size():
         want, word = oracle.lower_bounds(v[a:a + n], q[b:b + m], sub, max_qc=cfg["max_query_count"],
                                          tile=cfg["queries_per_tile"])
         assert word == 0 and np.array_equal(out[b:b + m] - a, want), s
+
+
+def test_tile_extremes_in_the_staged_kernel():
+    """One query per tile (T = 1): a query below the previous one is in a new
+    tile, so no bit 4; one tile for the whole record (T >= qc): it is bit 4.
+    Both with a record count small enough for the per-record kernel
+    (max_query_count / T <= 256)."""
+    rng = np.random.default_rng(41)
+    v = np.sort(rng.standard_normal(3000)).astype(np.float32)
+    q = np.sort(rng.standard_normal(200))[::-1].astype(np.float32).copy()  # decreasing
+    seg = np.array([[0, 3000, 0, 100], [500, 2000, 100, 100]])
+    _check(v, q, seg, what="T=1, decreasing", tile=1, max_qc=200)
+    _check(v, q, seg, what="T=qc, decreasing", tile=100)
+    _check(v, q, seg, what="T>qc, decreasing", tile=100_000)
+    qs = q.copy()
+    qs[37] = np.nan
+    _check(v, qs, seg, what="T=7 with a NaN", tile=7)
