@@ -218,6 +218,10 @@ PRIVATE = [
     (57, 200_000, 1000, 1, "sorted", 0.0),
     (58, 300_000, 1000, 4, "random", 0.05),
     (59, 600_000, 500, 8, "runs", 0.0),  # float sums: global atomics (no per-wave copies); others private
+    # just eligible, a grid of one or a few workgroups (no first fold stage)
+    (61, 200, 1, 1, "random", 0.0),
+    (62, 1_200, 2, 3, "sorted", 0.1),
+    (63, 3_000, 1, 9, "random", 0.0),
 ]
 
 
