@@ -1,5 +1,8 @@
 """Build the HIP library libsegred.so for gfx950 with hipcc (in-tree).
 
+Each source is compiled to an object of its own (in parallel), then the
+objects are linked into one shared library.
+
 Usage:  python -m segmented_reduction_amd.build_lib
 """
 from __future__ import annotations
@@ -8,12 +11,14 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(HERE, "_lib")
+OBJ_DIR = os.path.join(LIB_DIR, "obj")
 LIB = os.path.join(LIB_DIR, "libsegred.so")
 SOURCES = ["api.hip", "reduce.hip", "rle.hip", "scatter.hip", "segscan.hip", "galloping.hip"]
 ARCH = os.environ.get("SEGRED_OFFLOAD_ARCH", "gfx950")
@@ -32,7 +37,6 @@ def flags() -> list[str]:
         "-O3",
         "-std=c++17",
         "-fPIC",
-        "-shared",
         "-Wall",
         # keep the compiler from forming packed fp32 instructions
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -41,16 +45,26 @@ def flags() -> list[str]:
     ]
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(LIB_DIR, exist_ok=True)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *flags(), *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _run(cmd: list[str], verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         sys.stderr.write(proc.stdout + proc.stderr)
-        raise RuntimeError("hipcc failed to build libsegred.so")
+        raise RuntimeError(f"hipcc failed: {' '.join(cmd[-3:])}")
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    cc = hipcc()
+    objs = [os.path.join(OBJ_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    cmds = [[cc, *flags(), "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(max_workers=jobs) as pool:
+        for f in [pool.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -58,7 +58,7 @@ __device__ __forceinline__ void load_tile(const uint32_t *keys, int64_t n, int64
         // a start is a nonzero flag: no neighbour is needed
         const auto rf = make_rsrc(keys + start, (uint32_t)(avail * 4));
 #pragma unroll
-        for (int u = 0; u < kRleKeysPerThread; ++u) t.k[u] = ld32(rf, (uint32_t)((u * kRleThreads + tid) * 4), 0);
+        for (int u = 0; u < kRleKeysPerThread; ++u) t.k[u] = ld32(rf, (uint32_t)((u * kRleThreads + tid) * 4));
 #pragma unroll
         for (int u = 0; u < kRleKeysPerThread; ++u)
             t.head[u] = start + u * kRleThreads + tid < n && t.k[u] != 0u;
@@ -70,8 +70,8 @@ __device__ __forceinline__ void load_tile(const uint32_t *keys, int64_t n, int64
     uint32_t p0[kRleKeysPerThread];
 #pragma unroll
     for (int u = 0; u < kRleKeysPerThread; ++u) {
-        t.k[u] = ld32(rs, (uint32_t)((u * kRleThreads + tid) * 4), 0);
-        p0[u] = ld32(rp, (uint32_t)((u * kRleThreads + wid * 64 - 1 + (int)back) * 4), 0);
+        t.k[u] = ld32(rs, (uint32_t)((u * kRleThreads + tid) * 4));
+        p0[u] = ld32(rp, (uint32_t)((u * kRleThreads + wid * 64 - 1 + (int)back) * 4));
     }
 #pragma unroll
     for (int u = 0; u < kRleKeysPerThread; ++u) {

@@ -141,7 +141,7 @@ void seg_scan_tails(const ScanArgs a) {
             const int64_t n = max((int64_t)0, min(E, sh.j1 - rb));
             const auto rs = make_rsrc(a.values + sh.o0 + rb, (uint32_t)(n * 4));
 #pragma unroll
-            for (int u = 0; u < U; ++u) q[u] = ld128(rs, (uint32_t)(lane * 16), (uint32_t)(u * 1024));
+            for (int u = 0; u < U; ++u) q[u] = ld128(rs, (uint32_t)(lane * 16 + u * 1024));
         };
         auto add = [&](int64_t rb, const uint4 (&q)[U]) __attribute__((always_inline)) {
             const int64_t n = min(E, sh.j1 - rb);
@@ -172,7 +172,7 @@ void seg_scan_tails(const ScanArgs a) {
                                       n > 0 ? (uint32_t)(n * a.F - chunk * 64) * 4u : 0u);
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                x[u] = ld32(rs, (uint32_t)((g * a.F + c) * 4), (uint32_t)u * (uint32_t)G * row_bytes);
+                x[u] = ld32(rs, (uint32_t)((g * a.F + c) * 4) + (uint32_t)u * (uint32_t)G * row_bytes);
         };
         auto add = [&](int64_t rb, const uint32_t (&x)[U]) __attribute__((always_inline)) {
 #pragma unroll
@@ -281,13 +281,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void s
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if constexpr (V == 4) {
-                const uint4 q = ld128(rin, (uint32_t)(lane * 16), (uint32_t)(u * SR * 4));
+                const uint4 q = ld128(rin, (uint32_t)(lane * 16 + u * SR * 4));
                 x[u][0] = q.x;
                 x[u][1] = q.y;
                 x[u][2] = q.z;
                 x[u][3] = q.w;
             } else {
-                x[u][0] = ld32(rin, (uint32_t)((g * a.F + c) * 4), (uint32_t)u * (uint32_t)G * row_bytes);
+                x[u][0] = ld32(rin, (uint32_t)((g * a.F + c) * 4) + (uint32_t)u * (uint32_t)G * row_bytes);
             }
         }
     };
@@ -366,16 +366,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void s
                 if (rb + SR <= j1) {
                     typedef uint32_t v4u __attribute__((ext_vector_type(4)));
                     const v4u d = {ob[0], ob[1], ob[2], ob[3]};
-                    __builtin_amdgcn_raw_buffer_store_b128(d, rout, (int)(lane * 16), (int)so, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(d, rout, (int)(lane * 16 + so), 0, 0);
                 } else {
 #pragma unroll
                     for (int v = 0; v < V; ++v)
-                        __builtin_amdgcn_raw_buffer_store_b32(ob[v], rout, (int)(lane * 16 + v * 4), (int)so, 0);
+                        __builtin_amdgcn_raw_buffer_store_b32(ob[v], rout, (int)(lane * 16 + v * 4 + so), 0, 0);
                 }
             } else {
                 if (fv)
-                    __builtin_amdgcn_raw_buffer_store_b32(ob[0], rout, (int)((g * a.F + c) * 4),
-                                                          (int)((uint32_t)u * (uint32_t)G * row_bytes), 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        ob[0], rout, (int)((uint32_t)((g * a.F + c) * 4) + (uint32_t)u * (uint32_t)G * row_bytes), 0, 0);
             }
         }
     };

@@ -56,22 +56,32 @@ __device__ __forceinline__ int64_t readfirst(int64_t v) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Raw buffer access: a descriptor over [base, base + bytes); a load whose
-// byte offset (lane offset + scalar offset) is at or past `bytes` returns 0
-// without touching memory, so a descriptor limited to the valid part of an
-// array makes clamping unnecessary.  Descriptor word 3 is the gfx9-family
-// raw 32-bit layout.
+// Raw buffer access: a descriptor over [base, base + bytes).  A load whose
+// lane offset (the VGPR offset plus the instruction's immediate offset) is at
+// or past `bytes` returns 0 without touching memory, so a descriptor limited
+// to the valid part of an array makes clamping unnecessary.  The scalar
+// offset field (soffset) is added to the address but is not part of that
+// range check on raw (stride 0) buffers, so every step through an array is
+// put into the lane offset and soffset is always 0.  Descriptor word 3 is the
+// gfx9-family raw 32-bit layout.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ uint32_t ld32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+
+// Cache policy of the streaming loads: non-temporal (nt).  Every element is
+// read once, so nothing is gained by keeping it in the caches; with the hint
+// a plain streaming read of 2 GiB ran at 6.7-7.0 TB/s on MI355X against
+// 5.6-6.1 TB/s without it, for dword and dwordx4 loads alike.
+constexpr int kStreamPolicy = 2;
+
+__device__ __forceinline__ uint32_t ld32(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, kStreamPolicy);
 }
 
-__device__ __forceinline__ uint4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+__device__ __forceinline__ uint4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
     // Range checking is per dword: a 16-byte unit cut by the limit returns its
     // in-range dwords and zeros for the rest.
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, kStreamPolicy);
     return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
 }
 
