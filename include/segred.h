@@ -60,11 +60,13 @@ enum segred_status {
  *   op            SEGRED_SUM, SEGRED_MIN, SEGRED_MAX or SEGRED_MEAN.
  *   out           [S, feat] of the input type (float32 for MEAN).
  *                 SUM of u32/i32 wraps modulo 2^32.  SUM and MEAN of f32 are
- *                 accumulated in a fixed order, so results are bitwise
- *                 identical run to run on a given device: in float64 and
- *                 rounded to float32 once, except that 1-D inputs (feat = 1)
- *                 add runs of at most 32 consecutive elements and a 64-way
- *                 tree of such runs in float32 first (error below
+ *                 accumulated in an order fixed by the offsets alone (the
+ *                 work partition is a constant of the library, not of the
+ *                 device), so results are bitwise identical from run to run
+ *                 and from device to device: in float64 and rounded to
+ *                 float32 once, except that 1-D inputs (feat = 1) add runs
+ *                 of at most 32 consecutive elements and a 64-way tree of
+ *                 such runs in float32 first (error below
  *                 38 * 2^-24 * sum|x| in all).  MIN/MAX order u32 unsigned, i32 signed,
  *                 f32 by the monotone bit key (so -0.0 < +0.0 and NaNs sort
  *                 past +-inf by their bits); `out` holds the element's bits.
@@ -73,6 +75,10 @@ enum segred_status {
  *                 the absolute row of the extremum, the lowest such row on
  *                 ties, -1 for an empty segment.
  *   stream        HIP stream the work is ordered on.
+ *
+ * Rows whose width is a multiple of 4 features are read and written 16
+ * bytes per lane when values, out and arg_out start on 16-byte boundaries;
+ * other rows one element per lane.  Results are the same either way.
  *
  * Errors: SEGRED_ERR_INVALID_ARGUMENT for S < 0, feat < 1, an unknown dtype
  * or op, a NULL values/offsets/out with S > 0, values/out not 4-byte aligned,
@@ -367,46 +373,6 @@ int segred_galloping_search(const void *values, int32_t dtype, int64_t value_cou
 
 /* Static, host-side description of a status code (never NULL). */
 const char *segred_status_string(int status);
-
-/*
- * Work partition of segred_reduce (a tuning and testing knob, not part of the
- * method).  The rows and segment ends of a call are split into `shares`
- * equal parts of the merged (rows + segment ends) sequence, one per wave of
- * the streaming kernel; segments cut by a part boundary are finished by a
- * second, fixed-order combine kernel.  0 restores the default.  The float
- * summation order, and so the last bits of float sums, depend on this value;
- * integer, min/max and arg results do not.  Applies to calls made after it
- * returns; process-wide.  The count is rounded up to a multiple of 4 (whole
- * workgroups).  Returns SEGRED_ERR_INVALID_ARGUMENT unless shares == 0 or
- * 1 <= shares <= 2^22.
- */
-int segred_set_shares(int64_t shares);
-
-/* The share count (after rounding) segred_reduce uses for this dtype/op/feat. */
-int64_t segred_get_shares(int32_t dtype, int32_t op, int64_t feat);
-
-/*
- * Kernel timing (instrumentation for benchmarks).  While enabled, every
- * kernel the library launches carries a HIP event that the runtime stamps
- * when that kernel ends (hipExtLaunchKernel).  segred_timing_read waits for
- * the recorded events and reports, for every streaming kernel (the first
- * kernel of a segred_reduce call, both kernels of segred_scan, the atomic or
- * private-copy kernel of segred_scatter_reduce, the search kernel of
- * segred_galloping_search,
- * the histogram of segred_offsets_from_index, the counting and materialising
- * kernels of segred_offsets_from_rle / segred_unique /
- * segred_offsets_from_flags), the time from the end of the launch recorded
- * before it to its own end (-1 for the first launch of the record):
- * when the library's kernels run back to back on one stream (nothing else
- * queued in between), this is the streaming kernel's execution time.  It
- * returns the summed duration of the timed launches in milliseconds and the
- * number of streaming launches, writes the first `capacity` durations (ms,
- * in launch order) to the host array `each_ms` (may be NULL when capacity is
- * 0), and clears the record.  Up to 8192 launches are kept;
- * later ones are not timed.  Host-side state, process-wide, not thread-safe.
- */
-int segred_timing_enable(int enable);
-int segred_timing_read(double *total_ms, int64_t *launches, float *each_ms, int64_t capacity);
 
 #ifdef __cplusplus
 }

@@ -81,6 +81,8 @@ def library(path: str | None = None):
             lib.segred_set_shares.restype = ctypes.c_int
             lib.segred_get_shares.argtypes = [i32, i32, i64]
             lib.segred_get_shares.restype = i64
+            lib.segred_resident_waves.argtypes = [i32, i32, i64]
+            lib.segred_resident_waves.restype = i64
             lib.segred_timing_enable.argtypes = [ctypes.c_int]
             lib.segred_timing_enable.restype = ctypes.c_int
             lib.segred_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64),

@@ -9,6 +9,7 @@
 #include <mutex>
 
 #include "segred.h"
+#include "segred_instrument.h"
 
 namespace segred {
 

@@ -86,7 +86,8 @@ constexpr int kProbesA = 1024, kProbesB = 64;
 
 //
 // `wave` is the share index (4 * share block + wave in the workgroup); every
-// wave of the workgroup must call this together (it synchronises).
+// wave of the workgroup must call this together (it synchronises).  `gran`
+// rounds the share size up to a multiple of itself (see D below).
 //
 // SNAP moves each share boundary d onto the nearer edge of the block of the
 // segment it falls in (block i = segment i's rows and its end item, items
@@ -97,7 +98,7 @@ constexpr int kProbesA = 1024, kProbesB = 64;
 template <bool SNAP = false, int CW = 1>
 __device__ __forceinline__ Share find_share(const int64_t *off, int64_t S, int64_t NW, int64_t wave, int lane,
                                             int64_t *s_probe /* LDS [kProbesA], workgroup-wide */,
-                                            int64_t min_share = 1) {
+                                            int64_t min_share = 1, int64_t gran = 1) {
     static_assert(!(SNAP && CW != 1), "snapping is defined for unit weights");
     const int tid = threadIdx.x;
     const int wid = tid >> 6;
@@ -114,8 +115,12 @@ __device__ __forceinline__ Share find_share(const int64_t *off, int64_t S, int64
     const int64_t o0 = s_probe[0];
     const int64_t T = (s_probe[kProbesA - 1] - o0) + CW * S;
     // Shares of at least min_share items: small inputs use fewer waves (the
-    // rest get empty shares and only write their header).
-    const int64_t D = max((T + NW - 1) / NW, min_share);
+    // rest get empty shares and only write their header).  A share is a
+    // whole number of granules of `gran` items, so that a wave can split its
+    // share into `gran` equal parts that are also a uniform partition of the
+    // whole sequence.
+    const int64_t Dg = max((T + NW * gran - 1) / (NW * gran), (min_share + gran - 1) / gran);
+    const int64_t D = Dg * gran;
     const int64_t g0 = min(blk * 4 * D, T), g4 = min((blk * 4 + 4) * D, T);
     const int64_t d0 = min((blk * 4 + wid) * D, T), d1 = min(d0 + D, T);
     const Bracket a0 = bracket<kProbesA, CW>(s_probe, 0, stepA, S, o0, g0, lane);

@@ -52,13 +52,15 @@ namespace segred {
 struct KArgs {
     const uint32_t *values;  // element bits, row-major [rows, F]
     const int64_t *offsets;  // [S + 1]
-    int64_t S, F, NW;        // S: segment count, or the capacity when S_dev is set
+    int64_t S, F;            // S: segment count, or the capacity when S_dev is set
+    int64_t NW;              // waves of the streaming kernel (one merge-path share each)
+    int64_t NS;              // shares the combine kernel sees: NW, or NW * teams per wave
     const int64_t *S_dev;    // segment count on the device (min(*S_dev, S) is used), or null
     uint32_t *out;           // [S, F]
     int64_t *arg;            // [S, F] or null
-    int64_t *hdr;            // [NW][4]: see write_header
-    uint64_t *hval;          // [NW][F]: partial of the share's first segment when it began earlier
-    uint64_t *tval;          // [NW][F]: partial of the share's last segment when it continues
+    int64_t *hdr;            // [NS][4]: see write_header
+    uint64_t *hval;          // [NS][F]: partial of the share's first segment when it began earlier
+    uint64_t *tval;          // [NS][F]: partial of the share's last segment when it continues
 };
 
 // The call's segment count: the host value, or the device one clamped to it.
@@ -109,6 +111,34 @@ struct Red {
         return OP == OP_MAX ? ~(uint32_t)p : (uint32_t)p;
     }
 };
+
+// The same partial with its row code counted from `delta` rows earlier.
+template <typename acc_t>
+__device__ __forceinline__ acc_t rebase_word(acc_t p, uint32_t delta, bool is_max) {
+    if constexpr (std::is_same_v<acc_t, uint64_t>) {
+        const uint32_t rel = is_max ? ~(uint32_t)p : (uint32_t)p;
+        if (rel == 0xFFFFFFFFu) return p;
+        const uint32_t r2 = rel + delta;
+        return (p & 0xFFFFFFFF00000000ull) | (is_max ? ~r2 : r2);
+    } else {
+        return p;
+    }
+}
+
+// Waves per SIMD that each streaming kernel is built for (the compiler keeps
+// its registers within 512 / W per lane), and so the share count of a call:
+// one share per wave of a whole MI355X, 256 CUs x 4 SIMDs x W.  The count is
+// a constant of the kernel, not of the device the call runs on, so every
+// summation order -- and with it every float result -- is the same on any
+// device and partition mode (a device with fewer CUs runs the same shares in
+// several rounds).
+constexpr int64_t kShareSimds = 256 * 4;
+constexpr int kTeamWpe = 4;  // row walk by teams
+constexpr int kRowsWpe = 3;  // row walk by chunks
+template <int DT, int OP>
+constexpr int flat_wpe() {
+    return Red<DT, OP>::kMinMax ? 2 : 4;  // 1-D
+}
 
 // Final value of one (segment, feature); `base` turns a share-relative row
 // into an absolute one.
@@ -176,22 +206,48 @@ __device__ __forceinline__ void write_header(const KArgs &a, int64_t wave, const
     a.hdr[wave * 4 + 3] = sh.split_head ? (sh.first_row + sh.cw * sh.i0) / sh.D : wave;
 }
 
-// Pass 1 for rows of F >= 2 features: each lane owns one feature of a row.
-//   L   lanes per row (next power of two >= F, at most 64; wider rows are
-//       done in blocks of 64 features); G = 64 / L row groups per wave
+// Pass 1 for rows of F >= 2 features: each lane owns VEC consecutive
+// features of a row (VEC = 4: 16-byte loads and stores; VEC = 1: one 4-byte
+// feature, for rows whose width or alignment rules out 16-byte access).
+//   L   lanes per row (the power of two >= F / VEC, at most 64; wider rows
+//       are done in blocks of 64 * VEC features); G = 64 / L row groups per
+//       wave
 //   V   consecutive rows per group per chunk; CH = G * V items per chunk
-// With F >= 64 a row is the whole wave: segment control is wave-uniform and
+//   FC  the row width F when it is fixed at compile time (0: read from the
+//       arguments), which turns every row step into an immediate offset
+// With L = 64 a row is the whole wave: segment control is wave-uniform and
 // no cross-lane step is needed at all.  A chunk's rows are fetched together
 // with its first 64 segment ends before its row count is known (up to CH
 // rows; rows past the chunk are fetched again by the next chunk), and the
 // next chunk is fetched while the current one is processed.
-template <int DT, int OP, int L, int V>
-__global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
+template <int VEC>
+struct Lanes;
+template <>
+struct Lanes<1> {
+    using type = uint32_t;
+    __device__ static __forceinline__ uint32_t at(uint32_t x, int) { return x; }
+    __device__ static __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) { return ld32(r, off); }
+};
+template <>
+struct Lanes<4> {
+    using type = uint4;
+    __device__ static __forceinline__ uint32_t at(const uint4 &x, int v) {
+        return v == 0 ? x.x : v == 1 ? x.y : v == 2 ? x.z : x.w;
+    }
+    __device__ static __forceinline__ uint4 load(__amdgpu_buffer_rsrc_t r, uint32_t off) { return ld128(r, off); }
+};
+
+template <int DT, int OP, int L, int V, int VEC, int FC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kRowsWpe))) void seg_reduce_rows(const KArgs a) {
     using R = Red<DT, OP>;
     using acc_t = typename R::acc_t;
+    using LN = Lanes<VEC>;
+    using x_t = typename LN::type;
     constexpr int G = 64 / L;
     constexpr int CH = G * V;
+    constexpr int FB = L * VEC;  // features per block
     constexpr uint32_t kInf = 0xFFFFFFFFu;
+    const int64_t F = FC > 0 ? (int64_t)FC : a.F;
 
     __shared__ __attribute__((aligned(16))) uint32_t s_ends[4][CH];
 
@@ -208,15 +264,19 @@ __global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
     uint32_t *se = s_ends[wid];
     const uint32_t gv = (uint32_t)(g * V);
 
-    for (int64_t fbase = 0; fbase < a.F; fbase += L) {
-        const int64_t f = fbase + c;
-        const bool fvalid = f < a.F;
+    for (int64_t fbase = 0; fbase < F; fbase += FB) {
+        const int64_t f0 = fbase + (int64_t)c * VEC;
+        // VEC = 4 is used only when F is a multiple of 4, so a lane's four
+        // features are all inside the row or all past it
+        const bool fvalid = f0 < F;
 
         // Partial of the open segment (the one the next chunk starts in),
         // kept per lane; summed over the groups only when a chunk finishes
         // the segment, so chunks without a segment end need no cross-lane
         // work.
-        acc_t open = R::id();
+        acc_t open[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) open[v] = R::id();
         bool open_spread = false;  // open partials are in several groups
         // MEAN: first row (relative to offsets[0]) of the open segment, so a
         // finished segment's length comes from the ends already in LDS.
@@ -225,28 +285,37 @@ __global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
         // Fetch: a chunk's first 64 segment ends (index clamped into the
         // array, loaded unconditionally: a load under a branch would be
         // waited for inside the branch) and its rows through a buffer
-        // descriptor that covers only the rows inside the share, so rows past
-        // it read as 0 without touching memory (a chunk that does not exist
-        // gets an empty descriptor).  One lane offset serves all rows; the row
-        // step is a scalar offset.  Register x[t] is refilled with row t of
+        // descriptor whose range ends with the chunk's last row, so reads past
+        // it return 0 without touching memory (a chunk that does not exist
+        // gets an empty descriptor).  Register x[t] is refilled with row t of
         // the next chunk as soon as row t of the current chunk is consumed, so
         // the next chunk streams in while this one is processed without a
         // second register set.
-        const uint32_t row_bytes = (uint32_t)(a.F * 4);
-        const uint32_t voff = (uint32_t)((gv * a.F + c) * 4);
+        const uint32_t row_bytes = (uint32_t)(F * 4);
+        const uint32_t voff = (uint32_t)((gv * F + c * VEC) * 4);
         auto rows_of = [&](int64_t ic_, int64_t jc_) __attribute__((always_inline)) {
             const int64_t rmax = ic_ + jc_ < sh.d1 ? min((int64_t)CH, sh.j1 - jc_) : 0;
-            return make_rsrc(a.values + (o0 + jc_) * a.F + fbase, (uint32_t)(rmax * row_bytes));
+            return make_rsrc(a.values + (o0 + jc_) * F + fbase,
+                             rmax > 0 ? (uint32_t)(rmax * row_bytes - fbase * 4) : 0u);
         };
-        uint32_t x[V];
+        // Byte offset of row t of a chunk for this lane.  With a fixed row
+        // width it is an immediate; otherwise the step is hidden from the
+        // optimiser once per chunk so that the V offsets are formed next to
+        // their loads instead of being kept in V registers.
+        uint32_t rstep = row_bytes;
+        auto row_off = [&](int t) __attribute__((always_inline)) -> uint32_t {
+            return voff + (uint32_t)t * (FC > 0 ? (uint32_t)(FC * 4) : rstep);
+        };
+        x_t x[V];
         int64_t ic = sh.i0, jc = sh.j0;
         int64_t en = off[min(ic + 1 + lane, S)];
         {
             const auto rs = rows_of(ic, jc);
 #pragma unroll
-            for (int t = 0; t < V; ++t) x[t] = ld32(rs, voff, t * row_bytes);
+            for (int t = 0; t < V; ++t) x[t] = LN::load(rs, row_off(t));
         }
         while (ic + jc < sh.d1) {
+            if constexpr (FC == 0) asm volatile("" : "+s"(rstep));
             const int64_t items = min((int64_t)CH, sh.d1 - ic - jc);
             const int64_t ends_left = min((int64_t)CH, sh.i1 - ic);
 
@@ -291,8 +360,11 @@ __global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
 #pragma unroll
                 for (int t = 0; t < V; ++t) {
                     const uint32_t r = gv + t;
-                    if ((int)r < rows) open = R::comb(open, R::lift(x[t], relbase + r));
-                    x[t] = ld32(rsn, voff, t * row_bytes);
+                    if ((int)r < rows) {
+#pragma unroll
+                        for (int v = 0; v < VEC; ++v) open[v] = R::comb(open[v], R::lift(LN::at(x[t], v), relbase + r));
+                    }
+                    x[t] = LN::load(rsn, row_off(t));
                 }
                 open_spread = G > 1;
                 ic = icn;
@@ -302,12 +374,17 @@ __global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
 
             // The open segment's partial so far, needed by group 0 only: the
             // groups' parts in group order when they are spread.
-            acc_t carry = open;
+            acc_t carry[VEC];
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) carry[v] = open[v];
             if (G > 1 && open_spread) {
 #pragma unroll
                 for (int m = L; m < 64; m <<= 1) {
-                    const acc_t o = lane_get(carry, lane ^ m);
-                    carry = (lane & m) ? R::comb(o, carry) : R::comb(carry, o);
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) {
+                        const acc_t o = lane_get(carry[v], lane ^ m);
+                        carry[v] = (lane & m) ? R::comb(o, carry[v]) : R::comb(carry[v], o);
+                    }
                 }
             }
             wave_lds_sync();
@@ -321,7 +398,9 @@ __global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
             }
 
             // Walk the group's rows in order (wave-uniform control for G = 1).
-            acc_t acc = R::id(), hacc = R::id();
+            acc_t acc[VEC], hacc[VEC];
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) acc[v] = hacc[v] = R::id();
             bool hh = false;  // this group finished at least one segment
             int64_t hseg = 0, hlen = 0;
             int k = a_lo;
@@ -347,12 +426,14 @@ __global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
                 if (!hh) {
                     hh = true;
                     hseg = seg;
-                    hacc = acc;
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) hacc[v] = acc[v];
                     hlen = len;
                 } else if (fvalid) {
-                    store_final<DT, OP, 1>(a, seg, f, &acc, base, len);
+                    store_final<DT, OP, VEC>(a, seg, f0, acc, base, len);
                 }
-                acc = R::id();
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) acc[v] = R::id();
                 ++seg;
                 ++k;
                 next_end = end_at(k);
@@ -362,42 +443,66 @@ __global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
             for (int t = 0; t < V; ++t) {
                 const uint32_t r = gv + t;
                 while (next_end <= r) finish();
-                if ((int)r < rows) acc = R::comb(acc, R::lift(x[t], relbase + r));
-                x[t] = ld32(rsn, voff, t * row_bytes);
+                if ((int)r < rows) {
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) acc[v] = R::comb(acc[v], R::lift(LN::at(x[t], v), relbase + r));
+                }
+                x[t] = LN::load(rsn, row_off(t));
             }
             while (k < a_hi) finish();
 
             // Segmented inclusive scan over the groups; the carry enters at
             // group 0.  A group that finished a segment restarts the scan.
-            acc_t xs = (g == 0 && !hh) ? R::comb(carry, acc) : acc;
-            acc_t ex = carry;
+            acc_t xs[VEC], ex[VEC];
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                xs[v] = (g == 0 && !hh) ? R::comb(carry[v], acc[v]) : acc[v];
+                ex[v] = carry[v];
+            }
             if constexpr (G > 1) {
                 bool flag = hh;
 #pragma unroll
                 for (int o = L; o < 64; o <<= 1) {
                     const int src = (lane - o) & 63;
                     const bool pf = lane_get(flag, src);
-                    const acc_t px = lane_get(xs, src);
+                    acc_t px[VEC];
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) px[v] = lane_get(xs[v], src);
                     if (lane >= o) {
-                        if (!flag) xs = R::comb(px, xs);
+                        if (!flag) {
+#pragma unroll
+                            for (int v = 0; v < VEC; ++v) xs[v] = R::comb(px[v], xs[v]);
+                        }
                         flag = flag || pf;
                     }
                 }
-                const acc_t prev = lane_get(xs, (lane - L) & 63);
-                if (g != 0) ex = prev;
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) {
+                    const acc_t prev = lane_get(xs[v], (lane - L) & 63);
+                    if (g != 0) ex[v] = prev;
+                }
             }
             if (hh && fvalid) {
-                const acc_t hv = R::comb(ex, hacc);
-                if (sh.split_head && hseg == sh.i0) a.hval[wave * a.F + f] = R::to_slot(hv);
-                else store_final<DT, OP, 1>(a, hseg, f, &hv, base, hlen);
+                acc_t hv[VEC];
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) hv[v] = R::comb(ex[v], hacc[v]);
+                if (sh.split_head && hseg == sh.i0) {
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) a.hval[wave * F + f0 + v] = R::to_slot(hv[v]);
+                } else {
+                    store_final<DT, OP, VEC>(a, hseg, f0, hv, base, hlen);
+                }
             }
             // The open segment after this chunk: group G-1's inclusive value,
             // parked in group 0.
-            if constexpr (G > 1) {
-                const acc_t last = lane_get(xs, (G - 1) * L + c);
-                open = g == 0 ? last : R::id();
-            } else {
-                open = xs;
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                if constexpr (G > 1) {
+                    const acc_t last = lane_get(xs[v], (G - 1) * L + c);
+                    open[v] = g == 0 ? last : R::id();
+                } else {
+                    open[v] = xs[v];
+                }
             }
             open_spread = false;
             if constexpr (OP == OP_MEAN) open_start = jc + (int64_t)__builtin_amdgcn_readfirstlane(se[ne - 1]);
@@ -407,15 +512,253 @@ __global__ __launch_bounds__(256) void seg_reduce_rows(const KArgs a) {
             wave_lds_sync();
         }
         if (sh.has_tail) {
-            acc_t t = open;
+            acc_t t[VEC];
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) t[v] = open[v];
             if (G > 1 && open_spread) {
 #pragma unroll
                 for (int m = L; m < 64; m <<= 1) {
-                    const acc_t o = lane_get(t, lane ^ m);
-                    t = (lane & m) ? R::comb(o, t) : R::comb(t, o);
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) {
+                        const acc_t o = lane_get(t[v], lane ^ m);
+                        t[v] = (lane & m) ? R::comb(o, t[v]) : R::comb(t[v], o);
+                    }
                 }
             }
-            if (g == 0 && fvalid) a.tval[wave * a.F + f] = R::to_slot(t);
+            if (g == 0 && fvalid) {
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) a.tval[wave * F + f0 + v] = R::to_slot(t[v]);
+            }
+        }
+    }
+    if (lane == 0) write_header(a, wave, sh);
+}
+
+// Pass 1 for rows of F >= 2 features, by teams: a team is the L lanes that
+// hold one row (VEC features per lane), G = 64 / L teams per wave.  The
+// merge-path partition is made at team granularity: the wave's share is
+// split into G equal parts of the (rows + segment ends) sequence, and team
+// g walks the rows of part g one at a time, in order, finishing every
+// segment whose end it meets.  Each team keeps its own accumulators and its
+// own queue of upcoming segment ends, so the walk needs no cross-lane step;
+// a load instruction of the wave fetches one row of every team (G rows from
+// G places, each a whole number of cache lines).  Loads run V rows ahead of
+// the walk.  After the walk the teams' partials of segments cut by part
+// boundaries go to LDS and the wave folds them in team order: segments that
+// began in this wave are finished there, and the wave leaves at most one
+// head and one tail partial in scratch for the combine kernel, as a share
+// of the 1-D kernel does.
+//   L    lanes per row (power of two >= F / VEC, at most 64; wider rows are
+//        walked again per block of 64 * VEC features)
+//   V    rows in flight per team
+//   FC   F when fixed at compile time (row steps become immediates), else 0
+template <int DT, int OP, int L, int V, int VEC, int FC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kTeamWpe))) void seg_reduce_team(const KArgs a) {
+    using R = Red<DT, OP>;
+    using acc_t = typename R::acc_t;
+    using LN = Lanes<VEC>;
+    using x_t = typename LN::type;
+    constexpr int G = 64 / L;
+    constexpr int FB = L * VEC;
+    constexpr int P = 4;  // probes per lane per search round
+    constexpr uint32_t kNoRow = 0xFFFFFFF0u;  // lane offset past any descriptor
+    constexpr uint32_t kNoEnd = 0xFFFFFFFFu;
+    const int64_t F = FC > 0 ? (int64_t)FC : a.F;
+
+    const int wid = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int g = lane / L;
+    const int c = lane % L;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + wid;
+    const int64_t *off = a.offsets;
+    __shared__ int64_t s_probe[kProbesA];
+    const int64_t S = seg_count(a);
+    const Share sh = find_share(off, S, a.NW, wave, lane, s_probe, 1, G);
+    const int64_t o0 = sh.o0;
+    const int64_t dT = sh.D / G;  // items per team part
+    auto rebase = [](acc_t p, uint32_t delta) __attribute__((always_inline)) -> acc_t {
+        if constexpr (R::kMinMax) return rebase_word(p, delta, OP == OP_MAX);
+        else return p;
+    };
+    // per wave: the teams' head and tail partials of the current feature
+    // block, and what the fold needs to know of each part
+    struct PartInfo {
+        int64_t i0, i1;
+        uint32_t delta;  // first row of the part - first row of the share
+        uint32_t flags;  // 1: split head, 2: tail, 4: the head began in this wave
+    };
+    __shared__ uint64_t s_hp[4][2][64 * VEC];
+    __shared__ PartInfo s_info[4][G];
+
+    // Part g starts at diagonal t0 = d0 + g dT: i(t0) lies in [i0, i1] and
+    // key(i0) <= d0 <= t0.  The team's L lanes narrow it with (L P)-way
+    // rounds over consecutive offsets (counts and keys within the team).
+    const int64_t t0 = min(sh.d0 + (int64_t)g * dT, sh.d1);
+    int64_t lo = sh.i0, hi = g == 0 ? sh.i0 : sh.i1, klo = sh.first_row + sh.i0;
+    const uint64_t tmask = (G == 1 ? ~0ull : ((1ull << L) - 1ull)) << (g * L);
+    while (lo < hi) {
+        const int64_t st = (hi - lo + L * P - 1) / (L * P);
+        int64_t kp[P];
+        int n = 0;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int64_t pos = lo + (int64_t)(p * L + c + 1) * st;
+            const int64_t q = min(pos, S);
+            kp[p] = off[q] - o0 + q;
+            n += popc64(ballot(pos <= hi && kp[p] <= t0) & tmask);
+        }
+        if (n > 0) {
+            // key of probe n (1-based): slot (n - 1) / L of team lane (n - 1) % L
+            const int m = n - 1;
+            const int src = g * L + (m % L), slot = m / L;
+            int64_t v = 0;
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const int64_t w = lane_get(kp[p], src);
+                v = slot == p ? w : v;
+            }
+            klo = v;
+        }
+        hi = min(hi, lo + (int64_t)(n + 1) * st - 1);
+        lo += (int64_t)n * st;
+    }
+    // The part: ends [ti0, ti1), rows [tj0, tj1) relative to o0; its end is
+    // the next team's start (the share's end for the last team).
+    const int64_t ti0 = lo, tj0 = t0 - lo, tfirst = klo - lo;
+    int64_t ti1 = lane_get(ti0, (lane + L) & 63), tj1 = lane_get(tj0, (lane + L) & 63);
+    int64_t ttail = lane_get(tfirst, (lane + L) & 63);
+    if (g == G - 1) {
+        ti1 = sh.i1;
+        tj1 = sh.j1;
+        ttail = sh.tail_row;
+    }
+    const bool split_head = ti0 < ti1 && tfirst < tj0;
+    const bool has_tail = ti1 < S && ttail < tj1;
+    const int64_t base = o0 + tj0;                    // absolute first row of the part
+    const uint32_t nrows = (uint32_t)(tj1 - tj0);     // rows of the part
+    const uint32_t row_bytes = (uint32_t)(F * 4);
+    // relative end of segment k (k < ti1), or kNoEnd
+    auto end_rel = [&](int64_t k) __attribute__((always_inline)) -> uint32_t {
+        const int64_t e = off[min(k + 1, S)] - o0 - tj0;
+        return k < ti1 ? (uint32_t)e : kNoEnd;
+    };
+
+    for (int64_t fbase = 0; fbase < F; fbase += FB) {
+        const int64_t f0 = fbase + (int64_t)c * VEC;
+        const bool fvalid = f0 < F;
+        // All rows of the wave's share lie in one descriptor; a team's row r
+        // (relative to its part) is at lane offset toff + r * row_bytes, and
+        // rows at or past the part's end are asked for at kNoRow (read as 0).
+        const auto rs = make_rsrc(a.values + (o0 + sh.j0) * F + fbase,
+                                  sh.j1 > sh.j0 ? (uint32_t)((sh.j1 - sh.j0) * F * 4 - fbase * 4) : 0u);
+        const uint32_t toff = (uint32_t)((tj0 - sh.j0) * F + c * VEC) * 4u;
+        auto row_at = [&](uint32_t r) __attribute__((always_inline)) -> uint32_t {
+            return r < nrows ? toff + r * row_bytes : kNoRow;
+        };
+        acc_t acc[VEC], hacc[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[v] = hacc[v] = R::id();
+        int64_t seg = ti0;
+        uint32_t e1 = end_rel(seg), e2 = end_rel(seg + 1);  // the next two ends
+        uint32_t seg_start = (uint32_t)(tfirst - tj0);      // MEAN: start of segment `seg` (wraps if earlier)
+
+        auto finish = [&]() __attribute__((always_inline)) {
+            if (seg == ti0 && split_head) {
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) hacc[v] = acc[v];
+            } else if (fvalid) {
+                store_final<DT, OP, VEC>(a, seg, f0, acc, base, (int64_t)(e1 - seg_start));
+            }
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) acc[v] = R::id();
+            seg_start = e1;
+            ++seg;
+            e1 = e2;
+            e2 = end_rel(seg + 1);
+        };
+
+        x_t x[V];
+#pragma unroll
+        for (int t = 0; t < V; ++t) x[t] = LN::load(rs, row_at((uint32_t)t));
+        for (uint32_t rb = 0; ballot(rb < nrows) != 0; rb += V) {
+#pragma unroll
+            for (int t = 0; t < V; ++t) {
+                const uint32_t r = rb + t;
+                while (e1 <= r) finish();
+                if (r < nrows) {
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) acc[v] = R::comb(acc[v], R::lift(LN::at(x[t], v), r));
+                }
+                x[t] = LN::load(rs, row_at(r + V));
+            }
+        }
+        while (e1 != kNoEnd) finish();
+
+        // Fold the parts' partials in team order (row codes rebased to the
+        // share's first row).
+        if constexpr (G > 1) {
+            const uint32_t delta = (uint32_t)(tj0 - sh.j0);
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                s_hp[wid][0][lane * VEC + v] = R::to_slot(rebase(hacc[v], delta));
+                s_hp[wid][1][lane * VEC + v] = R::to_slot(rebase(acc[v], delta));
+            }
+            if (c == 0) {
+                const bool in_wave = (tfirst + ti0) / dT >= wave * G;
+                s_info[wid][g] = PartInfo{ti0, ti1, delta,
+                                          (split_head ? 1u : 0u) | (has_tail ? 2u : 0u) | (in_wave ? 4u : 0u)};
+            }
+            wave_lds_sync();
+            if (g == 0) {
+                acc_t run[VEC];
+                bool run_on = false;
+                for (int gg = 0; gg < G; ++gg) {
+                    const PartInfo pi = s_info[wid][gg];
+                    if (pi.flags & 1u) {
+                        acc_t val[VEC];
+#pragma unroll
+                        for (int v = 0; v < VEC; ++v) {
+                            const acc_t h = R::from_slot(s_hp[wid][0][(gg * L + c) * VEC + v]);
+                            val[v] = run_on ? R::comb(run[v], h) : h;
+                        }
+                        if (pi.flags & 4u) {
+                            if (fvalid) {
+                                int64_t len = 0;
+                                if constexpr (OP == OP_MEAN) len = off[pi.i0 + 1] - off[pi.i0];
+                                store_final<DT, OP, VEC>(a, pi.i0, f0, val, o0 + sh.j0, len);
+                            }
+                        } else if (fvalid) {
+#pragma unroll
+                            for (int v = 0; v < VEC; ++v) a.hval[wave * F + f0 + v] = R::to_slot(val[v]);
+                        }
+                        run_on = false;
+                    }
+                    if (pi.flags & 2u) {
+#pragma unroll
+                        for (int v = 0; v < VEC; ++v) {
+                            const acc_t t = R::from_slot(s_hp[wid][1][(gg * L + c) * VEC + v]);
+                            run[v] = (run_on && pi.i0 == pi.i1) ? R::comb(run[v], t) : t;
+                        }
+                        run_on = true;
+                    } else {
+                        run_on = false;
+                    }
+                }
+                if (sh.has_tail && fvalid) {
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) a.tval[wave * F + f0 + v] = R::to_slot(run[v]);
+                }
+            }
+            wave_lds_sync();
+        } else {
+            if (split_head && fvalid) {
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) a.hval[wave * F + f0 + v] = R::to_slot(hacc[v]);
+            }
+            if (has_tail && fvalid) {
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) a.tval[wave * F + f0 + v] = R::to_slot(acc[v]);
+            }
         }
     }
     if (lane == 0) write_header(a, wave, sh);
@@ -460,7 +803,7 @@ __device__ __forceinline__ int flat_unit(int owner, int c) {
 constexpr int kFlatEndWeight = 8;
 
 template <int DT, int OP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Red<DT, OP>::kMinMax ? 2 : 4)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(flat_wpe<DT, OP>())))
 void seg_reduce_flat(const KArgs a) {
     using R = Red<DT, OP>;
     using acc_t = typename R::acc_t;
@@ -527,7 +870,7 @@ void seg_reduce_flat(const KArgs a) {
         const int64_t rmax = ic_ + jc_ < sh.d1 ? min((int64_t)CH, sh.j1 - jc_) : 0;
         const auto rs = make_rsrc(a.values + (o0 + jc_), (uint32_t)(rmax * 4));
 #pragma unroll
-        for (int u = 0; u < V / 4; ++u) X[u] = ld128(rs, (uint32_t)(lane * 16), (uint32_t)(u * 1024));
+        for (int u = 0; u < V / 4; ++u) X[u] = ld128(rs, (uint32_t)(lane * 16 + u * 1024));
     };
 
     acc_t carry = R::id();
@@ -748,14 +1091,15 @@ struct P2<DT, OP, true> {
 };
 
 // Pass 2: a share whose first segment began in earlier shares folds the tail
-// partials of those shares, in share order, into its head partial.
+// partials of those shares, in share order, into its head partial.  One wave
+// per share; a share without such a segment only reads its header.
 template <int DT, int OP>
 __global__ __launch_bounds__(256) void seg_reduce_pass2(const KArgs a) {
     using P = P2<DT, OP>;
     const int wid = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int64_t w = (int64_t)blockIdx.x * 4 + wid;
-    if (w >= a.NW) return;
+    if (w >= a.NS) return;
     const int64_t s = a.hdr[w * 4 + 0];
     const int64_t first = a.hdr[w * 4 + 3];  // share holding the segment's first row
     if (s < 0) return;
@@ -803,78 +1147,102 @@ __global__ __launch_bounds__(256) void seg_reduce_pass2(const KArgs a) {
 
 // ------------------------------------------------------------------ host side
 
-constexpr int64_t kFallbackShares = 8192;
 constexpr int64_t kMaxFeat = int64_t(1) << 24;
 
-
-// Waves of `kernel` that fit on the device at once (CUs x resident
-// workgroups x 4): one share per resident wave, so every wave streams its
-// share from start to end without a second generation of workgroups.
-static int64_t resident_waves(const void *kernel) {
-    static std::mutex mu;
-    static std::map<std::pair<int, const void *>, int64_t> cache;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return kFallbackShares;
-    std::lock_guard<std::mutex> lk(mu);
-    auto it = cache.find({dev, kernel});
-    if (it != cache.end()) return it->second;
-    int cus = 0, blocks = 0;
-    int64_t w = kFallbackShares;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, 256, 0) == hipSuccess && cus > 0 &&
-        blocks > 0)
-        w = (int64_t)cus * blocks * 4;
-    (void)hipGetLastError();
-    cache[{dev, kernel}] = w;
-    return w;
-}
-
-static int lanes_for(int64_t feat) {
-    int64_t l = 2;
-    while (l < feat && l < 64) l <<= 1;
+// Lanes per row for rows of `units` lane-sized pieces: the power of two at
+// or above it, at most 64.
+static int lanes_for(int64_t units, int lo) {
+    int64_t l = lo;
+    while (l < units && l < 64) l <<= 1;
     return (int)l;
 }
 
+// Pass-1 kernel for a row width and the alignment of the arrays, and its
+// share count.  Rows take 16-byte access (four features per lane) when they
+// are whole 16-byte units and values, out and arg_out start on 16 bytes,
+// else one feature per lane.  Rows of at most 128 bytes are walked by teams
+// (8 or more rows per load instruction, no per-chunk cross-lane step); wider
+// rows by chunks, whose few row groups per wave make the chunk's cross-lane
+// steps cheap and keep each load instruction on one contiguous stretch.
+struct Pick {
+    const void *kernel;
+    int64_t waves;  // shares (one per wave) of a call
+};
+#define SEGRED_TEAM(L, V, VEC, FC) \
+    Pick{reinterpret_cast<const void *>(&seg_reduce_team<DT, OP, L, V, VEC, FC>), kShareSimds * kTeamWpe}
+#define SEGRED_ROWS(L, V, VEC, FC) \
+    Pick{reinterpret_cast<const void *>(&seg_reduce_rows<DT, OP, L, V, VEC, FC>), kShareSimds * kRowsWpe}
 template <int DT, int OP>
-static const void *pick_kernel(int64_t feat) {
-    if (feat == 1) return reinterpret_cast<const void *>(&seg_reduce_flat<DT, OP>);
-    switch (lanes_for(feat)) {
-    case 2: return reinterpret_cast<const void *>(&seg_reduce_rows<DT, OP, 2, 16>);
-    case 4: return reinterpret_cast<const void *>(&seg_reduce_rows<DT, OP, 4, 16>);
-    case 8: return reinterpret_cast<const void *>(&seg_reduce_rows<DT, OP, 8, 16>);
-    case 16: return reinterpret_cast<const void *>(&seg_reduce_rows<DT, OP, 16, 16>);
-    case 32: return reinterpret_cast<const void *>(&seg_reduce_rows<DT, OP, 32, 24>);
-    default: return reinterpret_cast<const void *>(&seg_reduce_rows<DT, OP, 64, 24>);
+static Pick pick_kernel(int64_t feat, bool vec4) {
+    if (feat == 1)
+        return Pick{reinterpret_cast<const void *>(&seg_reduce_flat<DT, OP>), kShareSimds * flat_wpe<DT, OP>()};
+    if (vec4 && feat % 4 == 0) {
+        if (feat == 32) return SEGRED_TEAM(8, 8, 4, 32);
+        if (feat == 64) return SEGRED_ROWS(16, 8, 4, 64);
+        switch (lanes_for(feat / 4, 1)) {
+        case 1: return SEGRED_TEAM(1, 8, 4, 0);
+        case 2: return SEGRED_TEAM(2, 8, 4, 0);
+        case 4: return SEGRED_TEAM(4, 8, 4, 0);
+        case 8: return SEGRED_TEAM(8, 8, 4, 0);
+        case 16: return SEGRED_ROWS(16, 8, 4, 0);
+        case 32: return SEGRED_ROWS(32, 8, 4, 0);
+        default: return SEGRED_ROWS(64, 8, 4, 0);
+        }
+    }
+    switch (lanes_for(feat, 2)) {
+    case 2: return SEGRED_TEAM(2, 16, 1, 0);
+    case 4: return SEGRED_TEAM(4, 16, 1, 0);
+    case 8: return SEGRED_TEAM(8, 16, 1, 0);
+    case 16: return SEGRED_TEAM(16, 16, 1, 0);
+    case 32: return SEGRED_ROWS(32, 24, 1, 0);
+    default: return SEGRED_ROWS(64, 24, 1, 0);
     }
 }
+#undef SEGRED_TEAM
+#undef SEGRED_ROWS
 
-// Shares per call: one per wave that fits on the device at once.
-static int64_t shares_for(const void *kernel) {
+static int64_t shares_for(const Pick &pk) {
     const int64_t o = shares_override();
-    return ((o > 0 ? o : resident_waves(kernel)) + 3) / 4 * 4;  // whole workgroups of 4 waves
+    return o > 0 ? (o + 3) / 4 * 4 : pk.waves;  // whole workgroups of 4 waves
+}
+
+// Waves of a kernel that fit on the current device at once (0 if unknown).
+static int64_t resident_waves(const void *kernel) {
+    int dev = 0, cus = 0, blocks = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, 256, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return (int64_t)cus * blocks * 4;
 }
 
 template <int DT, int OP>
 static int run(KArgs k, hipStream_t st) {
-    const void *kernel = pick_kernel<DT, OP>(k.F);
-    const int64_t nw = shares_for(kernel);
-    const size_t hdr_bytes = (size_t)nw * 4 * sizeof(int64_t);
-    const size_t val_bytes = (size_t)nw * (size_t)k.F * sizeof(uint64_t);
+    const bool vec4 = aligned(k.values, 16) && aligned(k.out, 16) && (!k.arg || aligned(k.arg, 16));
+    const Pick pk = pick_kernel<DT, OP>(k.F, vec4);
+    const int64_t nw = shares_for(pk);
+    const int64_t ns = nw;
+    const size_t hdr_bytes = (size_t)ns * 4 * sizeof(int64_t);
+    const size_t val_bytes = (size_t)ns * (size_t)k.F * sizeof(uint64_t);
     ScratchLease scratch;
     int rc = scratch_acquire(scratch, hdr_bytes + 2 * val_bytes, st);
     if (rc != SEGRED_OK) return rc;
     char *p = static_cast<char *>(scratch.ptr);
     k.NW = nw;
+    k.NS = ns;
     k.hdr = reinterpret_cast<int64_t *>(p);
     k.hval = reinterpret_cast<uint64_t *>(p + hdr_bytes);
-    k.tval = k.hval + (size_t)nw * (size_t)k.F;
+    k.tval = k.hval + (size_t)ns * (size_t)k.F;
 
-    const dim3 grid((unsigned)(nw / 4)), block(256);
     void *params[] = {&k};
-    hipError_t e = hipExtLaunchKernel(kernel, grid, block, params, 0, st, nullptr, timing_stop(true), 0);
+    hipError_t e = hipExtLaunchKernel(pk.kernel, dim3((unsigned)(nw / 4)), dim3(256), params, 0, st, nullptr,
+                                      timing_stop(true), 0);
     if (e == hipSuccess)
-        e = hipExtLaunchKernel(reinterpret_cast<const void *>(&seg_reduce_pass2<DT, OP>), grid, block, params, 0,
-                               st, nullptr, timing_stop(false), 0);
+        e = hipExtLaunchKernel(reinterpret_cast<const void *>(&seg_reduce_pass2<DT, OP>),
+                               dim3((unsigned)((ns + 3) / 4)), dim3(256), params, 0, st, nullptr,
+                               timing_stop(false), 0);
     return e == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
 }
 
@@ -895,8 +1263,26 @@ static int dispatch(int32_t dtype, int32_t op, const KArgs &k, hipStream_t st) {
 }
 
 template <int DT, int OP>
-static int64_t shares_of(int64_t feat) {
-    return shares_for(pick_kernel<DT, OP>(feat));
+static int64_t shares_of(int64_t feat, bool resident) {
+    const Pick pk = pick_kernel<DT, OP>(feat, true);
+    return resident ? resident_waves(pk.kernel) : shares_for(pk);
+}
+
+static int64_t shares_query(int32_t dtype, int32_t op, int64_t feat, bool resident) {
+    if (feat < 1) return -1;
+    switch (dtype * 4 + op) {
+    case DT_U32 * 4 + OP_SUM: return shares_of<DT_U32, OP_SUM>(feat, resident);
+    case DT_U32 * 4 + OP_MIN: return shares_of<DT_U32, OP_MIN>(feat, resident);
+    case DT_U32 * 4 + OP_MAX: return shares_of<DT_U32, OP_MAX>(feat, resident);
+    case DT_I32 * 4 + OP_SUM: return shares_of<DT_I32, OP_SUM>(feat, resident);
+    case DT_I32 * 4 + OP_MIN: return shares_of<DT_I32, OP_MIN>(feat, resident);
+    case DT_I32 * 4 + OP_MAX: return shares_of<DT_I32, OP_MAX>(feat, resident);
+    case DT_F32 * 4 + OP_SUM: return shares_of<DT_F32, OP_SUM>(feat, resident);
+    case DT_F32 * 4 + OP_MIN: return shares_of<DT_F32, OP_MIN>(feat, resident);
+    case DT_F32 * 4 + OP_MAX: return shares_of<DT_F32, OP_MAX>(feat, resident);
+    case DT_F32 * 4 + OP_MEAN: return shares_of<DT_F32, OP_MEAN>(feat, resident);
+    default: return -1;
+    }
 }
 
 }  // namespace segred
@@ -904,20 +1290,11 @@ static int64_t shares_of(int64_t feat) {
 using namespace segred;
 
 extern "C" int64_t segred_get_shares(int32_t dtype, int32_t op, int64_t feat) {
-    if (feat < 1) return -1;
-    switch (dtype * 4 + op) {
-    case DT_U32 * 4 + OP_SUM: return shares_of<DT_U32, OP_SUM>(feat);
-    case DT_U32 * 4 + OP_MIN: return shares_of<DT_U32, OP_MIN>(feat);
-    case DT_U32 * 4 + OP_MAX: return shares_of<DT_U32, OP_MAX>(feat);
-    case DT_I32 * 4 + OP_SUM: return shares_of<DT_I32, OP_SUM>(feat);
-    case DT_I32 * 4 + OP_MIN: return shares_of<DT_I32, OP_MIN>(feat);
-    case DT_I32 * 4 + OP_MAX: return shares_of<DT_I32, OP_MAX>(feat);
-    case DT_F32 * 4 + OP_SUM: return shares_of<DT_F32, OP_SUM>(feat);
-    case DT_F32 * 4 + OP_MIN: return shares_of<DT_F32, OP_MIN>(feat);
-    case DT_F32 * 4 + OP_MAX: return shares_of<DT_F32, OP_MAX>(feat);
-    case DT_F32 * 4 + OP_MEAN: return shares_of<DT_F32, OP_MEAN>(feat);
-    default: return -1;
-    }
+    return shares_query(dtype, op, feat, false);
+}
+
+extern "C" int64_t segred_resident_waves(int32_t dtype, int32_t op, int64_t feat) {
+    return shares_query(dtype, op, feat, true);
 }
 
 static int reduce_impl(const void *values, int32_t dtype, int64_t feat, const int64_t *offsets,

@@ -9,6 +9,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "segred.h")
+INSTRUMENT = os.path.join(ROOT, "include", "segred_instrument.h")
 CSRC = os.path.join(ROOT, "segmented_reduction_amd", "csrc")
 
 
@@ -20,8 +21,8 @@ def _lib():
     return sr.library()
 
 
-def _declared():
-    text = open(HEADER).read()
+def _declared(path=HEADER):
+    text = open(path).read()
     return sorted(set(re.findall(r"\b(segred_[a-z_]+)\s*\(", text)))
 
 
@@ -33,12 +34,21 @@ def test_header_declares_the_boundary():
         assert required in names
 
 
+def test_public_header_holds_only_the_method():
+    """Test and benchmark hooks live in their own header, not in the ABI."""
+    names = _declared()
+    for hook in _declared(INSTRUMENT):
+        assert hook not in names, hook
+    assert set(_declared(INSTRUMENT)) == {"segred_set_shares", "segred_get_shares", "segred_resident_waves",
+                                          "segred_timing_enable", "segred_timing_read"}
+
+
 def test_library_exports_every_declared_symbol():
     lib = _lib()
     import segmented_reduction_amd as sr
     out = subprocess.run(["nm", "-D", "--defined-only", sr.LIB_PATH], capture_output=True, text=True, check=True)
     exported = set(re.findall(r"\bT (segred_\w+)", out.stdout))
-    for name in _declared():
+    for name in _declared() + _declared(INSTRUMENT):
         assert name in exported, name
         assert hasattr(lib, name), name
 
@@ -220,7 +230,21 @@ def test_share_knob_range():
     assert lib.segred_set_shares(37) == 0
     assert lib.segred_get_shares(2, 0, 1) == 40  # rounded up to whole workgroups of 4 waves
     assert lib.segred_set_shares(0) == 0
-    assert lib.segred_get_shares(2, 0, 1) > 0
+
+
+# The default share count of each kernel: one share per wave of a whole
+# MI355X (1,024 SIMDs x the waves per SIMD the kernel is built for), the same
+# on every device, so float sums repeat across devices and partition modes.
+@pytest.mark.parametrize("dtype,op,feat,shares", [
+    (2, 0, 1, 4096), (2, 3, 1, 4096), (0, 0, 1, 4096), (2, 1, 1, 2048), (1, 2, 1, 2048),
+    (2, 0, 32, 4096), (2, 2, 32, 4096), (2, 3, 32, 4096), (2, 0, 8, 4096), (0, 1, 3, 4096),
+    (2, 0, 64, 3072), (2, 2, 64, 3072), (2, 0, 260, 3072), (2, 0, 33, 3072), (1, 1, 100, 3072),
+])
+def test_default_share_counts_are_constants(dtype, op, feat, shares):
+    lib = _lib()
+    assert lib.segred_set_shares(0) == 0
+    assert lib.segred_get_shares(dtype, op, feat) == shares
+    assert lib.segred_get_shares(dtype, op, 0) == -1
 
 
 def test_timing_read_without_launches():
