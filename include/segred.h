@@ -36,7 +36,8 @@ enum segred_status {
     SEGRED_ERR_INVALID_ARGUMENT = 1, /* rejected on the host before any device work */
     SEGRED_ERR_UNSUPPORTED = 2,      /* a valid request this library does not do (integer MEAN) */
     SEGRED_ERR_OUT_OF_MEMORY = 3,    /* scratch could not be obtained */
-    SEGRED_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
+    SEGRED_ERR_HIP = 4,              /* a HIP runtime call or kernel launch failed */
+    SEGRED_ERR_SCRATCH_LIMIT = 5     /* segred_reduce_noalloc: the call needs more than its fixed scratch */
 };
 
 /*
@@ -93,6 +94,31 @@ enum segred_status {
 int segred_reduce(const void *values, int32_t dtype, int64_t feat,
                   const int64_t *offsets, int64_t num_segments, int32_t op,
                   void *out, int64_t *arg_out, hipStream_t stream);
+
+/*
+ * segred_reduce_noalloc -- segred_reduce for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): it calls no hipMalloc, hipFree or other
+ * allocating routine.  Its scratch is a fixed array of 16 MiB in device
+ * memory that the library holds on each device it runs on until the process
+ * ends (its address is looked up once per device, on the first call there).
+ *
+ *   Arguments, results and errors: as segred_reduce, plus
+ *   SEGRED_ERR_SCRATCH_LIMIT when the call needs more than the fixed
+ *   scratch: 32 * NS + 16 * NS * feat bytes, NS = the call's share count
+ *   (4,096 for 1-D values and rows of at most 128 bytes, 3,072 for wider
+ *   rows), i.e. feat up to 339.  Results are bitwise equal to
+ *   segred_reduce's (same kernels, same shares).
+ *
+ * All calls on one device share that device's array: calls that overlap in
+ * time on one device (on different streams, or from different host threads)
+ * race on it and must not be issued; calls on one stream run in order and
+ * are safe.  Nothing in the array needs clearing between calls (every
+ * header is written before it is read).
+ */
+int segred_reduce_noalloc(const void *values, int32_t dtype, int64_t feat,
+                          const int64_t *offsets, int64_t num_segments, int32_t op,
+                          void *out, int64_t *arg_out, hipStream_t stream);
 
 /*
  * segred_offsets_from_rle -- run-length encoding of uint32 keys and the

@@ -30,7 +30,7 @@ SUM, MIN, MAX, MEAN = 0, 1, 2, 3
 OPS = {"sum": SUM, "min": MIN, "max": MAX, "mean": MEAN}
 DTYPES = {torch.uint32: 0, torch.int32: 1, torch.float32: 2}
 STATUS = {0: "SEGRED_OK", 1: "SEGRED_ERR_INVALID_ARGUMENT", 2: "SEGRED_ERR_UNSUPPORTED",
-          3: "SEGRED_ERR_OUT_OF_MEMORY", 4: "SEGRED_ERR_HIP"}
+          3: "SEGRED_ERR_OUT_OF_MEMORY", 4: "SEGRED_ERR_HIP", 5: "SEGRED_ERR_SCRATCH_LIMIT"}
 
 
 class SegredError(RuntimeError):
@@ -58,6 +58,8 @@ def library(path: str | None = None):
             vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
             lib.segred_reduce.argtypes = [vp, i32, i64, vp, i64, i32, vp, vp, vp]
             lib.segred_reduce.restype = ctypes.c_int
+            lib.segred_reduce_noalloc.argtypes = [vp, i32, i64, vp, i64, i32, vp, vp, vp]
+            lib.segred_reduce_noalloc.restype = ctypes.c_int
             lib.segred_reduce_device_count.argtypes = [vp, i32, i64, vp, vp, i64, i32, vp, vp, vp]
             lib.segred_reduce_device_count.restype = ctypes.c_int
             lib.segred_offsets_from_rle.argtypes = [vp, i64, vp, vp, vp, vp, vp]

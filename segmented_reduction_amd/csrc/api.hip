@@ -137,6 +137,7 @@ extern "C" const char *segred_status_string(int status) {
     case SEGRED_ERR_UNSUPPORTED: return "unsupported request (MEAN needs float32 values)";
     case SEGRED_ERR_OUT_OF_MEMORY: return "out of device memory for scratch";
     case SEGRED_ERR_HIP: return "HIP runtime error";
+    case SEGRED_ERR_SCRATCH_LIMIT: return "the call needs more than the fixed scratch of segred_reduce_noalloc";
     default: return "unknown status";
     }
 }

@@ -1218,18 +1218,40 @@ static int64_t resident_waves(const void *kernel) {
     return (int64_t)cus * blocks * 4;
 }
 
+// Scratch of one call: per share a 32-byte header and two F-wide 8-byte
+// partial slots.
+static size_t scratch_bytes(int64_t ns, int64_t feat) {
+    return (size_t)ns * 4 * sizeof(int64_t) + 2 * (size_t)ns * (size_t)feat * sizeof(uint64_t);
+}
+
+// Fixed scratch of segred_reduce_noalloc: one array per device, found at
+// set-up with hipGetSymbolAddress (the array's name in host code is not a
+// device address).  Every header is written by the streaming kernel before
+// the combine kernel reads it, and a partial slot is read only when its
+// header says it was written, so nothing in it needs clearing between calls.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+// Launch a call's two kernels with scratch at `scratch_ptr` (or, when it is
+// null, scratch from the stream's cached buffer).  `noalloc` makes a request
+// beyond the fixed scratch an error instead.
 template <int DT, int OP>
-static int run(KArgs k, hipStream_t st) {
+static int run(KArgs k, hipStream_t st, void *fixed_scratch) {
     const bool vec4 = aligned(k.values, 16) && aligned(k.out, 16) && (!k.arg || aligned(k.arg, 16));
     const Pick pk = pick_kernel<DT, OP>(k.F, vec4);
     const int64_t nw = shares_for(pk);
     const int64_t ns = nw;
+    const size_t bytes = scratch_bytes(ns, k.F);
+    ScratchLease lease;
+    char *p = static_cast<char *>(fixed_scratch);
+    if (p) {
+        if (bytes > kNoAllocScratchBytes) return SEGRED_ERR_SCRATCH_LIMIT;
+    } else {
+        int rc = scratch_acquire(lease, bytes, st);
+        if (rc != SEGRED_OK) return rc;
+        p = static_cast<char *>(lease.ptr);
+    }
     const size_t hdr_bytes = (size_t)ns * 4 * sizeof(int64_t);
-    const size_t val_bytes = (size_t)ns * (size_t)k.F * sizeof(uint64_t);
-    ScratchLease scratch;
-    int rc = scratch_acquire(scratch, hdr_bytes + 2 * val_bytes, st);
-    if (rc != SEGRED_OK) return rc;
-    char *p = static_cast<char *>(scratch.ptr);
     k.NW = nw;
     k.NS = ns;
     k.hdr = reinterpret_cast<int64_t *>(p);
@@ -1246,18 +1268,18 @@ static int run(KArgs k, hipStream_t st) {
     return e == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
 }
 
-static int dispatch(int32_t dtype, int32_t op, const KArgs &k, hipStream_t st) {
+static int dispatch(int32_t dtype, int32_t op, const KArgs &k, hipStream_t st, void *fixed_scratch) {
     switch (dtype * 4 + op) {
-    case DT_U32 * 4 + OP_SUM: return run<DT_U32, OP_SUM>(k, st);
-    case DT_U32 * 4 + OP_MIN: return run<DT_U32, OP_MIN>(k, st);
-    case DT_U32 * 4 + OP_MAX: return run<DT_U32, OP_MAX>(k, st);
-    case DT_I32 * 4 + OP_SUM: return run<DT_I32, OP_SUM>(k, st);
-    case DT_I32 * 4 + OP_MIN: return run<DT_I32, OP_MIN>(k, st);
-    case DT_I32 * 4 + OP_MAX: return run<DT_I32, OP_MAX>(k, st);
-    case DT_F32 * 4 + OP_SUM: return run<DT_F32, OP_SUM>(k, st);
-    case DT_F32 * 4 + OP_MIN: return run<DT_F32, OP_MIN>(k, st);
-    case DT_F32 * 4 + OP_MAX: return run<DT_F32, OP_MAX>(k, st);
-    case DT_F32 * 4 + OP_MEAN: return run<DT_F32, OP_MEAN>(k, st);
+    case DT_U32 * 4 + OP_SUM: return run<DT_U32, OP_SUM>(k, st, fixed_scratch);
+    case DT_U32 * 4 + OP_MIN: return run<DT_U32, OP_MIN>(k, st, fixed_scratch);
+    case DT_U32 * 4 + OP_MAX: return run<DT_U32, OP_MAX>(k, st, fixed_scratch);
+    case DT_I32 * 4 + OP_SUM: return run<DT_I32, OP_SUM>(k, st, fixed_scratch);
+    case DT_I32 * 4 + OP_MIN: return run<DT_I32, OP_MIN>(k, st, fixed_scratch);
+    case DT_I32 * 4 + OP_MAX: return run<DT_I32, OP_MAX>(k, st, fixed_scratch);
+    case DT_F32 * 4 + OP_SUM: return run<DT_F32, OP_SUM>(k, st, fixed_scratch);
+    case DT_F32 * 4 + OP_MIN: return run<DT_F32, OP_MIN>(k, st, fixed_scratch);
+    case DT_F32 * 4 + OP_MAX: return run<DT_F32, OP_MAX>(k, st, fixed_scratch);
+    case DT_F32 * 4 + OP_MEAN: return run<DT_F32, OP_MEAN>(k, st, fixed_scratch);
     default: return SEGRED_ERR_UNSUPPORTED;
     }
 }
@@ -1297,9 +1319,32 @@ extern "C" int64_t segred_resident_waves(int32_t dtype, int32_t op, int64_t feat
     return shares_query(dtype, op, feat, true);
 }
 
+// Device address of this device's fixed scratch array (null on failure),
+// looked up once per device with that device current.
+static void *fixed_scratch_for_current_device() {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *ptrs[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lk(mu);
+    if (!ptrs[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        ptrs[dev] = ptr;
+    }
+    return ptrs[dev];
+}
+
 static int reduce_impl(const void *values, int32_t dtype, int64_t feat, const int64_t *offsets,
                        int64_t num_segments, const int64_t *num_segments_dev, int32_t op, void *out,
-                       int64_t *arg_out, hipStream_t stream) {
+                       int64_t *arg_out, hipStream_t stream, bool noalloc = false) {
     if (num_segments < 0 || feat < 1 || dtype < SEGRED_U32 || dtype > SEGRED_F32 || op < SEGRED_SUM ||
         op > SEGRED_MEAN)
         return SEGRED_ERR_INVALID_ARGUMENT;
@@ -1320,7 +1365,12 @@ static int reduce_impl(const void *values, int32_t dtype, int64_t feat, const in
     k.F = feat;
     k.out = static_cast<uint32_t *>(out);
     k.arg = arg_out;
-    return dispatch(dtype, op, k, stream);
+    void *fixed = nullptr;
+    if (noalloc) {
+        fixed = fixed_scratch_for_current_device();
+        if (!fixed) return SEGRED_ERR_HIP;
+    }
+    return dispatch(dtype, op, k, stream, fixed);
 }
 
 extern "C" int segred_reduce(const void *values, int32_t dtype, int64_t feat, const int64_t *offsets,
@@ -1334,4 +1384,10 @@ extern "C" int segred_reduce_device_count(const void *values, int32_t dtype, int
                                           int64_t *arg_out, hipStream_t stream) {
     if (!num_segments) return SEGRED_ERR_INVALID_ARGUMENT;
     return reduce_impl(values, dtype, feat, offsets, max_segments, num_segments, op, out, arg_out, stream);
+}
+
+extern "C" int segred_reduce_noalloc(const void *values, int32_t dtype, int64_t feat, const int64_t *offsets,
+                                     int64_t num_segments, int32_t op, void *out, int64_t *arg_out,
+                                     hipStream_t stream) {
+    return reduce_impl(values, dtype, feat, offsets, num_segments, nullptr, op, out, arg_out, stream, true);
 }
