@@ -1,22 +1,26 @@
 #!/usr/bin/env python3
 """Throughput of the segmented reduction on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config message]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config powerlaw]
+                    [--also message,rle,skew]
 
-One step is one pass of the workload's hot path over one batch of seeded
-synthetic input already resident in HBM.  The default workload is graph
-message passing: 1,000,000 destination-sorted rows x 64 float32 features
-reduced into 10,000 segments, one segmented sum and one segmented max with
-its producing row per step (the graph-reduce README's 1M x 64 -> 10,000
-case).  Several copies of the input are kept and rotated so that each call
-reads rows no call touched for the last few calls: the 256 MB last-level
-cache cannot serve them and the rate is an HBM rate.
+One step is one pass of a workload's hot path over one batch of seeded
+synthetic input already resident in HBM.  The headline workload is the
+largest configuration: a power-law graph of 32,000,000 destination-sorted
+edge rows x 32 float32 features reduced into 2,000,000 segments, one
+segmented sum, one mean and one max with its producing row per step.  The
+other gated configurations (1M x 64 message passing, 16M-key sort -> RLE ->
+reduce, 50M-element heavy skew) run in the same process and are reported
+under "configs", each with its own roofline.  Several copies of an input
+that fits the 256 MB last-level cache are kept and rotated, so every rate
+is an HBM rate.
 
 Prints ONE JSON line: the effective bandwidth (algorithmic bytes / wall time
 of the K timed steps), Gelem/s, the roofline of the dominant kernel (its
-algorithmic bytes per launch / its average duration, from kernel-stamped HIP
-stop events on its stream over a second pass of the same K steps) and the CPU
-oracle timed on the host on the same workload.
+algorithmic bytes per launch / its average duration, from start and stop
+events the runtime stamps on the kernel itself over a second pass of the
+same K steps) and the CPU oracle timed on the host's cores (T threads over
+contiguous row-balanced segment ranges, and one thread on a sample).
 """
 from __future__ import annotations
 
@@ -160,9 +164,11 @@ class RleWorkload(Workload):
 
     def call_bytes(self, label):
         if label == "rle_count":
-            return self.n * 4
+            return self.n * 4  # every key read once
         if label == "rle_materialize":
-            return self.n * 4 + self.count * (4 + 4 + 8) + 8
+            # values, lengths and offsets of each run written (+ offsets[count]),
+            # and the key of each run read once more to write its value
+            return self.count * (4 + 4 + 8 + 4) + 8
         return reduce_bytes(self.n, 1, self.count, "min" if label == "min_i32" else "sum")
 
     def bytes_per_step(self):
@@ -408,13 +414,40 @@ def build_workload(name, sr, torch):
 
 # ---------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(wl, name, budget_s):
-    """The oracle, as it stands, on the host (one thread), on the same workload."""
+def host_threads():
+    """Host threads for the oracle: this process's CPUs, at most 16 (one
+    GPU's share of a node)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, name, budget_s, threads):
+    """The oracle, as it stands, on the host.  Reduction workloads: the whole
+    workload on `threads` threads (each over a contiguous, row-balanced range
+    of segments; every segment is reduced by one sequential pass, so results
+    do not depend on the thread count), repeated while the budget lasts, and
+    one thread on a sample of the segments.  Other workloads: one thread."""
     import oracle
     lib = oracle.load()
     t = 0.0
     reps = 0
     results = {}
+    cores = 1
+    single = None
     if isinstance(wl, SearchWorkload):
         cfg = wl.cfg
         seg = cfg["segments"]
@@ -434,11 +467,10 @@ def cpu_baseline(wl, name, budget_s):
             results.setdefault("search", []).append((b0, b1, a0, out, word))
             done_q += b1 - b0
             s = e
-        reps = 1
         sample = f"first {s} of {seg.shape[0]} segments ({done_q} queries)"
         qps = done_q / t
         return {"value": round(qps * wl.call_bytes("search") / wl.nq / 1e9, 4), "unit": "GB/s", "cores": 1,
-                "kind": "oracle", "sample": sample, "seconds": round(t, 2),
+                "kind": "oracle", "sample": sample, "seconds": round(t, 2), "cpu_model": cpu_model(),
                 "gelem_per_s": round(qps / 1e9, 6)}, results
     if isinstance(wl, ScanWorkload):
         while reps == 0 or (t < budget_s and reps < 50):
@@ -458,15 +490,24 @@ def cpu_baseline(wl, name, budget_s):
         sample = f"full workload ({name}), {reps} rep(s)"
     elif isinstance(wl, RleWorkload):
         cfg = wl.cfg
+        cores = threads
         while reps == 0 or (t < budget_s and reps < 50):
             t0 = time.perf_counter()
             v, ln, off, c = oracle.rle(cfg["keys"], lib=lib)
-            results["sum_u32"] = oracle.reduce(cfg["u32"], off, "sum", lib=lib)
-            results["min_i32"] = oracle.reduce(cfg["i32"], off, "min", lib=lib)
+            results["sum_u32"] = oracle.reduce(cfg["u32"], off, "sum", lib=lib, threads=threads)
+            results["min_i32"] = oracle.reduce(cfg["i32"], off, "min", lib=lib, threads=threads)
             t += time.perf_counter() - t0
             reps += 1
         results["rle"] = (v, ln, off, c)
-        sample = f"full workload ({name}), {reps} rep(s)"
+        sample = (f"full workload ({name}), {reps} rep(s): run-length encoding on one thread (sequential by "
+                  f"definition), both reductions on {threads} threads")
+        t1 = time.perf_counter()
+        oracle.reduce(cfg["u32"], off, "sum", lib=lib)
+        oracle.reduce(cfg["i32"], off, "min", lib=lib)
+        ts = time.perf_counter() - t1
+        b = wl.call_bytes("sum_u32") + wl.call_bytes("min_i32")
+        single = {"value": round(b / ts / 1e9, 3), "unit": "GB/s", "cores": 1,
+                  "sample": "both reductions of the workload", "seconds": round(ts, 2)}
     elif isinstance(wl, ScatterWorkload):
         while reps == 0 or (t < budget_s and reps < 50):
             t0 = time.perf_counter()
@@ -476,16 +517,34 @@ def cpu_baseline(wl, name, budget_s):
             reps += 1
         sample = f"full workload ({name}), all {len(wl.ops)} ops, {reps} rep(s)"
     else:
+        cores = threads
         while reps == 0 or (t < budget_s and reps < 50):
             t0 = time.perf_counter()
             for op in wl.ops:
-                results[op] = oracle.reduce(wl.host_vals, wl.host_off, op, lib=lib)
+                results[op] = oracle.reduce(wl.host_vals, wl.host_off, op, lib=lib, threads=threads)
             t += time.perf_counter() - t0
             reps += 1
-        sample = f"full workload ({name}), all {len(wl.ops)} ops, {reps} rep(s)"
+        sample = f"full workload ({name}), all {len(wl.ops)} ops, {reps} rep(s), {threads} threads"
+        # one thread on the first 1/16 of the segments
+        s_all = wl.host_off.size - 1
+        s_end = max(1, s_all // 16)
+        off_s = wl.host_off[: s_end + 1]
+        rows_s = int(off_s[-1] - off_s[0])
+        t1 = time.perf_counter()
+        for op in wl.ops:
+            oracle.reduce(wl.host_vals, off_s, op, lib=lib)
+        ts = time.perf_counter() - t1
+        b = sum(reduce_bytes(rows_s, wl.feat, s_end, op) for op in wl.ops)
+        single = {"value": round(b / ts / 1e9, 3), "unit": "GB/s", "cores": 1,
+                  "sample": f"first {s_end} of {s_all} segments ({rows_s} rows), all {len(wl.ops)} ops",
+                  "seconds": round(ts, 2)}
     gbs = wl.bytes_per_step() * reps / t / 1e9
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle", "sample": sample,
-            "seconds": round(t, 2), "gelem_per_s": round(wl.elems_per_step() * reps / t / 1e9, 4)}, results
+    res = {"value": round(gbs, 3), "unit": "GB/s", "cores": cores, "kind": "oracle", "sample": sample,
+           "seconds": round(t, 2), "gelem_per_s": round(wl.elems_per_step() * reps / t / 1e9, 4),
+           "cpu_model": cpu_model()}
+    if single is not None:
+        res["single_core"] = single
+    return res, results
 
 
 def check_parity(wl, results):
@@ -590,13 +649,153 @@ def load_traffic(name, dominant_label, src_hash):
 
 # ---------------------------------------------------------------- main
 
+GATED = ["message", "rle", "skew"]  # reported beside the headline (largest) configuration
+
+
+def measure(name, steps, warmup, cpu_seconds, threads, sr, torch, with_cpu=True):
+    """Build one workload, time it and check it; returns a dict (and frees the
+    workload's device memory)."""
+    print(f"[bench] generating {name} ...", file=sys.stderr, flush=True)
+    wl, cfg = build_workload(name, sr, torch)
+    torch.cuda.synchronize()
+    # launches the timing record keeps: at most 4 kernels per call here
+    if steps * len(wl.calls) * 4 > 8192:
+        steps = 8192 // (4 * len(wl.calls))
+
+    for i in range(warmup):
+        wl.step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, nothing attached to the launches.
+    print(f"[bench] timing {name}: {steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        wl.step(warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    # Kernel durations for the roofline: the same K steps again, with every
+    # library kernel launched with a start and a stop event that the runtime
+    # stamps when that kernel begins and ends (hipExtLaunchKernel); the
+    # duration of a launch is its own stop minus its own start.  This pass is
+    # kept out of the wall-clock figure above.
+    sr.timing_enable(True)
+    sr.timing_read()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        wl.step(warmup + steps + i)
+    torch.cuda.synchronize()
+    _, _, each = sr.timing_read()
+    sr.timing_enable(False)
+
+    elapsed = t1 - t0
+    bytes_step = wl.bytes_per_step()
+    value = bytes_step * steps / elapsed / 1e9
+    gelem = wl.elems_per_step() * steps / elapsed / 1e9
+
+    # per-call streaming-kernel times (launch order repeats every step)
+    ncalls = len(wl.calls)
+    kernels = {}
+    for j, (label, op) in enumerate(wl.calls):
+        times = each[j::ncalls]
+        if not times:
+            continue
+        avg_ms = sum(times) / len(times)
+        b = wl.call_bytes(label)
+        kernels[label] = {"avg_us": round(avg_ms * 1e3, 2), "min_us": round(min(times) * 1e3, 2),
+                          "launches": len(times), "bytes": b,
+                          "GBps": round(b / (avg_ms * 1e-3) / 1e9, 1),
+                          "frac": round(b / (avg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    dk = kernels[dominant]
+    src_hash = kernel_source_hash(name)
+    traffic = load_traffic(name, dominant, src_hash)
+    roofline = {"bound": "hbm", "achieved": dk["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": dk["frac"], "traffic": traffic,
+                "kernel": (dominant if dominant.startswith("rle_")
+                           else f"seg_scan_tails ({dominant})" if dominant.endswith("_tails")
+                           else f"{getattr(wl, 'kernel_name', 'reduce pass 1')} ({dominant})"),
+                "algorithmic_bytes_per_launch": dk["bytes"], "avg_launch_us": dk["avg_us"],
+                "timing": "start and stop events stamped on the kernel itself (hipExtLaunchKernel) on the "
+                          "launch stream, over a second pass of the same K steps"}
+
+    cpu = None
+    parity = None
+    if with_cpu:
+        print(f"[bench] timing the CPU oracle on {name} ...", file=sys.stderr, flush=True)
+        cpu, results = cpu_baseline(wl, name, cpu_seconds, threads)
+        parity = check_parity(wl, results)
+        del results
+
+    # bitwise repeat: the rotated copies hold identical inputs (or the one
+    # copy is reduced twice)
+    repeat_ok = None
+    if isinstance(wl, ScatterWorkload) and "max" in wl.ops:
+        # float atomic sums may move in the last bits; max and its rows may not
+        a, aa = sr.scatter(wl.sets[0][0], wl.sets[0][1], wl.dim, "max")
+        b, bb = sr.scatter(wl.sets[-1][0], wl.sets[-1][1], wl.dim, "max")
+        torch.cuda.synchronize()
+        repeat_ok = bool(torch.equal(a.view(torch.int32), b.view(torch.int32)) and torch.equal(aa, bb))
+    if isinstance(wl, ScanWorkload):
+        a = sr.scan(wl.vals[0], wl.off, "sum").clone()
+        b = sr.scan(wl.vals[-1], wl.off, "sum")
+        torch.cuda.synchronize()
+        repeat_ok = bool(torch.equal(a.view(torch.int32), b.view(torch.int32)))
+    if isinstance(wl, ReduceWorkload):
+        ok = True
+        for op in wl.ops:
+            a, _ = sr.reduce(wl.vals[0], wl.off, op)
+            a = a.clone()
+            b, _ = sr.reduce(wl.vals[-1], wl.off, op)
+            torch.cuda.synchronize()
+            ok = ok and bool(torch.equal(a.view(torch.int32), b.view(torch.int32)))
+        repeat_ok = ok
+    if isinstance(wl, RleWorkload):
+        a, _ = sr.reduce(wl.sets[0][1], wl.outs["rle"][2], "sum", num_segments=wl.outs["rle"][3])
+        a = a.clone()
+        b, _ = sr.reduce(wl.sets[-1][1], wl.outs["rle"][2], "sum", num_segments=wl.outs["rle"][3])
+        torch.cuda.synchronize()
+        repeat_ok = bool(torch.equal(a.view(torch.int32), b.view(torch.int32)))
+
+    res = {
+        "workload": DESCRIPTIONS[name],
+        "name": cfg.get("name", name),
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "gelem_per_s": round(gelem, 3),
+        "steps": steps,
+        "ms_per_step": round(elapsed * 1e3 / steps, 5),
+        "bytes_per_step": bytes_step,
+        "input_copies_rotated": len(getattr(wl, "vals", getattr(wl, "sets", getattr(wl, "inputs", [None])))),
+        "dtype": {"rle": "u32/i32", "unique": "u32", "flags": "u32", "search": "f32 (int64 positions)"}.get(
+            name, "f32"),
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "bitwise_repeat": repeat_ok,
+        "kernel_source_hash": src_hash,
+    }
+    del wl
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="message", choices=sorted(DESCRIPTIONS))
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the CPU oracle leg")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="powerlaw", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--also", default=None,
+                    help="comma-separated workloads reported beside the headline (default: the other gated "
+                         "configurations when the headline is powerlaw, else none; '' for none)")
+    ap.add_argument("--also-steps", type=int, default=100, help="timed steps of each --also workload")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0, help="time budget of each CPU oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain device copy of 256 MiB (HBM counter calibration)")
@@ -624,137 +823,48 @@ def main():
 
     import segmented_reduction_amd as sr
 
-    print(f"[bench] generating {args.config} ...", file=sys.stderr, flush=True)
-    wl, cfg = build_workload(args.config, sr, torch)
-    torch.cuda.synchronize()
-    # launches the timing record keeps: at most 4 kernels per call here
-    if args.steps * len(wl.calls) * 4 > 8192:
-        args.steps = 8192 // (4 * len(wl.calls))
+    threads = host_threads()
+    also = GATED if (args.also is None and args.config == "powerlaw") else \
+        [x for x in (args.also or "").split(",") if x and x != args.config]
+    for x in also:
+        if x not in DESCRIPTIONS:
+            ap.error(f"unknown workload in --also: {x}")
 
-    for i in range(args.warmup):
-        wl.step(i)
-    torch.cuda.synchronize()
-
-    # Timed region: K steps, nothing attached to the launches.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        wl.step(args.warmup + i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-
-    # Kernel durations for the roofline: the same K steps again, with every
-    # library kernel launched with a HIP event that the runtime stamps when the
-    # kernel ends on its stream; a streaming kernel's duration is the time
-    # from the end of the kernel before it (the kernels run back to back).
-    # This pass is kept out of the wall-clock figure above.
-    # Stamping an event at a kernel's end leaves the GPU idle for a few
-    # microseconds before the next kernel starts; that idle time is inside
-    # each stop-to-stop duration.  It is taken out per launch as the extra
-    # wall time of this pass over the untimed one, divided by the number of
-    # kernel launches (the kernels themselves are the same).
-    sr.timing_enable(True)
-    sr.timing_read()
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for i in range(args.steps):
-        wl.step(args.warmup + args.steps + i)
-    torch.cuda.synchronize()
-    t3 = time.perf_counter()
-    total_ms, launches, each = sr.timing_read()
-    sr.timing_enable(False)
-    gap_ms = max(0.0, ((t3 - t2) - (t1 - t0)) * 1e3 / (args.steps * wl.kernels_per_step))
-
-    elapsed = t1 - t0
-    ms_per_step = elapsed * 1e3 / args.steps
-    bytes_step = wl.bytes_per_step()
-    value = bytes_step * args.steps / elapsed / 1e9
-    gelem = wl.elems_per_step() * args.steps / elapsed / 1e9
-
-    # per-call streaming-kernel times (launch order repeats every step)
-    ncalls = len(wl.calls)
-    kernels = {}
-    for j, (label, op) in enumerate(wl.calls):
-        times = [t for t in each[j::ncalls] if t >= 0]  # -1: first launch, nothing before it
-        if not times:
-            continue
-        raw_ms = sum(times) / len(times)
-        avg_ms = raw_ms - gap_ms
-        b = wl.call_bytes(label)
-        kernels[label] = {"avg_us": round(avg_ms * 1e3, 2), "event_us": round(raw_ms * 1e3, 2),
-                          "stamp_gap_us": round(gap_ms * 1e3, 2), "launches": len(times), "bytes": b,
-                          "GBps": round(b / (avg_ms * 1e-3) / 1e9, 1),
-                          "frac": round(b / (avg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-    dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
-    dk = kernels[dominant]
-    src_hash = kernel_source_hash(args.config)
-    traffic = load_traffic(args.config, dominant, src_hash)
-    roofline = {"bound": "hbm", "achieved": dk["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": dk["frac"], "traffic": traffic,
-                "kernel": (dominant if dominant.startswith("rle_")
-                           else f"seg_scan_tails ({dominant})" if dominant.endswith("_tails")
-                           else f"{getattr(wl, 'kernel_name', 'seg_reduce_pass1')} ({dominant})"),
-                "algorithmic_bytes_per_launch": dk["bytes"], "avg_launch_us": dk["avg_us"],
-                "timing": "kernel-stamped HIP stop events (hipExtLaunchKernel) on the launch stream, end of "
-                          "previous kernel to end of this one, a second pass of the same K steps, minus the "
-                          "per-launch idle time the stamping adds (extra wall time of that pass / launches)"}
-
-    cpu = None
-    parity = None
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle ...", file=sys.stderr, flush=True)
-        cpu, results = cpu_baseline(wl, args.config, args.cpu_seconds)
-        parity = check_parity(wl, results)
-
-    # bitwise repeat: the rotated copies hold identical inputs
-    repeat_ok = None
-    if isinstance(wl, ScatterWorkload) and len(wl.sets) > 1 and "max" in wl.ops:
-        # float atomic sums may move in the last bits; max and its rows may not
-        a, aa = sr.scatter(wl.sets[0][0], wl.sets[0][1], wl.dim, "max")
-        b, bb = sr.scatter(wl.sets[-1][0], wl.sets[-1][1], wl.dim, "max")
-        torch.cuda.synchronize()
-        repeat_ok = bool(torch.equal(a.view(torch.int32), b.view(torch.int32)) and torch.equal(aa, bb))
-    if isinstance(wl, ScanWorkload) and len(wl.vals) > 1:
-        a = sr.scan(wl.vals[0], wl.off, "sum").clone()
-        b = sr.scan(wl.vals[-1], wl.off, "sum")
-        torch.cuda.synchronize()
-        repeat_ok = bool(torch.equal(a.view(torch.int32), b.view(torch.int32)))
-    if isinstance(wl, ReduceWorkload) and len(wl.vals) > 1:
-        op = wl.ops[0]
-        a, _ = sr.reduce(wl.vals[0], wl.off, op)
-        b, _ = sr.reduce(wl.vals[-1], wl.off, op)
-        torch.cuda.synchronize()
-        repeat_ok = bool(torch.equal(a.view(torch.int32), b.view(torch.int32)))
+    head = measure(args.config, args.steps, args.warmup, args.cpu_seconds, threads, sr, torch,
+                   with_cpu=not args.no_cpu_baseline)
+    others = {}
+    for x in also:
+        others[x] = measure(x, args.also_steps, args.warmup, args.cpu_seconds, threads, sr, torch,
+                            with_cpu=not args.no_cpu_baseline)
 
     line = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": head["value"],
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": head["steps"],
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"rle": "u32/i32", "unique": "u32", "flags": "u32", "search": "f32 (int64 positions)"}.get(
-            args.config, "f32"),
+        "dtype": head["dtype"],
         "data": "synthetic (seeded numpy generators, workloads.py)",
-        "config": {"workload": DESCRIPTIONS[args.config], "name": cfg.get("name", args.config),
-                   "input_copies_rotated": len(getattr(wl, "vals", getattr(wl, "sets", getattr(wl, "inputs",
-                                                                                           [None]))))},
-        "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
-        "gelem_per_s": round(gelem, 3),
-        "bytes_per_step": bytes_step,
-        "roofline": roofline,
-        "kernels": kernels,
-        "cpu_baseline": cpu,
-        "parity": parity,
-        "bitwise_repeat": repeat_ok,
-        "kernel_source_hash": src_hash,
+        "config": {"workload": head["workload"], "name": head["name"],
+                   "input_copies_rotated": head["input_copies_rotated"]},
+        "pct_of_peak": head["pct_of_peak"],
+        "gelem_per_s": head["gelem_per_s"],
+        "bytes_per_step": head["bytes_per_step"],
+        "roofline": head["roofline"],
+        "kernels": head["kernels"],
+        "cpu_baseline": head["cpu_baseline"],
+        "parity": head["parity"],
+        "bitwise_repeat": head["bitwise_repeat"],
+        "kernel_source_hash": head["kernel_source_hash"],
         "accumulate": ("f32 atomic adds in arrival order (not bitwise repeatable); max via packed 64-bit "
-                       "atomic max" if isinstance(wl, ScatterWorkload)
+                       "atomic max" if args.config.startswith("scatter")
                        else "f64 for float sums, wrapping u32 for integer sums"),
+        "configs": {k: {kk: vv for kk, vv in v.items() if kk not in ("unit",)} for k, v in others.items()},
     }
     print(json.dumps(line), flush=True)
 

@@ -93,8 +93,27 @@ class Reduced:
         self.out, self.arg, self.ref, self.mag = out, arg, ref, mag
 
 
-def reduce(values: np.ndarray, offsets: np.ndarray, op: str, lib=None) -> Reduced:
-    """Segmented reduction of ``values`` ([rows] or [rows, F]) over int64 ``offsets``."""
+def segment_ranges(offsets: np.ndarray, parts: int):
+    """Split segments [0, S) into ``parts`` contiguous ranges of about equal
+    row counts (used to run the oracle on several host threads; each segment
+    is still reduced by one sequential pass, so results do not depend on the
+    split)."""
+    s = int(offsets.shape[0]) - 1
+    o0, o1 = int(offsets[0]), int(offsets[-1])
+    cuts = [0]
+    for k in range(1, parts):
+        r = o0 + (o1 - o0) * k // parts
+        cuts.append(min(s, max(cuts[-1], int(np.searchsorted(offsets, r, side="left")))))
+    cuts.append(s)
+    return [(a, b) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+
+
+def reduce(values: np.ndarray, offsets: np.ndarray, op: str, lib=None, threads: int = 1) -> Reduced:
+    """Segmented reduction of ``values`` ([rows] or [rows, F]) over int64 ``offsets``.
+
+    ``threads`` > 1 runs the same C function on that many host threads, each
+    over a contiguous range of segments (segment_ranges); every segment is
+    computed exactly as with one thread."""
     lib = lib or load()
     values = np.ascontiguousarray(values)
     offsets = np.ascontiguousarray(offsets, dtype=np.int64)
@@ -109,9 +128,20 @@ def reduce(values: np.ndarray, offsets: np.ndarray, op: str, lib=None) -> Reduce
     if dt == "f32" and op in ("sum", "mean"):
         ref = np.zeros((s, feat), dtype=np.float64)
         mag = np.zeros((s, feat), dtype=np.float64)
-    rc = lib.oracle_reduce(_ptr(values), DTYPES[dt], feat, _ptr(offsets), s, OPS[op],
-                           _ptr(out), _ptr(arg), _ptr(ref), _ptr(mag))
-    if rc != 0:
+    def run(a, b):
+        def at(x, row):
+            return None if x is None else x.ctypes.data + row * x.strides[0]
+        return lib.oracle_reduce(_ptr(values), DTYPES[dt], feat, offsets.ctypes.data + a * 8, b - a, OPS[op],
+                                 at(out, a), at(arg, a), at(ref, a), at(mag, a))
+
+    if threads <= 1 or s < 2:
+        rcs = [run(0, s)]
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        ranges = segment_ranges(offsets, threads)
+        with ThreadPoolExecutor(max_workers=len(ranges)) as pool:
+            rcs = list(pool.map(lambda ab: run(*ab), ranges))
+    if any(rc != 0 for rc in rcs):
         raise ValueError(f"oracle_reduce rejected dtype={dt} op={op} feat={feat}")
     return Reduced(out, arg, ref, mag)
 

@@ -393,9 +393,9 @@ def timing_enable(enable: bool = True):
     _check(library().segred_timing_enable(1 if enable else 0), "segred_timing_enable")
 
 
-def timing_read(capacity: int = 4096):
+def timing_read(capacity: int = 8192):
     """(total ms, launches, per-launch ms list) of the streaming kernels since the last read:
-    each is the time from the end of the kernel launched before it (-1 for the first)."""
+    each is the kernel's own stop event minus its own start event."""
     ms = ctypes.c_double(0.0)
     n = ctypes.c_int64(0)
     each = (ctypes.c_float * max(capacity, 1))()

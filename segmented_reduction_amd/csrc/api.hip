@@ -40,8 +40,9 @@ constexpr int kMaxTimed = 8192;  // kernel launches recorded between reads
 struct Timing {
     bool on = false;
     int used = 0;
-    hipEvent_t ev[kMaxTimed] = {};   // stop event of each launch, in launch order
-    bool streaming[kMaxTimed] = {};  // launch i is a streaming (first) kernel
+    hipEvent_t start[kMaxTimed] = {};  // start and stop events of each launch, in launch order
+    hipEvent_t stop[kMaxTimed] = {};
+    bool streaming[kMaxTimed] = {};    // launch i is a streaming (first) kernel
     bool created = false;
 };
 Timing g_timing;
@@ -117,11 +118,14 @@ int scratch_acquire(ScratchLease &lease, size_t bytes, hipStream_t stream) {
 
 bool timing_on() { return g_timing.on; }
 
-hipEvent_t timing_stop(bool streaming) {
-    if (!g_timing.on || g_timing.used >= kMaxTimed) return nullptr;
+TimingEvents timing_events(bool streaming) {
+    TimingEvents te;
+    if (!g_timing.on || g_timing.used >= kMaxTimed) return te;
     const int slot = g_timing.used++;
     g_timing.streaming[slot] = streaming;
-    return g_timing.ev[slot];
+    te.start = g_timing.start[slot];
+    te.stop = g_timing.stop[slot];
+    return te;
 }
 
 int64_t shares_override() { return g_shares.load(std::memory_order_relaxed); }
@@ -153,7 +157,8 @@ extern "C" int segred_timing_enable(int enable) {
         // no system-scope cache writeback at each stamp: it would slow the
         // kernels being timed (only this process reads the timestamps)
         for (int i = 0; i < kMaxTimed; ++i)
-            if (hipEventCreateWithFlags(&g_timing.ev[i], hipEventDisableSystemFence) != hipSuccess)
+            if (hipEventCreateWithFlags(&g_timing.start[i], hipEventDisableSystemFence) != hipSuccess ||
+                hipEventCreateWithFlags(&g_timing.stop[i], hipEventDisableSystemFence) != hipSuccess)
                 return SEGRED_ERR_HIP;
         g_timing.created = true;
     }
@@ -168,12 +173,10 @@ extern "C" int segred_timing_read(double *total_ms, int64_t *launches, float *ea
     int64_t n = 0;
     for (int i = 0; i < g_timing.used; ++i) {
         if (!g_timing.streaming[i]) continue;
-        if (hipEventSynchronize(g_timing.ev[i]) != hipSuccess) return SEGRED_ERR_HIP;
-        float ms = -1.f;  // no launch recorded before this one
-        if (i > 0) {
-            if (hipEventElapsedTime(&ms, g_timing.ev[i - 1], g_timing.ev[i]) != hipSuccess) return SEGRED_ERR_HIP;
-            sum += ms;
-        }
+        if (hipEventSynchronize(g_timing.stop[i]) != hipSuccess) return SEGRED_ERR_HIP;
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, g_timing.start[i], g_timing.stop[i]) != hipSuccess) return SEGRED_ERR_HIP;
+        sum += ms;
         if (n < capacity) each_ms[n] = ms;
         ++n;
     }

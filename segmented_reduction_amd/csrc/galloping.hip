@@ -442,22 +442,18 @@ static int gallop_launch(const GArgs &a, hipStream_t st) {
         // a workgroup per record (its tiles fit the workgroup's lanes)
         if (a.S > INT32_MAX) return SEGRED_ERR_UNSUPPORTED;
         if (a.order)
-            hipExtLaunchKernelGGL((gallop_staged<DT, true>), dim3((unsigned)a.S), dim3(kGThreads), 0, st, nullptr,
-                                  timing_stop(true), 0, a);
+            timed_launch_ggl(true, (gallop_staged<DT, true>), dim3((unsigned)a.S), dim3(kGThreads), 0, st, a);
         else
-            hipExtLaunchKernelGGL((gallop_staged<DT, false>), dim3((unsigned)a.S), dim3(kGThreads), 0, st, nullptr,
-                                  timing_stop(true), 0, a);
+            timed_launch_ggl(true, (gallop_staged<DT, false>), dim3((unsigned)a.S), dim3(kGThreads), 0, st, a);
         return hipGetLastError() == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
     }
     const int64_t lanes = a.S * a.tiles;
     const int64_t wgs = (lanes + kGThreads - 1) / kGThreads;
     if (wgs > INT32_MAX) return SEGRED_ERR_UNSUPPORTED;
     if (a.order)
-        hipExtLaunchKernelGGL((gallop_kernel<DT, true>), dim3((unsigned)wgs), dim3(kGThreads), 0, st, nullptr,
-                              timing_stop(true), 0, a);
+        timed_launch_ggl(true, (gallop_kernel<DT, true>), dim3((unsigned)wgs), dim3(kGThreads), 0, st, a);
     else
-        hipExtLaunchKernelGGL((gallop_kernel<DT, false>), dim3((unsigned)wgs), dim3(kGThreads), 0, st, nullptr,
-                              timing_stop(true), 0, a);
+        timed_launch_ggl(true, (gallop_kernel<DT, false>), dim3((unsigned)wgs), dim3(kGThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
 }
 
@@ -484,7 +480,7 @@ extern "C" int segred_galloping_search(const void *values, int32_t dtype, int64_
         (out && !aligned(out, 8)))
         return SEGRED_ERR_INVALID_ARGUMENT;
     if (!preserve_validation) {
-        hipExtLaunchKernelGGL(gallop_clear, dim3(1), dim3(64), 0, stream, nullptr, timing_stop(false), 0, validation);
+        timed_launch_ggl(false, gallop_clear, dim3(1), dim3(64), 0, stream, validation);
         if (hipGetLastError() != hipSuccess) return SEGRED_ERR_HIP;
     }
     GArgs a{};

@@ -44,12 +44,28 @@ struct ScratchLease {
 int scratch_acquire(ScratchLease &lease, size_t bytes, hipStream_t stream);
 
 // Launch timing (segred_timing_enable): while it is on, every kernel the
-// library launches carries a stop event that the runtime stamps when that
-// kernel ends (hipExtLaunchKernel); timing_stop returns the next one (null
-// when timing is off or the record is full).  A streaming kernel's duration
-// is the time from the end of the launch before it to its own end.
+// library launches carries a start and a stop event that the runtime stamps
+// when that kernel begins and ends (hipExtLaunchKernel); otherwise both are
+// null.  A streaming kernel's duration is its own stop minus its own start,
+// so idle time between launches is not counted.
+struct TimingEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
 bool timing_on();
-hipEvent_t timing_stop(bool streaming);
+TimingEvents timing_events(bool streaming);
+
+// Kernel launches with the timing events of the record.
+inline hipError_t timed_launch(bool streaming, const void *kernel, dim3 grid, dim3 block, void **params,
+                               size_t lds, hipStream_t st) {
+    const TimingEvents te = timing_events(streaming);
+    return hipExtLaunchKernel(kernel, grid, block, params, lds, st, te.start, te.stop, 0);
+}
+template <typename F, typename... Args>
+inline void timed_launch_ggl(bool streaming, F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t st,
+                             Args... args) {
+    const TimingEvents te = timing_events(streaming);
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, st, te.start, te.stop, 0, args...);
+}
 
 // Process-wide share override (0 = default).
 int64_t shares_override();

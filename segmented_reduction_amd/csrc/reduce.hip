@@ -1259,12 +1259,10 @@ static int run(KArgs k, hipStream_t st, void *fixed_scratch) {
     k.tval = k.hval + (size_t)ns * (size_t)k.F;
 
     void *params[] = {&k};
-    hipError_t e = hipExtLaunchKernel(pk.kernel, dim3((unsigned)(nw / 4)), dim3(256), params, 0, st, nullptr,
-                                      timing_stop(true), 0);
+    hipError_t e = timed_launch(true, pk.kernel, dim3((unsigned)(nw / 4)), dim3(256), params, 0, st);
     if (e == hipSuccess)
-        e = hipExtLaunchKernel(reinterpret_cast<const void *>(&seg_reduce_pass2<DT, OP>),
-                               dim3((unsigned)((ns + 3) / 4)), dim3(256), params, 0, st, nullptr,
-                               timing_stop(false), 0);
+        e = timed_launch(false, reinterpret_cast<const void *>(&seg_reduce_pass2<DT, OP>),
+                         dim3((unsigned)((ns + 3) / 4)), dim3(256), params, 0, st);
     return e == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
 }
 

@@ -290,14 +290,14 @@ int rle_launch(const uint32_t *keys, int64_t n, uint32_t *values, uint32_t *leng
     uint64_t *tmask = reinterpret_cast<uint64_t *>(tnext + tiles);  // [tiles][16][4] start bits
 
     if (tiles > 0)
-        hipExtLaunchKernelGGL(rle_count<MODE>, dim3((unsigned)tiles), dim3(kRleThreads), 0, stream, nullptr,
-                              timing_stop(true), 0, keys, n, tcount, tfirst, tmask);
-    hipExtLaunchKernelGGL(rle_scan<MODE>, dim3(1), dim3(kScanThreads), 0, stream, nullptr, timing_stop(false), 0,
-                          tiles, n, (const int64_t *)tcount, (const int64_t *)tfirst, tbase, tnext, count, offsets);
+        timed_launch_ggl(true, rle_count<MODE>, dim3((unsigned)tiles), dim3(kRleThreads), 0, stream, keys, n, tcount,
+                         tfirst, tmask);
+    timed_launch_ggl(false, rle_scan<MODE>, dim3(1), dim3(kScanThreads), 0, stream, tiles, n,
+                     (const int64_t *)tcount, (const int64_t *)tfirst, tbase, tnext, count, offsets);
     if (tiles > 0)
-        hipExtLaunchKernelGGL(rle_materialize<MODE>, dim3((unsigned)tiles), dim3(kRleThreads), 0, stream, nullptr,
-                              timing_stop(true), 0, keys, n, (const int64_t *)tbase, (const int64_t *)tnext,
-                              (const uint64_t *)tmask, values, lengths, offsets);
+        timed_launch_ggl(true, rle_materialize<MODE>, dim3((unsigned)tiles), dim3(kRleThreads), 0, stream, keys, n,
+                         (const int64_t *)tbase, (const int64_t *)tnext, (const uint64_t *)tmask, values, lengths,
+                         offsets);
     return hipGetLastError() == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
 }
 

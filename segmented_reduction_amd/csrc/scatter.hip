@@ -631,14 +631,14 @@ int scatter_launch(const ScArgs &a, int64_t *arg, hipStream_t st) {
         const unsigned lds = (unsigned)a.priv_lds;
         if constexpr (DT == DT_F32 && (OP == OP_SUM || OP == OP_MEAN)) {
             if (a.priv_waves)
-                hipExtLaunchKernelGGL((scatter_private<DT, OP, true>), dim3((unsigned)a.priv_grid), dim3(kScThreads),
-                                      lds, st, nullptr, timing_stop(true), 0, a);
+                timed_launch_ggl(true, (scatter_private<DT, OP, true>), dim3((unsigned)a.priv_grid),
+                                 dim3(kScThreads), lds, st, a);
             else
-                hipExtLaunchKernelGGL((scatter_private<DT, OP, false>), dim3((unsigned)a.priv_grid), dim3(kScThreads),
-                                      lds, st, nullptr, timing_stop(true), 0, a);
+                timed_launch_ggl(true, (scatter_private<DT, OP, false>), dim3((unsigned)a.priv_grid),
+                                 dim3(kScThreads), lds, st, a);
         } else {
-            hipExtLaunchKernelGGL((scatter_private<DT, OP, false>), dim3((unsigned)a.priv_grid), dim3(kScThreads), lds,
-                                  st, nullptr, timing_stop(true), 0, a);
+            timed_launch_ggl(true, (scatter_private<DT, OP, false>), dim3((unsigned)a.priv_grid), dim3(kScThreads),
+                             lds, st, a);
         }
         e = hipGetLastError();
         const int64_t T = cells + (OP == OP_MEAN ? a.dim : 0);
@@ -648,8 +648,8 @@ int scatter_launch(const ScArgs &a, int64_t *arg, hipStream_t st) {
             const int64_t per = (n + 63) / 64, nparts = (n + per - 1) / per;
             const int64_t units = (T + 63) / 64 * nparts;
             const unsigned ga = (unsigned)std::max<int64_t>(1, std::min<int64_t>((units + 3) / 4, 8192));
-            hipExtLaunchKernelGGL((scatter_private_fold_a<DT, OP>), dim3(ga), dim3(kScThreads), 0, st, nullptr,
-                                  timing_stop(false), 0, a, n, T, per, nparts, a.part);
+            timed_launch_ggl(false, (scatter_private_fold_a<DT, OP>), dim3(ga), dim3(kScThreads), 0, st, a, n, T,
+                             per, nparts, a.part);
             e = hipGetLastError();
             rows = a.part;
             n = nparts;
@@ -657,25 +657,22 @@ int scatter_launch(const ScArgs &a, int64_t *arg, hipStream_t st) {
         if (e == hipSuccess) {
             // one wave per output cell
             const unsigned fg = (unsigned)std::max<int64_t>(1, std::min<int64_t>((cells + 3) / 4, 8192));
-            hipExtLaunchKernelGGL((scatter_private_fold_b<DT, OP>), dim3(fg), dim3(kScThreads), 0, st, nullptr,
-                                  timing_stop(false), 0, a, rows, n, T, arg);
+            timed_launch_ggl(false, (scatter_private_fold_b<DT, OP>), dim3(fg), dim3(kScThreads), 0, st, a, rows, n,
+                             T, arg);
             e = hipGetLastError();
         }
         return e == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
     } else if (wgs > 0) {
         if (a.lg == 0)
-            hipExtLaunchKernelGGL((scatter_kernel<DT, OP, true>), dim3((unsigned)wgs), dim3(kScThreads), 0, st,
-                                  nullptr, timing_stop(true), 0, a);
+            timed_launch_ggl(true, (scatter_kernel<DT, OP, true>), dim3((unsigned)wgs), dim3(kScThreads), 0, st, a);
         else
-            hipExtLaunchKernelGGL((scatter_kernel<DT, OP, false>), dim3((unsigned)wgs), dim3(kScThreads), 0, st,
-                                  nullptr, timing_stop(true), 0, a);
+            timed_launch_ggl(true, (scatter_kernel<DT, OP, false>), dim3((unsigned)wgs), dim3(kScThreads), 0, st, a);
         e = hipGetLastError();
     }
     if (e == hipSuccess && OP != OP_SUM) {
         const int64_t cells = a.dim * a.F;
         const unsigned grid = (unsigned)std::min<int64_t>((cells + kScThreads - 1) / kScThreads, 4096);
-        hipExtLaunchKernelGGL((scatter_finish<DT, OP>), dim3(grid), dim3(kScThreads), 0, st, nullptr,
-                              timing_stop(false), 0, a, arg);
+        timed_launch_ggl(false, (scatter_finish<DT, OP>), dim3(grid), dim3(kScThreads), 0, st, a, arg);
         e = hipGetLastError();
     }
     return e == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
@@ -787,16 +784,15 @@ extern "C" int segred_scatter_reduce(const void *values, int32_t dtype, int64_t 
     } else if (word_op) {
         a.words = arg ? reinterpret_cast<uint64_t *>(arg) : static_cast<uint64_t *>(scratch.ptr);
         const uint64_t empty = op == SEGRED_MAX ? kEmptyWord<OP_MAX> : kEmptyWord<OP_MIN>;
-        hipExtLaunchKernelGGL(scatter_init, dim3(fill_grid(cells)), dim3(kScThreads), 0, stream, nullptr,
-                              timing_stop(false), 0, (uint32_t *)nullptr, (int64_t)0, 0u, a.words, cells, empty);
+        timed_launch_ggl(false, scatter_init, dim3(fill_grid(cells)), dim3(kScThreads), 0, stream,
+                         (uint32_t *)nullptr, (int64_t)0, 0u, a.words, cells, empty);
     } else {
         if (op == SEGRED_MEAN) a.counts = static_cast<uint32_t *>(scratch.ptr);
-        hipExtLaunchKernelGGL(scatter_init, dim3(fill_grid(cells)), dim3(kScThreads), 0, stream, nullptr,
-                              timing_stop(false), 0, a.out, cells, 0u, (uint64_t *)nullptr, (int64_t)0, 0ull);
+        timed_launch_ggl(false, scatter_init, dim3(fill_grid(cells)), dim3(kScThreads), 0, stream, a.out, cells, 0u,
+                         (uint64_t *)nullptr, (int64_t)0, 0ull);
         if (op == SEGRED_MEAN && hipGetLastError() == hipSuccess)
-            hipExtLaunchKernelGGL(scatter_init, dim3(fill_grid(dim_size)), dim3(kScThreads), 0, stream, nullptr,
-                                  timing_stop(false), 0, a.counts, dim_size, 0u, (uint64_t *)nullptr, (int64_t)0,
-                                  0ull);
+            timed_launch_ggl(false, scatter_init, dim3(fill_grid(dim_size)), dim3(kScThreads), 0, stream, a.counts,
+                             dim_size, 0u, (uint64_t *)nullptr, (int64_t)0, 0ull);
     }
     if (hipGetLastError() != hipSuccess) return SEGRED_ERR_HIP;
     switch (dtype) {
@@ -824,19 +820,18 @@ extern "C" int segred_offsets_from_index(const int64_t *index, int64_t rows, int
     int64_t *tbase = tsum + tiles;
     int64_t *counts = offsets + 1;
 
-    hipExtLaunchKernelGGL(scatter_init, dim3(fill_grid(dim_size + 1)), dim3(kScThreads), 0, stream, nullptr,
-                          timing_stop(false), 0, (uint32_t *)nullptr, (int64_t)0, 0u,
-                          reinterpret_cast<uint64_t *>(offsets), dim_size + 1, 0ull);
+    timed_launch_ggl(false, scatter_init, dim3(fill_grid(dim_size + 1)), dim3(kScThreads), 0, stream,
+                     (uint32_t *)nullptr, (int64_t)0, 0u, reinterpret_cast<uint64_t *>(offsets), dim_size + 1, 0ull);
     if (wgs > 0 && dim_size > 0)
-        hipExtLaunchKernelGGL(index_count, dim3((unsigned)wgs), dim3(kScThreads), 0, stream, nullptr,
-                              timing_stop(true), 0, index, rows, dim_size, reinterpret_cast<uint64_t *>(counts));
+        timed_launch_ggl(true, index_count, dim3((unsigned)wgs), dim3(kScThreads), 0, stream, index, rows, dim_size,
+                         reinterpret_cast<uint64_t *>(counts));
     if (tiles > 0) {
-        hipExtLaunchKernelGGL(count_tiles, dim3((unsigned)tiles), dim3(kCountThreads), 0, stream, nullptr,
-                              timing_stop(false), 0, (const int64_t *)counts, dim_size, tsum);
-        hipExtLaunchKernelGGL(count_scan, dim3(1), dim3(kCountScanThreads), 0, stream, nullptr, timing_stop(false), 0,
-                              (const int64_t *)tsum, tiles, tbase);
-        hipExtLaunchKernelGGL(count_apply, dim3((unsigned)tiles), dim3(kCountThreads), 0, stream, nullptr,
-                              timing_stop(false), 0, counts, dim_size, (const int64_t *)tbase);
+        timed_launch_ggl(false, count_tiles, dim3((unsigned)tiles), dim3(kCountThreads), 0, stream,
+                         (const int64_t *)counts, dim_size, tsum);
+        timed_launch_ggl(false, count_scan, dim3(1), dim3(kCountScanThreads), 0, stream, (const int64_t *)tsum,
+                         tiles, tbase);
+        timed_launch_ggl(false, count_apply, dim3((unsigned)tiles), dim3(kCountThreads), 0, stream, counts, dim_size,
+                         (const int64_t *)tbase);
     }
     return hipGetLastError() == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
 }

@@ -451,9 +451,9 @@ static int scan_run(ScanArgs k, hipStream_t st) {
     if (blocks > INT32_MAX) return SEGRED_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)blocks), block(256);
     void *params[] = {&k};
-    hipError_t e = hipExtLaunchKernel(kern.first, grid, block, params, 0, st, nullptr, timing_stop(true), 0);
+    hipError_t e = timed_launch(true, kern.first, grid, block, params, 0, st);
     if (e == hipSuccess)
-        e = hipExtLaunchKernel(kern.second, grid, block, params, 0, st, nullptr, timing_stop(true), 0);
+        e = timed_launch(true, kern.second, grid, block, params, 0, st);
     return e == hipSuccess ? SEGRED_OK : SEGRED_ERR_HIP;
 }
 

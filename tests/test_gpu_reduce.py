@@ -267,3 +267,38 @@ def test_one_dimensional_weighted_shares(kind):
             gu.say(f"weighted shares kind={kind} op={op} shares={shares}")
             out, arg = gu.run_gpu(vals, off, op, shares=shares)
             gu.assert_parity(vals, off, op, out, arg, orc=orc, what=f"weighted shares={shares}")
+
+
+@pytest.mark.parametrize("feat", [1, 32, 65, 100, 260])
+@pytest.mark.parametrize("kind", ["u32", "f32"])
+def test_values_end_with_their_buffer(kind, feat):
+    """No unread rows after the last offset, and the values view ends exactly
+    at the end of its tensor's storage (a multiple of 2 MiB, so the caching
+    allocator has no slack to hide a read past it): every kernel's last
+    chunk or part must stop at offsets[S]."""
+    off, vals = W.ragged(seed=300 + feat, segments=1500, mean_len=9, feat=feat, dtype=kind, empty_frac=0.1,
+                         base=0, tail_rows=0, long_segment=2000)
+    rows = int(off[-1])
+    elems = rows * feat
+    total = -(-(elems * 4) // (2 << 20)) * (2 << 20) // 4
+    import segmented_reduction_amd as sr
+    torch_dt = {"u32": torch.int32, "f32": torch.float32}[kind]
+    buf = torch.empty(total, dtype=torch_dt, device="cuda")
+    view = buf[total - elems:]
+    view.copy_(torch.from_numpy(vals.reshape(-1).view(np.int32 if kind == "u32" else np.float32)).cuda())
+    v = view.view(torch.uint32 if kind == "u32" else torch.float32).reshape((rows,) if feat == 1 else (rows, feat))
+    o = gu.to_gpu(off)
+    for op in ("sum", "max") + (("mean",) if kind == "f32" else ()):
+        for shares in (None, 3, 64):
+            gu.say(f"end-of-buffer kind={kind} F={feat} op={op} shares={shares}")
+            if shares:
+                sr.set_shares(shares)
+            try:
+                out, arg = sr.reduce(v, o, op)
+                torch.cuda.synchronize()
+            finally:
+                sr.set_shares(0)
+            s = len(off) - 1
+            gu.assert_parity(vals, off, op, out.cpu().numpy().reshape(s, -1),
+                             arg.cpu().numpy().reshape(s, -1) if arg is not None else None,
+                             what=f"end-of-buffer F={feat} shares={shares}")
