@@ -38,7 +38,6 @@
 // Rows whose index lies outside [0, dim_size) are skipped: they take part in
 // no output (and no memory outside the outputs is touched for them).
 #include <algorithm>
-#include <map>
 
 #include "internal.hpp"
 #include "keys.hpp"
@@ -602,22 +601,11 @@ __global__ __launch_bounds__(kCountThreads) void count_apply(int64_t *counts, in
 
 // Compute units of the current device (cached per device; 256 if the query
 // fails).
-static int64_t device_cus() {
-    static std::mutex mu;
-    static std::map<int, int64_t> cache;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    std::lock_guard<std::mutex> lk(mu);
-    auto it = cache.find(dev);
-    if (it != cache.end()) return it->second;
-    int cus = 0;
-    const int64_t n = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0
-                          ? cus
-                          : 256;
-    (void)hipGetLastError();
-    cache[dev] = n;
-    return n;
-}
+// CUs the private-copy grid is sized for: those of a whole MI355X, a
+// constant rather than the current device's count, so the fixed-order float
+// sums of that path are the same on every device (a smaller device runs the
+// same workgroups in more rounds).
+constexpr int64_t kGridCus = 256;
 
 template <int DT, int OP>
 int scatter_launch(const ScArgs &a, int64_t *arg, hipStream_t st) {
@@ -746,7 +734,7 @@ extern "C" int segred_scatter_reduce(const void *values, int32_t dtype, int64_t 
         a.priv_lds = (int)(waves ? cells * 4 * (kScThreads / 64) + count_bytes : priv_bytes);
         const int64_t per_wave = (int64_t)kScSteps * (64 >> lg);
         const int64_t wgs = ((a.items + per_wave - 1) / per_wave + kScThreads / 64 - 1) / (kScThreads / 64);
-        const int64_t cus = device_cus();
+        const int64_t cus = kGridCus;
         const int64_t resident = cus * std::min<int64_t>(kWgPerCu, kLdsPerCu / a.priv_lds);
         a.priv_grid = std::max<int64_t>(
             1, std::min<int64_t>({wgs, resident, std::max<int64_t>(cus, elems / (8 * cells))}));

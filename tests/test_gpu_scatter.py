@@ -319,3 +319,53 @@ def test_scatter_full_size(feat):
     got = sr.offsets_from_index(gu.to_gpu(srt), dim)
     torch.cuda.synchronize()
     assert np.array_equal(got.cpu().numpy(), oracle.offsets_from_index(srt, dim))
+
+
+# ---------------------------------------------------------------- exact float sums on every path
+
+# (rows, outputs, features, path the call takes): many outputs -> one global
+# atomic per element; few outputs (one copy fits 32 KB, >= 128 elements per
+# output cell) -> private LDS copies with LDS atomics (F < 8) or one copy per
+# wave with fixed-order adds (float sums of F >= 8).
+EXACT_CASES = [
+    (400_000, 10_000, 1, "element atomics"),
+    (400_000, 10_000, 4, "element atomics"),
+    (200_000, 5_000, 16, "element atomics"),
+    (300_000, 100, 1, "private copies, LDS atomics"),
+    (200_000, 200, 4, "private copies, LDS atomics"),
+    (100_000, 100, 16, "private copies, one per wave"),
+    (100_000, 8, 64, "private copies, one per wave"),
+]
+
+
+@pytest.mark.parametrize("rows,dim,feat,path", EXACT_CASES)
+def test_integer_valued_float_sums_are_exact(rows, dim, feat, path):
+    """Float32 values in {-3..3} whose partial sums stay below 2^24 add
+    exactly in any order: on every path the scatter sum must equal the
+    oracle's bit for bit, so a dropped, doubled or misrouted row fails."""
+    rng = np.random.default_rng(rows + dim + feat)
+    idx = rng.integers(0, dim, rows, dtype=np.int64)
+    shape = (rows,) if feat == 1 else (rows, feat)
+    vals = rng.integers(-3, 4, shape).astype(np.float32)
+    assert np.bincount(idx, minlength=dim).max() * 3 < 2 ** 24
+    gu.say(f"scatter exact sum {path} rows={rows} dim={dim} F={feat}")
+    out, _ = _run(vals, idx, dim, "sum")
+    orc = oracle.scatter(vals, idx, dim, "sum")
+    assert np.array_equal(out.view(np.uint32), orc.out.view(np.uint32)), path
+    assert np.array_equal(out.astype(np.float64), orc.ref), path
+
+
+@pytest.mark.parametrize("rows,dim,feat", [(100_000, 100, 16), (100_000, 8, 64), (60_000, 30, 32)])
+def test_fixed_order_float_sums_meet_the_reduction_bar(rows, dim, feat):
+    """The per-wave-copy path adds in a fixed order: its float sums meet the
+    segmented reduction's bar, 1e-5 * sum|x| + 1e-6 per output, and repeat
+    bit for bit."""
+    rng = np.random.default_rng(rows + feat)
+    idx = rng.integers(0, dim, rows, dtype=np.int64)
+    vals = rng.standard_normal((rows, feat), dtype=np.float32)
+    gu.say(f"scatter fixed-order sum rows={rows} dim={dim} F={feat}")
+    out, _ = _run(vals, idx, dim, "sum")
+    orc = oracle.scatter(vals, idx, dim, "sum")
+    assert (np.abs(out.astype(np.float64) - orc.ref) <= 1e-5 * orc.mag + 1e-6).all()
+    again, _ = _run(vals, idx, dim, "sum")
+    assert np.array_equal(out.view(np.uint32), again.view(np.uint32))
