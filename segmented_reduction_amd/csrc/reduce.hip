@@ -970,23 +970,11 @@ void seg_reduce_flat(const KArgs a) {
             // local (key, V - t) word -> (key, ~row code)
             if (acc != 0) xs = (acc & 0xFFFFFFFF00000000ull) | ~(rel0 + (uint32_t)V - (uint32_t)acc);
         }
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int src = (lane - o) & 63;
-            const bool pf = lane_get(fl, src);
-            const lacc_t px = lane_get(xs, src);
-            if (lane >= o) {
-                if (!fl) xs = lcomb(px, xs);
-                fl = fl || pf;
-            }
-        }
+        seg_scan_wave(xs, fl, lacc_t{}, lcomb);
         const acc_t cm = to_max(carry);
-        lacc_t ex = lane_get(xs, (lane - 1) & 63);
-        bool fx = lane_get(fl, (lane - 1) & 63);
-        if (lane == 0) {
-            ex = lacc_t{};
-            fx = false;
-        }
+        // the scan up to the lane before (lane 0: nothing)
+        const lacc_t ex = dpp_move<kDppWaveShr1>(lacc_t{}, xs);
+        const bool fx = dpp32<kDppWaveShr1>(0u, fl ? 1u : 0u) != 0u;
         const acc_t cin = fx ? widen(ex) : acomb(cm, widen(ex));
         sc[lane] = R::to_slot(cin);
         wave_lds_sync();

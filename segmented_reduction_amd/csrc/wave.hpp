@@ -38,6 +38,59 @@ __device__ __forceinline__ bool lane_get(bool v, int src) {
     return lane_get((uint32_t)v, src) != 0u;
 }
 
+// DPP moves (data-parallel primitives of the gfx9 family): a VALU operand
+// taken from another lane of the same 16-lane row, or broadcast from the
+// last lane of a row, in the instruction itself -- no LDS round trip as for
+// ds_bpermute.  Lanes without a source (or in rows the row mask leaves out)
+// receive `old`.
+enum : int {
+    kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118,
+    kDppWaveShr1 = 0x138, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143
+};
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp32(uint32_t old, uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_move(float old, float v) {
+    return __uint_as_float(dpp32<CTRL, ROW_MASK>(__float_as_uint(old), __float_as_uint(v)));
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t old, uint32_t v) {
+    return dpp32<CTRL, ROW_MASK>(old, v);
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint64_t dpp_move(uint64_t old, uint64_t v) {
+    const uint32_t lo = dpp32<CTRL, ROW_MASK>((uint32_t)old, (uint32_t)v);
+    const uint32_t hi = dpp32<CTRL, ROW_MASK>((uint32_t)(old >> 32), (uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Segmented inclusive scan across the 64 lanes: on return lane l holds
+// comb over the values of lanes k..l in lane order, k the last lane <= l
+// whose flag was set (0 if none), and its flag is the OR of flags 0..l.
+// comb(a, b) joins an earlier part a and a later part b; `id` is its
+// identity.  Four in-row steps (shifts by 1, 2, 4, 8), then the rows' last
+// lanes are broadcast into the next row (rows 1, 3) and lane 31 into rows 2
+// and 3: six steps, all DPP.
+template <typename T, typename Comb>
+__device__ __forceinline__ void seg_scan_wave(T &x, bool &f, T id, Comb comb) {
+#define SEGRED_SCAN_STEP(CTRL, RM)                                     \
+    {                                                                  \
+        const T px = dpp_move<CTRL, RM>(id, x);                        \
+        const uint32_t pf = dpp32<CTRL, RM>(0u, f ? 1u : 0u);          \
+        if (!f) x = comb(px, x);                                       \
+        f = f || pf != 0u;                                             \
+    }
+    SEGRED_SCAN_STEP(kDppRowShr1, 0xF)
+    SEGRED_SCAN_STEP(kDppRowShr2, 0xF)
+    SEGRED_SCAN_STEP(kDppRowShr4, 0xF)
+    SEGRED_SCAN_STEP(kDppRowShr8, 0xF)
+    SEGRED_SCAN_STEP(kDppRowBcast15, 0xA)
+    SEGRED_SCAN_STEP(kDppRowBcast31, 0xC)
+#undef SEGRED_SCAN_STEP
+}
+
 // Make LDS writes of this wave visible to the other lanes of the same wave.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
