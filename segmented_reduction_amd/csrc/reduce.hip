@@ -901,8 +901,17 @@ void seg_reduce_flat(const KArgs a) {
 #pragma unroll
         for (int b = 0; b < NB; ++b)
             if (more) take(b, E[b]);
-        // dense stretches: further ends, fetched on demand
-        for (int b = NB; more && b < EC / 64; ++b) take(b, off[min(ic + 1 + b * 64 + lane, S)]);
+        // Dense stretches: the chunk's further ends, all of their loads
+        // issued together once the preloaded ones are used up (one round
+        // trip instead of one per batch of 64).
+        if (more) {
+            int64_t Ex[EC / 64 - NB];
+#pragma unroll
+            for (int b = NB; b < EC / 64; ++b) Ex[b - NB] = off[min(ic + 1 + b * 64 + lane, S)];
+#pragma unroll
+            for (int b = NB; b < EC / 64; ++b)
+                if (more) take(b, Ex[b - NB]);
+        }
         wave_lds_sync();
         // With EC ends the chunk stops at the last of them.
         const int rows = ne == EC ? (int)__builtin_amdgcn_readfirstlane(se[EC - 1]) : (int)rows_avail;
