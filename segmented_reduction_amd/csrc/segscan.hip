@@ -334,19 +334,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void s
                 p[v] = (v == 0 || ((fl >> v) & 1u)) ? xv : O::comb(p[v - 1], xv);
             }
             // segmented scan of (lane total, lane has a start) across groups
+            // (1-D: across all 64 lanes, by DPP)
             acc_t T = p[V - 1];
             bool has = fl != 0;
+            if constexpr (L == 1) {
+                seg_scan_wave(T, has, O::id(), [](acc_t a, acc_t b) { return O::comb(a, b); });
+            } else {
 #pragma unroll
-            for (int o = L; o < 64; o <<= 1) {
-                const acc_t y = lane_get(T, (lane - o) & 63);
-                const bool yh = lane_get(has, (lane - o) & 63);
-                if (lane >= o && !has) {
-                    T = O::comb(y, T);
-                    has = yh;
+                for (int o = L; o < 64; o <<= 1) {
+                    const acc_t y = lane_get(T, (lane - o) & 63);
+                    const bool yh = lane_get(has, (lane - o) & 63);
+                    if (lane >= o && !has) {
+                        T = O::comb(y, T);
+                        has = yh;
+                    }
                 }
             }
             const acc_t lane_incl = has ? T : O::comb(carry, T);
-            const acc_t prev = lane_get(lane_incl, (lane - L) & 63);
+            acc_t prev;
+            if constexpr (L == 1) prev = dpp_move<kDppWaveShr1>(O::id(), lane_incl);
+            else prev = lane_get(lane_incl, (lane - L) & 63);
             const acc_t E = g == 0 ? carry : prev;  // everything before this lane's first element
             uint32_t ob[V];
             acc_t q = E;

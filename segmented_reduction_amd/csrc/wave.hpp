@@ -65,6 +65,11 @@ __device__ __forceinline__ uint64_t dpp_move(uint64_t old, uint64_t v) {
     const uint32_t hi = dpp32<CTRL, ROW_MASK>((uint32_t)(old >> 32), (uint32_t)(v >> 32));
     return ((uint64_t)hi << 32) | lo;
 }
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_move(double old, double v) {
+    return __longlong_as_double((long long)dpp_move<CTRL, ROW_MASK>((uint64_t)__double_as_longlong(old),
+                                                                     (uint64_t)__double_as_longlong(v)));
+}
 
 // Segmented inclusive scan across the 64 lanes: on return lane l holds
 // comb over the values of lanes k..l in lane order, k the last lane <= l
