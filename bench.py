@@ -342,7 +342,10 @@ class RunsWorkload(Workload):
         return self.count * 4 + 8 if self.mode == "unique" else (self.count + 1) * 8 + 8
 
     def call_bytes(self, label):
-        return self.n * 4 + (self.out_bytes() if label == "rle_materialize" else 0)
+        if label == "rle_count":
+            return self.n * 4  # every key (flag) read once
+        # the outputs written, and for unique the key of each run read again
+        return self.out_bytes() + (self.count * 4 if self.mode == "unique" else 0)
 
     def bytes_per_step(self):
         return self.n * 4 + self.out_bytes()
@@ -525,15 +528,20 @@ def cpu_baseline(wl, name, budget_s, threads):
             t += time.perf_counter() - t0
             reps += 1
         sample = f"full workload ({name}), all {len(wl.ops)} ops, {reps} rep(s), {threads} threads"
-        # one thread on the first 1/16 of the segments
+        # one thread on a leading sample of the segments: 1/16 of them, or
+        # more (up to all) until it takes half a second
         s_all = wl.host_off.size - 1
         s_end = max(1, s_all // 16)
-        off_s = wl.host_off[: s_end + 1]
-        rows_s = int(off_s[-1] - off_s[0])
-        t1 = time.perf_counter()
-        for op in wl.ops:
-            oracle.reduce(wl.host_vals, off_s, op, lib=lib)
-        ts = time.perf_counter() - t1
+        while True:
+            off_s = wl.host_off[: s_end + 1]
+            rows_s = int(off_s[-1] - off_s[0])
+            t1 = time.perf_counter()
+            for op in wl.ops:
+                oracle.reduce(wl.host_vals, off_s, op, lib=lib)
+            ts = time.perf_counter() - t1
+            if ts >= 0.5 or s_end == s_all:
+                break
+            s_end = min(s_all, s_end * 4)
         b = sum(reduce_bytes(rows_s, wl.feat, s_end, op) for op in wl.ops)
         single = {"value": round(b / ts / 1e9, 3), "unit": "GB/s", "cores": 1,
                   "sample": f"first {s_end} of {s_all} segments ({rows_s} rows), all {len(wl.ops)} ops",

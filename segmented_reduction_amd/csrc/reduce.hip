@@ -9,27 +9,36 @@
 // Work partition.  The rows and the segment ends are merged into one
 // sequence (a segment's rows, then its end), the merge-path view of
 // Merrill & Garland's merge-based SpMV that the graph-reduce README cites.
-// The sequence is cut into NW equal shares, one per resident wave; the four
-// waves of a workgroup find their shares' (segment, row) coordinates with a
-// joint search over the offsets.  Long or skewed segments are therefore
-// spread over many waves instead of serialising on one.
+// The sequence is cut into NW equal shares, one per wave (NW is a constant
+// of each kernel: one share per wave of a whole MI355X); the four waves of
+// a workgroup find their shares' (segment, row) coordinates with a joint
+// search over the offsets.  Long or skewed segments are therefore spread
+// over many waves instead of serialising on one.
 //
-// Inside a share the wave walks chunks.  For rows of F >= 2 features each
-// lane owns one feature; a chunk's rows are split into G groups of V
-// consecutive rows (G = 1 for F >= 64, where segment control is
-// wave-uniform); a group walks its rows in order, finishing every segment
-// that ends inside it, and a segmented scan over the groups completes the
-// segments cut by group and chunk boundaries.  For 1-D values a chunk is 2048
-// elements staged through LDS, 32 consecutive ones per lane, reduced by one
-// branch-free pass per lane over reset masks (see seg_reduce_flat).  Segments
-// cut by a share boundary leave one partial per share in scratch; a second
-// kernel combines them in share order.  Every summation order is a fixed
-// function of the offsets and NW, so results repeat bit for bit; no atomic
-// operation touches global memory (the only atomic is a bit-OR in LDS).
+// Inside a share:
+//  - rows of at most 128 bytes (seg_reduce_team): the wave's share is cut
+//    again into equal parts, one per team of L lanes (one row), and each
+//    team walks its part row by row with its own accumulators and queue of
+//    segment ends; the teams' partials of cut segments are folded in team
+//    order at the end;
+//  - wider rows (seg_reduce_rows): the wave walks chunks of G groups x V
+//    consecutive rows; a group walks its rows in order, finishing every
+//    segment that ends inside it, and a segmented scan over the groups
+//    completes the segments cut by group and chunk boundaries;
+//  - 1-D values (seg_reduce_flat): a chunk is 2048 elements staged through
+//    LDS, 32 consecutive ones per lane, reduced by one branch-free pass per
+//    lane over reset masks and a DPP segmented scan across the lanes.
+// Segments cut by a share boundary leave one partial per share in scratch; a
+// second kernel combines them in share order.  Every summation order is a
+// fixed function of the offsets, so results repeat bit for bit on any
+// device; no atomic operation touches global memory (the 1-D kernel's reset
+// masks are built with a bit-OR in LDS, whose result does not depend on
+// arrival order).
 //
-// Memory: rows are read through buffer descriptors that cover exactly the
-// valid part of a chunk (reads past it return 0, so no clamping), and the
-// next chunk streams into registers while the current one is processed.
+// Memory: rows are read through buffer descriptors whose range ends with the
+// valid rows (reads past it return 0, so no clamping), with the non-temporal
+// hint, and the next rows stream into registers while the current ones are
+// processed.
 //
 // Accumulators: float sums in float64 (rounded to float32 once; the 1-D
 // kernel adds runs of <= 32 elements and a 64-way tree of them in float32
@@ -37,10 +46,8 @@
 // key << 32 | row code) whose integer max/min picks the extremum and, on
 // equal keys, the lowest row (the packed value/row word of the graph-reduce
 // README's "Method").
-#include <map>
 #include <mutex>
 #include <type_traits>
-#include <utility>
 
 #include "internal.hpp"
 #include "keys.hpp"

@@ -153,9 +153,10 @@ __device__ __forceinline__ uint32_t sbit(uint32_t m, int t) {
     return r;
 }
 
-// Bitwise OR into a word of this wave's LDS (ds_or_b32).  The only atomic
-// operation in the library: it sets flag bits, so the result does not depend
-// on the order in which lanes arrive.
+// Bitwise OR into a word of this wave's LDS (ds_or_b32).  It only sets flag
+// bits, so the result does not depend on the order in which lanes arrive.
+// (The segmented reduction, RLE and scan kernels use no other atomic; the
+// scatter kernels and the search's validation word use global atomics.)
 __device__ __forceinline__ void lds_or(uint32_t *p, uint32_t v) {
     __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
 }

@@ -302,3 +302,17 @@ def test_values_end_with_their_buffer(kind, feat):
             gu.assert_parity(vals, off, op, out.cpu().numpy().reshape(s, -1),
                              arg.cpu().numpy().reshape(s, -1) if arg is not None else None,
                              what=f"end-of-buffer F={feat} shares={shares}")
+
+
+@pytest.mark.parametrize("dtype,op,feat", [(2, 0, 1), (2, 1, 1), (0, 0, 1), (1, 2, 1), (2, 0, 32), (2, 2, 32),
+                                           (2, 3, 32), (2, 0, 64), (2, 2, 64), (2, 0, 8), (0, 1, 3), (2, 2, 100),
+                                           (2, 2, 260)])
+def test_default_shares_fit_one_round(dtype, op, feat):
+    """The share count is a constant of each kernel (the same on every
+    device); on MI355X it must not exceed the waves that fit at once, so a
+    call runs as one round of waves."""
+    import segmented_reduction_amd as sr
+    lib = sr.library()
+    shares = lib.segred_get_shares(dtype, op, feat)
+    resident = lib.segred_resident_waves(dtype, op, feat)
+    assert 0 < shares <= resident, (shares, resident)
