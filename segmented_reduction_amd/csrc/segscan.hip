@@ -13,7 +13,8 @@
 // Rows outside [offsets[0], offsets[S]) are not written.
 //
 // Work partition: the merge-path shares of the segmented reduction (rows +
-// segment ends, one share per resident wave; partition.hpp), with each share
+// segment ends, a constant number of shares: one per wave of a whole
+// MI355X; partition.hpp), with each share
 // boundary moved onto a nearby segment boundary when one lies within a
 // quarter share, so only segments longer than that are cut.  Two launches:
 //   seg_scan_tails  per share, the partial of the segment the share leaves
@@ -33,8 +34,6 @@
 // monotone order key.  Every order is a fixed function of the offsets and
 // the share count, so results repeat bit for bit; no atomic operations.
 #include <algorithm>
-#include <map>
-#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -421,31 +420,20 @@ static std::pair<const void *, const void *> scan_kernels(int64_t feat) {
     }
 }
 
-// One share per wave of the main kernel that fits on the device at once.
-static int64_t scan_shares(const void *kernel) {
-    static std::mutex mu;
-    static std::map<std::pair<int, const void *>, int64_t> cache;
+// Shares per call: one per wave of the main kernel on a whole MI355X (256
+// CUs x 4 SIMDs x the 8 waves per SIMD both kernels are built for), a
+// constant, so the fixed-order float sums do not depend on the device (a
+// smaller device runs the same shares in more rounds).
+constexpr int64_t kScanShares = 256 * 4 * 8;
+static int64_t scan_shares() {
     const int64_t o = shares_override();
-    if (o > 0) return (o + 3) / 4 * 4;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 8192;
-    std::lock_guard<std::mutex> lk(mu);
-    auto it = cache.find({dev, kernel});
-    if (it != cache.end()) return it->second;
-    int cus = 0, blocks = 0;
-    int64_t w = 8192;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, 256, 0) == hipSuccess && cus > 0 && blocks > 0)
-        w = (int64_t)cus * blocks * 4;
-    (void)hipGetLastError();
-    cache[{dev, kernel}] = w;
-    return w;
+    return o > 0 ? (o + 3) / 4 * 4 : kScanShares;
 }
 
 template <int DT, int OP, bool EXCL>
 static int scan_run(ScanArgs k, hipStream_t st) {
     const auto kern = scan_kernels<DT, OP, EXCL>(k.F);
-    const int64_t nw = scan_shares(kern.second);
+    const int64_t nw = scan_shares();
     k.NW = nw;
     k.chunks = (k.F + 63) / 64;
     const size_t rec_bytes = (size_t)nw * kRec * sizeof(int64_t);
