@@ -20,14 +20,18 @@ namespace segred {
 // next share), so shares still split the merged sequence at valid points.  The four waves
 // of a workgroup own four consecutive shares, so their five boundary
 // diagonals lie close together and the workgroup searches for them jointly:
-//   round A: 1024 evenly spaced offsets (the same for every workgroup, so
+//   round A: 256 evenly spaced offsets (the same for every workgroup, so
 //            they stay cached), which also give o0 and the item count T;
 //   round B: 64 evenly spaced offsets over the range round A leaves for the
 //            workgroup's first and last diagonal;
-//   round C: each wave narrows its own two diagonals with 256-way rounds over
-//            consecutive offsets (one round unless the workgroup's range is
-//            wider than 16K ends).
-// The workgroup-specific loads touch about 64 + 8 * 3 cache lines of the
+//   round C: each wave narrows its own two diagonals with 256-way rounds
+//            (one round unless the workgroup's range is wider than 16K
+//            ends); the last round probes consecutive offsets, which also
+//            gives the key just past each diagonal's end, key(i(d) + 1).
+// Round A is one cache line per probe and every workgroup asks for all of
+// them at once: on MI355X 1,024 such probes took 3.4-6 us (the L2s' request
+// rate, ~131K requests per XCD), 256 take about a quarter of that.  The
+// workgroup-specific loads touch about 64 + 2 * 2 cache lines of the
 // offsets, most of which its waves read again for their segment ends.
 // Every probe is clamped into the array and loaded unconditionally (a load
 // under a branch would be waited for inside the branch).  The key of the
@@ -82,7 +86,7 @@ __device__ __forceinline__ Bracket bracket(const int64_t *s, int64_t lo, int64_t
     return b;
 }
 
-constexpr int kProbesA = 1024, kProbesB = 64;
+constexpr int kProbesA = 256, kProbesB = 64;
 
 //
 // `wave` is the share index (4 * share block + wave in the workgroup); every
@@ -104,7 +108,7 @@ __device__ __forceinline__ Share find_share(const int64_t *off, int64_t S, int64
     const int wid = tid >> 6;
     const int64_t blk = wave >> 2;  // the workgroup's four shares are 4 * blk .. 4 * blk + 3
 
-    // Round A (4 probes per thread).
+    // Round A (one probe per thread).
     const int64_t stepA = (S + kProbesA - 2) / (kProbesA - 1);
 #pragma unroll
     for (int u = 0; u < kProbesA / 256; ++u) {
@@ -136,20 +140,31 @@ __device__ __forceinline__ Share find_share(const int64_t *off, int64_t S, int64
     Bracket b1 = bracket<kProbesB, CW>(s_probe, L, stepB, H, o0, d1, lane);
     __syncthreads();  // the probe array is free from here on
 
-    // Round C: 256-way rounds on both diagonals of this wave.
-    int64_t lo0 = b0.lo, hi0 = b0.hi, k0lo = b0.klo;
-    int64_t lo1 = b1.lo, hi1 = b1.hi, k1lo = b1.klo;
-    while (lo0 < hi0 || lo1 < hi1) {
-        const int64_t st0 = (hi0 - lo0 + 255) >> 8, st1 = (hi1 - lo1 + 255) >> 8;
+    // Round C: 256-way rounds on both diagonals of this wave, probes j =
+    // 1..256 at lo + j * st with st = ceil((hi - lo) / 255), so the probes
+    // reach past hi and a step-1 round leaves probe n + 1 (n: the probes at
+    // or below the diagonal) at the new lo + 1.  Kernels that need key(lo +
+    // 1) -- the end of the block the diagonal falls in -- make one step-1
+    // round even when round B has already fixed lo (NEXT).
+    constexpr bool NEXT = SNAP || CW != 1;
+    int64_t lo0 = b0.lo, hi0 = b0.hi, k0lo = b0.klo, k0nx = 0;
+    int64_t lo1 = b1.lo, hi1 = b1.hi, k1lo = b1.klo, k1nx = 0;
+    bool nx0 = !NEXT, nx1 = !NEXT;  // key(lo + 1) known, or not needed
+    while (lo0 < hi0 || lo1 < hi1 || !nx0 || !nx1) {
+        const bool go0 = lo0 < hi0 || !nx0, go1 = lo1 < hi1 || !nx1;
+        const int64_t st0 = max((hi0 - lo0 + 254) / 255, (int64_t)1);
+        const int64_t st1 = max((hi1 - lo1 + 254) / 255, (int64_t)1);
         int64_t k0[4], k1[4];
         bool ok0[4], ok1[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int64_t j = (int64_t)(u * 64 + lane + 1);
             const int64_t p0 = lo0 + j * st0, p1 = lo1 + j * st1;
-            ok0[u] = lo0 < hi0 && p0 <= hi0;
-            ok1[u] = lo1 < hi1 && p1 <= hi1;
-            const int64_t q0 = min(p0, S), q1 = min(p1, S);
+            // probes past the bracket only matter as the next key (probe
+            // hi + 1); the rest load hi + 1 again (same cache line)
+            ok0[u] = go0 && p0 <= hi0;
+            ok1[u] = go1 && p1 <= hi1;
+            const int64_t q0 = min(min(p0, hi0 + 1), S), q1 = min(min(p1, hi1 + 1), S);
             k0[u] = off[q0] - o0 + CW * q0;
             k1[u] = off[q1] - o0 + CW * q1;
         }
@@ -159,7 +174,8 @@ __device__ __forceinline__ Share find_share(const int64_t *off, int64_t S, int64
             n0 += popc64(ballot(ok0[u] && k0[u] <= d0));
             n1 += popc64(ballot(ok1[u] && k1[u] <= d1));
         }
-        // key of probe n (1-based), held by lane (n - 1) % 64 in slot (n - 1) / 64
+        // key of probe n (1-based, n <= 256), held by lane (n - 1) % 64 in
+        // slot (n - 1) / 64
         auto key_of = [&](int64_t v0, int64_t v1, int64_t v2, int64_t v3, int n)
             __attribute__((always_inline)) -> int64_t {
             const int m = n - 1, u = m >> 6;
@@ -167,23 +183,31 @@ __device__ __forceinline__ Share find_share(const int64_t *off, int64_t S, int64
             return (int64_t)__builtin_amdgcn_readlane((uint32_t)v, m & 63) |
                    ((int64_t)__builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), m & 63) << 32);
         };
-        if (lo0 < hi0) {
+        if (go0) {
             if (n0 > 0) k0lo = key_of(k0[0], k0[1], k0[2], k0[3], n0);
             hi0 = min(hi0, lo0 + (int64_t)(n0 + 1) * st0 - 1);
             lo0 += (int64_t)n0 * st0;
+            if (st0 == 1) {  // n0 <= 255: probe n0 + 1 is at lo0 + 1 (or clamped to S)
+                k0nx = key_of(k0[0], k0[1], k0[2], k0[3], n0 + 1);
+                nx0 = true;
+            }
         }
-        if (lo1 < hi1) {
+        if (go1) {
             if (n1 > 0) k1lo = key_of(k1[0], k1[1], k1[2], k1[3], n1);
             hi1 = min(hi1, lo1 + (int64_t)(n1 + 1) * st1 - 1);
             lo1 += (int64_t)n1 * st1;
+            if (st1 == 1) {
+                k1nx = key_of(k1[0], k1[1], k1[2], k1[3], n1 + 1);
+                nx1 = true;
+            }
         }
     }
     int64_t e0 = d0, e1 = d1;
     if constexpr (SNAP) {
         // key(i + 1) of each boundary's block (block S, the end of the
         // sequence, is never moved)
-        const int64_t n0 = off[min(lo0 + 1, S)] - o0 + lo0 + 1;
-        const int64_t n1 = off[min(lo1 + 1, S)] - o0 + lo1 + 1;
+        const int64_t n0 = k0nx;
+        const int64_t n1 = k1nx;
         const int64_t slack = D >> 2;
         auto snap = [&](int64_t d, int64_t i, int64_t klo, int64_t knext, int64_t &e, int64_t &ii, int64_t &kk)
             __attribute__((always_inline)) {
@@ -211,7 +235,8 @@ __device__ __forceinline__ Share find_share(const int64_t *off, int64_t S, int64
     // stops at the last row of that end's segment
     int64_t r0 = e0 - CW * lo0, r1 = e1 - CW * lo1;
     if constexpr (CW != 1) {
-        const int64_t n0 = off[min(lo0 + 1, S)] - o0, n1 = off[min(lo1 + 1, S)] - o0;
+        // rows before end lo + 1 (read only when lo < S)
+        const int64_t n0 = k0nx - CW * (lo0 + 1), n1 = k1nx - CW * (lo1 + 1);
         if (lo0 < S) r0 = min(r0, n0);
         if (lo1 < S) r1 = min(r1, n1);
     }
