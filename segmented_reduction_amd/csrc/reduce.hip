@@ -117,6 +117,24 @@ struct Red {
     __device__ static __forceinline__ uint32_t rel_of(uint64_t p) {
         return OP == OP_MAX ? ~(uint32_t)p : (uint32_t)p;
     }
+    // Min/max walked in row order: the word a piece (a run of consecutive
+    // rows of one segment) starts from, the identity key with the piece's
+    // first row.  An element then replaces the word only when its key is
+    // strictly better (a 32-bit compare), so equal keys keep the earliest
+    // row, and a piece whose keys all equal the identity key ends on its
+    // first row -- the same word as folding lift() over the piece with
+    // comb().  A piece without rows must be turned back into id().
+    __device__ static __forceinline__ uint64_t piece_start(uint32_t rel) {
+        return OP == OP_MAX ? (uint64_t)(uint32_t)~rel : (0xFFFFFFFFull << 32) | rel;
+    }
+    __device__ static __forceinline__ uint32_t code_of(uint32_t rel) { return OP == OP_MAX ? ~rel : rel; }
+    __device__ static __forceinline__ void step(uint64_t &w, uint32_t bits, uint32_t code) {
+        const uint32_t k = okey<DT>(bits), wk = (uint32_t)(w >> 32);
+        const bool better = OP == OP_MAX ? k > wk : k < wk;
+        // the new key by max/min, which does not wait for the compare
+        const uint32_t nk = OP == OP_MAX ? max(k, wk) : min(k, wk);
+        w = ((uint64_t)nk << 32) | (better ? code : (uint32_t)w);
+    }
 };
 
 // The same partial with its row code counted from `delta` rows earlier.
@@ -673,14 +691,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kTeamWpe)))
         auto row_at = [&](uint32_t r) __attribute__((always_inline)) -> uint32_t {
             return r < nrows ? toff + r * row_bytes : kNoRow;
         };
+        // Min/max: each piece starts from R::piece_start (see there); the
+        // piece of segment `seg` in this part begins at row pstart.
         acc_t acc[VEC], hacc[VEC];
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[v] = hacc[v] = R::id();
+        for (int v = 0; v < VEC; ++v) {
+            hacc[v] = R::id();
+            if constexpr (R::kMinMax) acc[v] = R::piece_start(0u);
+            else acc[v] = R::id();
+        }
         int64_t seg = ti0;
         uint32_t e1 = end_rel(seg), e2 = end_rel(seg + 1);  // the next two ends
         uint32_t seg_start = (uint32_t)(tfirst - tj0);      // MEAN: start of segment `seg` (wraps if earlier)
+        uint32_t pstart = 0;
 
         auto finish = [&]() __attribute__((always_inline)) {
+            if constexpr (R::kMinMax) {
+                if (e1 == pstart) {
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) acc[v] = R::id();
+                }
+            }
             if (seg == ti0 && split_head) {
 #pragma unroll
                 for (int v = 0; v < VEC; ++v) hacc[v] = acc[v];
@@ -688,7 +719,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kTeamWpe)))
                 store_final<DT, OP, VEC, true>(a, seg, f0, acc, base, (int64_t)(e1 - seg_start));
             }
 #pragma unroll
-            for (int v = 0; v < VEC; ++v) acc[v] = R::id();
+            for (int v = 0; v < VEC; ++v) {
+                if constexpr (R::kMinMax) acc[v] = R::piece_start(e1);
+                else acc[v] = R::id();
+            }
+            pstart = e1;
             seg_start = e1;
             ++seg;
             e1 = e2;
@@ -704,13 +739,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kTeamWpe)))
                 const uint32_t r = rb + t;
                 while (e1 <= r) finish();
                 if (r < nrows) {
+                    if constexpr (R::kMinMax) {
+                        const uint32_t code = R::code_of(r);
 #pragma unroll
-                    for (int v = 0; v < VEC; ++v) acc[v] = R::comb(acc[v], R::lift(LN::at(x[t], v), r));
+                        for (int v = 0; v < VEC; ++v) R::step(acc[v], LN::at(x[t], v), code);
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < VEC; ++v) acc[v] = R::comb(acc[v], R::lift(LN::at(x[t], v), r));
+                    }
                 }
                 x[t] = LN::load(rs, row_at(r + V));
             }
         }
         while (e1 != kNoEnd) finish();
+        if constexpr (R::kMinMax) {
+            if (pstart >= nrows) {  // the open piece has no rows
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) acc[v] = R::id();
+            }
+        }
 
         // Fold the parts' partials in team order (row codes rebased to the
         // share's first row).
