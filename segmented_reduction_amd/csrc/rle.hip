@@ -45,41 +45,49 @@ struct TileKeys {
     bool head[kRleKeysPerThread];
 };
 
-// All loads are unconditional buffer loads, issued together: the tile's keys
-// through a descriptor limited to the keys that exist (reads past n return
-// 0), and for each wave's first position the key before it (one address for
-// the whole wave; for position 0 of the input the offset wraps out of range
-// and the value is not used).
+// The tile's keys arrive as 16-byte buffer loads (four per thread, all
+// issued together, through a descriptor limited to the keys that exist:
+// reads past n return 0) and go through LDS into the per-step layout above.
+// A position's left neighbour is the key of the lane before (a DPP wave
+// shift); lane 0 takes the previous wave's last key of the same step from
+// LDS, and the tile's first position the key before the tile, the one
+// global load besides the tile's own (its descriptor is empty for the first
+// tile, whose position 0 starts a run anyway).  Sixteen 4-byte loads per
+// thread and a load of the neighbour key per step took 16-17.5 us for 16M
+// keys; the loads were the issue bottleneck.
 template <int MODE>
-__device__ __forceinline__ void load_tile(const uint32_t *keys, int64_t n, int64_t start, int tid, TileKeys &t) {
+__device__ __forceinline__ void load_tile(const uint32_t *keys, int64_t n, int64_t start, int tid, TileKeys &t,
+                                          uint32_t *s_keys /* LDS [kRleTile] */) {
     const int lane = tid & 63, wid = tid >> 6;
     const int64_t avail = min((int64_t)kRleTile, n - start);
+    const auto rs = make_rsrc(keys + start, (uint32_t)(avail * 4));
+    constexpr int Q = kRleTile / (kRleThreads * 4);
+    uint4 q[Q];
+#pragma unroll
+    for (int i = 0; i < Q; ++i) q[i] = ld128(rs, (uint32_t)((i * kRleThreads * 4 + tid * 4) * 4));
+    uint32_t before = 0;
+    if constexpr (MODE != MODE_FLAGS) {
+        const auto rp = make_rsrc(keys + start - (start > 0 ? 1 : 0), start > 0 ? 4u : 0u);
+        before = ld32(rp, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < Q; ++i) *reinterpret_cast<uint4 *>(&s_keys[i * kRleThreads * 4 + tid * 4]) = q[i];
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kRleKeysPerThread; ++u) t.k[u] = s_keys[u * kRleThreads + tid];
     if constexpr (MODE == MODE_FLAGS) {
         // a start is a nonzero flag: no neighbour is needed
-        const auto rf = make_rsrc(keys + start, (uint32_t)(avail * 4));
-#pragma unroll
-        for (int u = 0; u < kRleKeysPerThread; ++u) t.k[u] = ld32(rf, (uint32_t)((u * kRleThreads + tid) * 4));
 #pragma unroll
         for (int u = 0; u < kRleKeysPerThread; ++u)
             t.head[u] = start + u * kRleThreads + tid < n && t.k[u] != 0u;
         return;
     }
-    const int64_t back = start > 0 ? 1 : 0;
-    const auto rs = make_rsrc(keys + start, (uint32_t)(avail * 4));
-    const auto rp = make_rsrc(keys + start - back, (uint32_t)((avail + back) * 4));
-    uint32_t p0[kRleKeysPerThread];
 #pragma unroll
     for (int u = 0; u < kRleKeysPerThread; ++u) {
-        t.k[u] = ld32(rs, (uint32_t)((u * kRleThreads + tid) * 4));
-        p0[u] = ld32(rp, (uint32_t)((u * kRleThreads + wid * 64 - 1 + (int)back) * 4));
-    }
-#pragma unroll
-    for (int u = 0; u < kRleKeysPerThread; ++u) {
-        const int64_t i = start + u * kRleThreads + tid;
-        // the cross-lane read runs in every lane (a disabled source lane
-        // would read as 0); lane 0 then takes the loaded key instead
-        uint32_t prev = lane_get(t.k[u], (lane - 1) & 63);
-        if (lane == 0) prev = p0[u];
+        const int p0 = u * kRleThreads + wid * 64;  // the wave's first position in the tile at this step
+        const uint32_t wave_prev = p0 > 0 ? s_keys[p0 > 0 ? p0 - 1 : 0] : before;
+        const uint32_t prev = dpp_move<kDppWaveShr1>(wave_prev, t.k[u]);  // lane 0 keeps wave_prev
+        const int64_t i = start + p0 + lane;
         t.head[u] = i < n && (i == 0 || t.k[u] != prev);
     }
 }
@@ -95,10 +103,11 @@ __global__ __launch_bounds__(kRleThreads) void rle_count(const uint32_t *keys, i
                                                          int64_t *tile_first, uint64_t *tile_mask) {
     __shared__ int64_t s_cnt[4];
     __shared__ int64_t s_first[4];
+    __shared__ __attribute__((aligned(16))) uint32_t s_keys[kRleTile];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int64_t start = (int64_t)blockIdx.x * kRleTile;
     TileKeys t;
-    load_tile<MODE>(keys, n, start, tid, t);
+    load_tile<MODE>(keys, n, start, tid, t, s_keys);
     int64_t cnt = 0, first = INT64_MAX;
     uint64_t mine = 0;  // lane u keeps step u's ballot
 #pragma unroll
