@@ -209,11 +209,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void s
     using acc_t = typename O::acc_t;
     constexpr int G = 64 / L;
     constexpr int SR = G * V;
-    constexpr int U = V == 1 ? 16 : 4;
+    // loads per batch: 16 for rows of 64 lanes; narrower rows keep 8, which
+    // fits their group scan in the 64 registers of 8 waves per SIMD
+    constexpr int U = V == 1 ? (L == 64 ? 16 : 8) : 4;
     static_assert(V == 1 || L == 1, "several rows per lane only for 1-D values");
     static_assert(SR <= 256, "step masks hold 256 rows");
 
     const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    __shared__ uint32_t s_sm[4][8];  // per wave: start flags of a 1-D step (256 rows)
+    uint32_t *sm = s_sm[wid];
     const int64_t sblocks = a.NW / 4;
     const int64_t chunk = blockIdx.x / sblocks;
     const int64_t share = readfirst((int64_t)(blockIdx.x % sblocks) * 4 + wid);
@@ -296,33 +300,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void s
         for (int u = 0; u < U; ++u) {
             const int64_t rb = rb0 + (int64_t)u * SR;
             if (rb >= j1) break;
-            // start mask of rows [rb, min(rb + SR, j1))
+            // start flags of rows [rb, min(rb + SR, j1)), one bit per element
             const int64_t lim = min(rb + SR, j1);
-            uint64_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
-            for (;;) {
-                if (kp > S) break;
-                if (kp - kb >= 64) {
+            uint32_t fl;
+            if constexpr (V == 4) {
+                // Each lane of the batch whose start lies in the step sets
+                // its row's bit in the wave's 256-bit mask in LDS (bit-OR:
+                // starts of empty segments share a row); a ballot counts
+                // them.  The batch moves on once all 64 are used.  (A scalar
+                // walk over the starts, two readlanes and a 64-bit OR per
+                // start, cost about 150 scalar instructions per step.)
+                if (lane < SR / 32) sm[lane] = 0u;
+                wave_lds_sync();
+                for (;;) {
+                    const int used = (int)(kp - kb);  // starts of the batch already placed (0..64)
+                    const bool in = lane >= used && bst0 < lim;
+                    if (in) {
+                        const uint32_t p = (uint32_t)(bst0 - rb);
+                        lds_or(&sm[p >> 5], 1u << (p & 31));
+                    }
+                    kp += popc64(ballot(in));
+                    if (kp - kb < 64) break;
                     kb += 64;
                     bst0 = bst1;
                     bst1 = a.offsets[min(kb + 64 + lane, S)] - o0;
-                    continue;
                 }
-                const int64_t e = readlane64(bst0, (int)(kp - kb));
-                if (e >= lim) break;
-                const int p = (int)(e - rb);
-                if (p < 64) m0 |= 1ull << p;
-                else if (p < 128) m1 |= 1ull << (p - 64);
-                else if (p < 192) m2 |= 1ull << (p - 128);
-                else m3 |= 1ull << (p - 192);
-                ++kp;
-            }
-            // this lane's start flags, one bit per element
-            uint32_t fl;
-            if constexpr (V == 4) {
-                const int q = lane >> 4;
-                const uint64_t mw = q == 0 ? m0 : q == 1 ? m1 : q == 2 ? m2 : m3;
-                fl = (uint32_t)(mw >> ((lane & 15) * 4)) & 0xFu;
+                wave_lds_sync();
+                fl = (sm[lane >> 3] >> ((lane & 7) * 4)) & 0xFu;
             } else {
+                uint64_t m0 = 0;
+                for (;;) {
+                    if (kp > S) break;
+                    if (kp - kb >= 64) {
+                        kb += 64;
+                        bst0 = bst1;
+                        bst1 = a.offsets[min(kb + 64 + lane, S)] - o0;
+                        continue;
+                    }
+                    const int64_t e = readlane64(bst0, (int)(kp - kb));
+                    if (e >= lim) break;
+                    m0 |= 1ull << (int)(e - rb);
+                    ++kp;
+                }
                 fl = (uint32_t)(m0 >> g) & 1u;
             }
             // per-lane scan with resets at starts
