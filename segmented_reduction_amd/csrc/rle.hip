@@ -236,6 +236,9 @@ __global__ __launch_bounds__(kRleThreads) void rle_materialize(const uint32_t *k
     __shared__ int s_wc[kRleKeysPerThread][4];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int64_t start = (int64_t)blockIdx.x * kRleTile;
+    // the tile's run index and following start, loaded with its start bits
+    const int64_t rb = tile_base[blockIdx.x];
+    const int64_t next = MODE == MODE_RLE ? tile_next[blockIdx.x] : 0;
     uint64_t m[kRleKeysPerThread];
     bool head[kRleKeysPerThread];
 #pragma unroll
@@ -264,15 +267,35 @@ __global__ __launch_bounds__(kRleThreads) void rle_materialize(const uint32_t *k
     }
     __syncthreads();
     const int cnt = base;
-    const int64_t rb = tile_base[blockIdx.x];
-    const int64_t next = MODE == MODE_RLE ? tile_next[blockIdx.x] : 0;
-    for (int q = tid; q < cnt; q += kRleThreads) {
-        const int64_t pos = start + s_pos[q];
-        if (MODE != MODE_FLAGS) values[rb + q] = keys[pos];
-        if (MODE != MODE_UNIQUE) offsets[rb + q] = pos;
-        if (MODE == MODE_RLE) {
-            const int64_t npos = q + 1 < cnt ? start + s_pos[q + 1] : next;
-            lengths[rb + q] = (uint32_t)(npos - pos);
+    // Runs in batches of B per thread: every key load of a batch is issued
+    // before its stores (through a descriptor over the tile's keys; runs past
+    // cnt load the tile's first key and store nothing), so a tile of up to
+    // 4,096 runs costs two round trips instead of one per 256 runs.
+    constexpr int B = 8;
+    const auto rk = make_rsrc(keys + start, (uint32_t)(min((int64_t)kRleTile, n - start) * 4));
+    for (int q0 = 0; q0 < cnt; q0 += B * kRleThreads) {
+        uint32_t p[B], v[B];
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+            const int q = q0 + i * kRleThreads + tid;
+            p[i] = q < cnt ? s_pos[q] : 0u;
+        }
+        if constexpr (MODE != MODE_FLAGS) {
+#pragma unroll
+            for (int i = 0; i < B; ++i) v[i] = ld32(rk, p[i] * 4u);
+        }
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+            const int q = q0 + i * kRleThreads + tid;
+            if (q < cnt) {
+                const int64_t pos = start + p[i];
+                if (MODE != MODE_FLAGS) values[rb + q] = v[i];
+                if (MODE != MODE_UNIQUE) offsets[rb + q] = pos;
+                if (MODE == MODE_RLE) {
+                    const int64_t npos = q + 1 < cnt ? start + s_pos[q + 1] : next;
+                    lengths[rb + q] = (uint32_t)(npos - pos);
+                }
+            }
         }
     }
 }
