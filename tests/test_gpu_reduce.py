@@ -316,3 +316,36 @@ def test_default_shares_fit_one_round(dtype, op, feat):
     shares = lib.segred_get_shares(dtype, op, feat)
     resident = lib.segred_resident_waves(dtype, op, feat)
     assert 0 < shares <= resident, (shares, resident)
+
+
+# Bit patterns at the ends of each type's order (graph-reduce README,
+# "Method": the order key; luma.gl GPUSegmentedReduction, "Contract": an
+# empty segment gives the identity and -1).  Max over the lowest key and min
+# over the highest are the cases where every element equals the identity's
+# key: the result must still be the segment's first row, and an empty
+# segment must still give -1.
+_LOWEST = {"u32": 0x00000000, "i32": 0x80000000, "f32": 0xFFFFFFFF}   # order key 0
+_HIGHEST = {"u32": 0xFFFFFFFF, "i32": 0x7FFFFFFF, "f32": 0x7FFFFFFF}  # order key 0xFFFFFFFF
+
+
+@pytest.mark.parametrize("feat", [1, 3, 4, 8, 32, 64, 100])
+@pytest.mark.parametrize("kind", ["u32", "i32", "f32"])
+def test_extreme_keys_keep_the_first_row(kind, feat):
+    rng = np.random.default_rng(7000 + feat)
+    off, _ = W.ragged(seed=7100 + feat, segments=1500, mean_len=12, feat=feat, dtype=kind, long_segment=3000)
+    rows = int(off[-1])
+    shape = (rows,) if feat == 1 else (rows, feat)
+    for op, pat in (("max", _LOWEST[kind]), ("min", _HIGHEST[kind])):
+        bits = np.full(shape, pat, dtype=np.uint32)
+        for mixed in (False, True):
+            b = bits.copy()
+            if mixed:
+                # a few ordinary values, so positions other than the first win
+                # in some segments and rows of equal extreme keys in others
+                pick = rng.random(shape) < 0.05
+                b[pick] = rng.integers(1, 1 << 30, int(pick.sum()), dtype=np.uint32) | (1 << 30)
+            vals = b.view(NP_T[kind])
+            for shares in (None, 5, 411):
+                gu.say(f"extreme keys kind={kind} F={feat} op={op} mixed={mixed} shares={shares}")
+                out, arg = gu.run_gpu(vals, off, op, shares=shares)
+                gu.assert_parity(vals, off, op, out, arg, what=f"extreme {kind} F={feat} {op} mixed={mixed}")
