@@ -45,7 +45,9 @@
 // first), integer sums in wrapping uint32, min/max as a 64-bit word (order
 // key << 32 | row code) whose integer max/min picks the extremum and, on
 // equal keys, the lowest row (the packed value/row word of the graph-reduce
-// README's "Method").
+// README's "Method"); the team walk, which meets a piece's rows in order,
+// steps on the 32-bit key alone with the row kept beside it and packs the
+// same word for its partials and results.
 #include <mutex>
 #include <type_traits>
 
@@ -160,9 +162,15 @@ __device__ __forceinline__ acc_t rebase_word(acc_t p, uint32_t delta, bool is_ma
 constexpr int64_t kShareSimds = 256 * 4;
 constexpr int kTeamWpe = 4;  // row walk by teams
 constexpr int kRowsWpe = 3;  // row walk by chunks
+// 1-D: 2 for every operation.  Min/max need the registers.  Sums ran faster
+// at 2 than at 4 (at 4 the waves keep twice the bytes in flight that the
+// memory needs, and the latency-bound steps -- the partition search, the
+// first fetch -- wait behind them): the 50M-element heavy-skew sum 41.8-42.3
+// us against 42.6-42.9 us, the 16M-key RLE sum 22.7-24.4 us against
+// 23.3-25.8 us; at 1 wave per SIMD they took 48.2 and 28.1 us.
 template <int DT, int OP>
 constexpr int flat_wpe() {
-    return Red<DT, OP>::kMinMax ? 2 : 4;  // 1-D
+    return 2;
 }
 
 // Final value of one (segment, feature); `base` turns a share-relative row
