@@ -72,7 +72,7 @@ def test_noalloc_scratch_limit():
     """A row width whose partials exceed the fixed scratch is refused."""
     import segmented_reduction_amd as sr
     lib = sr.library()
-    feat = 400  # 32 * 3072 + 16 * 3072 * 400 bytes > 16 MiB
+    feat = 600  # 32 * 2048 + 16 * 2048 * 600 bytes > 16 MiB
     off = torch.tensor([0, 2, 3], dtype=torch.int64, device="cuda")
     vals = torch.zeros((3, feat), dtype=torch.float32, device="cuda")
     out = torch.empty((2, feat), dtype=torch.float32, device="cuda")
