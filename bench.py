@@ -20,7 +20,10 @@ of the K timed steps), Gelem/s, the roofline of the dominant kernel (its
 algorithmic bytes per launch / its average duration, from start and stop
 events the runtime stamps on the kernel itself over a second pass of the
 same K steps) and the CPU oracle timed on the host's cores (T threads over
-contiguous row-balanced segment ranges, and one thread on a sample).
+contiguous row-balanced segment ranges, and one thread on a sample).  As
+context it also measures the streaming ceiling of the device: a plain
+wave-per-share read of 2 GiB, alone and with 1/16 writes
+(segred_probe_stream).
 """
 from __future__ import annotations
 
@@ -30,6 +33,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -655,6 +660,49 @@ def load_traffic(name, dominant_label, src_hash):
     return entry.get("bytes_per_launch")
 
 
+# ---------------------------------------------------------------- ceiling
+
+CEILING_BYTES = 2 << 30  # 2 GiB: far past the 256 MB last-level cache
+
+
+def stream_ceiling(sr, torch, reps=20):
+    """What a plain streaming kernel reaches on this device, as context for
+    the roofline fractions: segred_probe_stream reads 2 GiB of float32 once
+    (one wave per contiguous share, non-temporal 16-byte loads), alone and
+    with one 1 KB block written per 16 read (the output share of the
+    power-law sum).  Per-launch durations come from the kernel's own start
+    and stop events, like the reduction kernels'; the figure is the median
+    of `reps` launches at each wave count, and the best wave count is kept."""
+    n = CEILING_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty(n // 16, dtype=torch.float32, device="cuda")
+    rows = {}
+    for wevery, label in ((0, "read"), (16, "read_plus_1_16_write")):
+        moved = CEILING_BYTES + (CEILING_BYTES // 16 if wevery else 0)
+        best = None
+        for waves in (2048, 4096):
+            for _ in range(3):
+                sr.probe_stream(src, wevery, waves, dst)
+            torch.cuda.synchronize()
+            sr.timing_enable(True)
+            sr.timing_read()
+            for _ in range(reps):
+                sr.probe_stream(src, wevery, waves, dst)
+            torch.cuda.synchronize()
+            _, _, each = sr.timing_read()
+            sr.timing_enable(False)
+            med = float(np.median(each))
+            gbs = moved / (med * 1e-3) / 1e9
+            if best is None or gbs > best["GBps"]:
+                best = {"GBps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4), "waves": waves,
+                        "median_us": round(med * 1e3, 2), "bytes": moved}
+        rows[label] = best
+    del src, dst
+    torch.cuda.empty_cache()
+    rows["kernel"] = "segred_probe_stream over 2 GiB (median of %d launches per wave count)" % reps
+    return rows
+
+
 # ---------------------------------------------------------------- main
 
 GATED = ["message", "rle", "skew"]  # reported beside the headline (largest) configuration
@@ -712,6 +760,8 @@ def measure(name, steps, warmup, cpu_seconds, threads, sr, torch, with_cpu=True)
         avg_ms = sum(times) / len(times)
         b = wl.call_bytes(label)
         kernels[label] = {"avg_us": round(avg_ms * 1e3, 2), "min_us": round(min(times) * 1e3, 2),
+                          "median_us": round(float(np.median(times)) * 1e3, 2),
+                          "p90_us": round(float(np.percentile(times, 90)) * 1e3, 2),
                           "launches": len(times), "bytes": b,
                           "GBps": round(b / (avg_ms * 1e-3) / 1e9, 1),
                           "frac": round(b / (avg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
@@ -805,6 +855,8 @@ def main():
     ap.add_argument("--also-steps", type=int, default=100, help="timed steps of each --also workload")
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="time budget of each CPU oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-ceiling probe (segred_probe_stream over 2 GiB)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain device copy of 256 MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -845,6 +897,8 @@ def main():
         others[x] = measure(x, args.also_steps, args.warmup, args.cpu_seconds, threads, sr, torch,
                             with_cpu=not args.no_cpu_baseline)
 
+    ceiling = None if args.no_ceiling else stream_ceiling(sr, torch)
+
     line = {
         "metric": METRIC,
         "value": head["value"],
@@ -869,6 +923,7 @@ def main():
         "parity": head["parity"],
         "bitwise_repeat": head["bitwise_repeat"],
         "kernel_source_hash": head["kernel_source_hash"],
+        "stream_ceiling": ceiling,
         "accumulate": ("f32 atomic adds in arrival order (not bitwise repeatable); max via packed 64-bit "
                        "atomic max" if args.config.startswith("scatter")
                        else "f64 for float sums, wrapping u32 for integer sums"),

@@ -2,13 +2,15 @@
  * segred_instrument.h -- testing and benchmarking hooks of the
  * segmented-reduction library.  They are not part of the method: the tests
  * use them to force segments across share boundaries and to check the share
- * count, the benchmark to time kernels.  All of them are host-side and
- * process-wide; none is thread-safe.
+ * count, the benchmark to time kernels and to measure the streaming rate the
+ * device reaches.  The share and timing hooks are host-side and
+ * process-wide; none of them is thread-safe.
  */
 #ifndef SEGRED_INSTRUMENT_H
 #define SEGRED_INSTRUMENT_H
 
 #include <stdint.h>
+#include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -41,24 +43,45 @@ int64_t segred_resident_waves(int32_t dtype, int32_t op, int64_t feat);
 
 /*
  * Kernel timing.  While enabled, every kernel the library launches carries
- * a HIP event that the runtime stamps when that kernel ends
- * (hipExtLaunchKernel).  segred_timing_read waits for the recorded events and
- * reports, for every streaming kernel (the first kernel of a segred_reduce
- * call, both kernels of segred_scan, the atomic or private-copy kernel of
- * segred_scatter_reduce, the search kernel of segred_galloping_search, the
- * histogram of segred_offsets_from_index, the counting and materialising
- * kernels of segred_offsets_from_rle / segred_unique /
- * segred_offsets_from_flags), the time from the end of the launch recorded
- * before it to its own end (-1 for the first launch of the record): when the
- * library's kernels run back to back on one stream (nothing else queued in
- * between), this is the streaming kernel's execution time.  It returns the
- * summed duration of the timed launches in milliseconds and the number of
- * streaming launches, writes the first `capacity` durations (ms, in launch
- * order) to the host array `each_ms` (may be NULL when capacity is 0), and
- * clears the record.  Up to 8192 launches are kept; later ones are not timed.
+ * a start and a stop HIP event that the runtime stamps when that kernel
+ * begins and ends (hipExtLaunchKernel), so a launch's duration is its own
+ * stop minus its own start and idle time between launches is not counted.
+ * segred_timing_read waits for the recorded events and reports the
+ * durations of the streaming kernels only (the first kernel of a
+ * segred_reduce call, both kernels of segred_scan, the atomic or
+ * private-copy kernel of segred_scatter_reduce, the search kernel of
+ * segred_galloping_search, the histogram of segred_offsets_from_index, the
+ * counting and materialising kernels of segred_offsets_from_rle /
+ * segred_unique / segred_offsets_from_flags, and segred_probe_stream).  It
+ * returns their summed duration in milliseconds and their number, writes the
+ * first `capacity` durations (ms, in launch order) to the host array
+ * `each_ms` (may be NULL when capacity is 0), and clears the record.  Up to
+ * 8192 launches (streaming or not) are kept; later ones are not timed.
  */
 int segred_timing_enable(int enable);
 int segred_timing_read(double *total_ms, int64_t *launches, float *each_ms, int64_t capacity);
+
+/*
+ * Streaming-rate probe, for measurement context only (it is not part of the
+ * method): the rate a plain read of device memory reaches, alone or with a
+ * fixed fraction of writes, i.e. the practical ceiling of a kernel that
+ * reads its input once and writes a fraction of it.  `src` (device, 16-byte
+ * aligned) holds `bytes` bytes of float32, a positive multiple of 1,024.  It
+ * is cut into `waves` contiguous shares of whole 1 KB blocks (1 <= waves <=
+ * 2^20, each share under 2 GiB), one wave per share, 4 waves per workgroup;
+ * each wave reads its share with non-temporal 16-byte loads and keeps a
+ * running float sum per lane.  With write_every = 0 nothing else is written;
+ * with 1 <= write_every <= 1024, after every input block b with
+ * (b + 1) % write_every == 0 the wave writes its 64 lanes' running sums (each
+ * as 4 equal floats, non-temporal) to the 1 KB block b / write_every of `dst`
+ * (device, 16-byte aligned, at least floor(bytes / 1024 / write_every) KiB),
+ * so the writes are 1/write_every of the reads.  `wave_sums` (device, `waves`
+ * floats) receives each wave's total.  Asynchronous on `stream`; timed like
+ * the streaming kernels above.  Returns SEGRED_ERR_INVALID_ARGUMENT for
+ * arguments outside these ranges, SEGRED_ERR_HIP if the launch fails.
+ */
+int segred_probe_stream(const void *src, int64_t bytes, void *dst, int32_t write_every, float *wave_sums,
+                        int32_t waves, hipStream_t stream);
 
 #ifdef __cplusplus
 }

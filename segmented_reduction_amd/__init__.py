@@ -90,6 +90,8 @@ def library(path: str | None = None):
             lib.segred_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64),
                                               ctypes.POINTER(ctypes.c_float), i64]
             lib.segred_timing_read.restype = ctypes.c_int
+            lib.segred_probe_stream.argtypes = [vp, i64, vp, i32, vp, i32, vp]
+            lib.segred_probe_stream.restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -401,3 +403,33 @@ def timing_read(capacity: int = 8192):
     each = (ctypes.c_float * max(capacity, 1))()
     _check(library().segred_timing_read(ctypes.byref(ms), ctypes.byref(n), each, capacity), "segred_timing_read")
     return ms.value, n.value, [each[i] for i in range(min(n.value, capacity))]
+
+
+def probe_stream(src: torch.Tensor, write_every: int = 0, waves: int = 4096,
+                 dst: torch.Tensor | None = None):
+    """Streaming-rate probe (measurement context, see segred_probe_stream).
+
+    src  contiguous float32 GPU tensor whose size in bytes is a multiple of
+         1,024, read once by `waves` waves over contiguous shares.
+    write_every  0 (read only) or 1..1024: one 1 KB block is written per
+         `write_every` blocks read, to `dst` (float32, at least
+         floor(blocks / write_every) * 256 elements; allocated when None).
+    Returns (wave_sums [waves] float32, dst or None).
+    """
+    if not src.is_cuda or src.dtype != torch.float32 or not src.is_contiguous():
+        raise ValueError("src must be a contiguous float32 GPU tensor")
+    nbytes = src.numel() * 4
+    if write_every > 0 and dst is None:
+        dst = torch.empty((nbytes // 1024 // write_every) * 256, dtype=torch.float32, device=src.device)
+    if dst is not None and (not dst.is_cuda or dst.dtype != torch.float32 or not dst.is_contiguous()
+                            or dst.device != src.device):
+        raise ValueError("dst must be a contiguous float32 tensor on the device of src")
+    if write_every > 0 and dst.numel() < (nbytes // 1024 // write_every) * 256:
+        raise ValueError("dst is smaller than one 1 KB block per write_every blocks of src")
+    sums = torch.empty(max(int(waves), 1), dtype=torch.float32, device=src.device)
+    _check(library().segred_probe_stream(
+        ctypes.c_void_p(src.data_ptr()), nbytes,
+        ctypes.c_void_p(dst.data_ptr() if dst is not None and write_every > 0 else 0),
+        int(write_every), ctypes.c_void_p(sums.data_ptr()), int(waves),
+        ctypes.c_void_p(_stream(src.device))), "segred_probe_stream")
+    return sums, (dst if write_every > 0 else None)

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(HERE, "_lib")
 OBJ_DIR = os.path.join(LIB_DIR, "obj")
 LIB = os.path.join(LIB_DIR, "libsegred.so")
-SOURCES = ["api.hip", "reduce.hip", "rle.hip", "scatter.hip", "segscan.hip", "galloping.hip"]
+SOURCES = ["api.hip", "reduce.hip", "rle.hip", "scatter.hip", "segscan.hip", "galloping.hip", "probe.hip"]
 ARCH = os.environ.get("SEGRED_OFFLOAD_ARCH", "gfx950")
 
 

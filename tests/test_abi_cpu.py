@@ -40,7 +40,7 @@ def test_public_header_holds_only_the_method():
     for hook in _declared(INSTRUMENT):
         assert hook not in names, hook
     assert set(_declared(INSTRUMENT)) == {"segred_set_shares", "segred_get_shares", "segred_resident_waves",
-                                          "segred_timing_enable", "segred_timing_read"}
+                                          "segred_timing_enable", "segred_timing_read", "segred_probe_stream"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -254,6 +254,27 @@ def test_timing_read_without_launches():
     assert n.value == 0 and ms.value == 0.0
     assert lib.segred_timing_read(None, None, None, 0) == 1
     assert lib.segred_timing_read(ctypes.byref(ms), ctypes.byref(n), None, 4) == 1
+
+
+@pytest.mark.parametrize("args,expect", [
+    # (src, bytes, dst, write_every, wave_sums, waves) -> status
+    ((FAKE, 1000, None, 0, FAKE, 4), 1),          # not whole 1 KB blocks
+    ((FAKE, 0, None, 0, FAKE, 4), 1),             # empty
+    ((FAKE, 1024, None, 0, FAKE, 0), 1),          # no wave
+    ((FAKE, 1024, None, 0, FAKE, 2 ** 20 + 1), 1),
+    ((FAKE, 1024, None, -1, FAKE, 4), 1),
+    ((FAKE, 1024, FAKE, 1025, FAKE, 4), 1),
+    ((FAKE, 1024, None, 2, FAKE, 4), 1),          # writes without dst
+    ((None, 1024, None, 0, FAKE, 4), 1),
+    ((FAKE, 1024, None, 0, None, 4), 1),
+    ((FAKE + 4, 1024, None, 0, FAKE, 4), 1),      # src not 16-byte aligned
+    ((FAKE, 1024, FAKE + 4, 1, FAKE, 4), 1),
+    ((FAKE, 1024, None, 0, FAKE + 2, 4), 1),
+    ((FAKE, 2 ** 31, None, 0, FAKE, 1), 1),       # a share of 2 GiB
+])
+def test_probe_argument_checks(args, expect):
+    lib = _lib()
+    assert lib.segred_probe_stream(*args, None) == expect
 
 
 def test_binding_refuses_cpu_tensors():
