@@ -857,6 +857,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-ceiling probe (segred_probe_stream over 2 GiB)")
+    ap.add_argument("--ceiling-only", action="store_true",
+                    help="run only the streaming-ceiling probe and print its figures")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain device copy of 256 MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -882,6 +884,10 @@ def main():
         return
 
     import segmented_reduction_amd as sr
+
+    if args.ceiling_only:
+        print(json.dumps({"stream_ceiling": stream_ceiling(sr, torch)}), flush=True)
+        return
 
     threads = host_threads()
     also = GATED if (args.also is None and args.config == "powerlaw") else \
