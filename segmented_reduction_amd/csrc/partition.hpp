@@ -78,8 +78,7 @@ __device__ __forceinline__ Bracket bracket(const int64_t *s, int64_t lo, int64_t
 #pragma unroll
     for (int u = 1; u < U; ++u) klast = ul == u ? kk[u] : klast;
     Bracket b;
-    b.klo = (int64_t)__builtin_amdgcn_readlane((uint32_t)klast, last & 63) |
-            ((int64_t)__builtin_amdgcn_readlane((uint32_t)((uint64_t)klast >> 32), last & 63) << 32);
+    b.klo = readlane64(klast, last & 63);
     b.lo = probe_pos<N>(last, lo, step, hi);
     b.hi = cnt >= N ? hi : probe_pos<N>(cnt, lo, step, hi) - 1;
     if (b.hi < b.lo) b.hi = b.lo;
@@ -180,8 +179,7 @@ __device__ __forceinline__ Share find_share(const int64_t *off, int64_t S, int64
             __attribute__((always_inline)) -> int64_t {
             const int m = n - 1, u = m >> 6;
             const int64_t v = u == 0 ? v0 : u == 1 ? v1 : u == 2 ? v2 : v3;
-            return (int64_t)__builtin_amdgcn_readlane((uint32_t)v, m & 63) |
-                   ((int64_t)__builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), m & 63) << 32);
+            return readlane64(v, m & 63);
         };
         if (go0) {
             if (n0 > 0) k0lo = key_of(k0[0], k0[1], k0[2], k0[3], n0);

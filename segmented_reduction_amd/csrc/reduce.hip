@@ -551,7 +551,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kRowsWpe)))
                 }
             }
             open_spread = false;
-            if constexpr (OP == OP_MEAN) open_start = jc + (int64_t)__builtin_amdgcn_readfirstlane(se[ne - 1]);
+            if constexpr (OP == OP_MEAN) open_start = jc + (int64_t)(uint32_t)__builtin_amdgcn_readfirstlane(se[ne - 1]);
 
             ic = icn;
             jc = jcn;

@@ -87,11 +87,6 @@ struct ScanOp {
     }
 };
 
-__device__ __forceinline__ int64_t readlane64(int64_t v, int idx) {
-    return (int64_t)__builtin_amdgcn_readlane((uint32_t)v, idx) |
-           ((int64_t)__builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), idx) << 32);
-}
-
 // Share record: [i0, j0, i1, j1, first_row, tail_row, o0, flags], rows
 // relative to offsets[0]; flags bit 0: the share's last segment continues
 // past it; bit 1: that segment starts inside the share.

@@ -108,6 +108,15 @@ __device__ __forceinline__ T uniform(T v) {
     return v;  // values that are wave-uniform by construction
 }
 
+// The 64-bit value of lane idx (idx wave-uniform).  readlane returns a
+// signed 32-bit int, so each half is taken as an unsigned word before it is
+// widened: a low half with bit 31 set must not fill the upper half with ones.
+__device__ __forceinline__ int64_t readlane64(int64_t v, int idx) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, idx);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), idx);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ int64_t readfirst(int64_t v) {
     uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
     uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
