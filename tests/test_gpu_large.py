@@ -165,3 +165,41 @@ def test_rows_past_4_gib(feat, m, rows):
     _run(vals, off, feat, m, ("sum", "max", "min"), f"rows F={feat} past 4 GiB")
     del vals
     torch.cuda.empty_cache()
+
+
+def test_runs_past_2_31_keys():
+    """2^31 + 4,097 keys r // 1000 (runs of 1,000 crossing row 2^31 and every
+    tile edge): RLE, unique and start flags against their closed forms."""
+    import segmented_reduction_amd as sr
+    n = 2 ** 31 + 4097
+    runs = (n + 999) // 1000
+    keys = torch.empty(n, dtype=torch.int32, device="cuda")
+    for c0 in range(0, n, 1 << 26):
+        c1 = min(n, c0 + (1 << 26))
+        keys[c0:c1] = (torch.arange(c0, c1, dtype=torch.int64, device="cuda") // 1000).to(torch.int32)
+    keys = keys.view(torch.uint32)
+    want_off = np.minimum(np.arange(runs + 1, dtype=np.int64) * 1000, n)
+    gu.say(f"rle n={n}")
+    v, ln, off, c = sr.rle(keys)
+    assert c == runs
+    assert np.array_equal(v.cpu().numpy().astype(np.int64), np.arange(runs))
+    assert np.array_equal(ln.cpu().numpy().astype(np.int64), np.diff(want_off))
+    assert np.array_equal(off.cpu().numpy(), want_off)
+    del v, ln, off
+    torch.cuda.empty_cache()
+    gu.say(f"unique n={n}")
+    uv, uc = sr.unique(keys)
+    uc = int(uc.item())
+    assert uc == runs and np.array_equal(uv[:uc].cpu().numpy().astype(np.int64), np.arange(runs))
+    del uv, keys
+    torch.cuda.empty_cache()
+    flags = torch.empty(n, dtype=torch.int32, device="cuda")
+    for c0 in range(0, n, 1 << 26):
+        c1 = min(n, c0 + (1 << 26))
+        flags[c0:c1] = ((torch.arange(c0, c1, dtype=torch.int64, device="cuda") % 1000) == 0).to(torch.int32) * 7
+    gu.say(f"offsets_from_flags n={n}")
+    fo, fc = sr.offsets_from_flags(flags.view(torch.uint32))
+    fc = int(fc.item())
+    assert fc == runs and np.array_equal(fo[: fc + 1].cpu().numpy(), want_off)
+    del flags, fo
+    torch.cuda.empty_cache()
