@@ -203,3 +203,15 @@ def test_runs_past_2_31_keys():
     assert fc == runs and np.array_equal(fo[: fc + 1].cpu().numpy(), want_off)
     del flags, fo
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("feat,rows", [(4099, 700), (40_000, 90)])
+def test_very_wide_rows(feat, rows):
+    """Rows of thousands of features: the chunked walk runs over many feature
+    blocks and the combine over wide partials (oracle comparison)."""
+    import workloads as W
+    off, vals = W.ragged(seed=feat, segments=9, mean_len=rows // 10, feat=feat, dtype="f32", empty_frac=0.2,
+                         base=3, tail_rows=2, long_segment=rows // 3)
+    for op in ("sum", "max"):
+        for shares in (None, 7):
+            gu.check(vals, off, op, shares=shares, what=f"wide F={feat}")
