@@ -75,20 +75,26 @@ __device__ __forceinline__ void load_tile(const uint32_t *keys, int64_t n, int64
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kRleKeysPerThread; ++u) t.k[u] = s_keys[u * kRleThreads + tid];
+    // Positions are taken relative to the tile (32-bit): those at or past
+    // `lim` lie past n (only in the last tile), and position 0 of the first
+    // tile starts a run whatever its key (`zero` is 0 there and no position
+    // elsewhere).
+    const uint32_t lim = (uint32_t)avail;
     if constexpr (MODE == MODE_FLAGS) {
         // a start is a nonzero flag: no neighbour is needed
 #pragma unroll
         for (int u = 0; u < kRleKeysPerThread; ++u)
-            t.head[u] = start + u * kRleThreads + tid < n && t.k[u] != 0u;
+            t.head[u] = (uint32_t)(u * kRleThreads + tid) < lim && t.k[u] != 0u;
         return;
     }
+    const uint32_t zero = start == 0 ? 0u : 0xFFFFFFFFu;
 #pragma unroll
     for (int u = 0; u < kRleKeysPerThread; ++u) {
         const int p0 = u * kRleThreads + wid * 64;  // the wave's first position in the tile at this step
         const uint32_t wave_prev = p0 > 0 ? s_keys[p0 > 0 ? p0 - 1 : 0] : before;
         const uint32_t prev = dpp_move<kDppWaveShr1>(wave_prev, t.k[u]);  // lane 0 keeps wave_prev
-        const int64_t i = start + p0 + lane;
-        t.head[u] = i < n && (i == 0 || t.k[u] != prev);
+        const uint32_t p = (uint32_t)(p0 + lane);
+        t.head[u] = p < lim && (t.k[u] != prev || p == zero);
     }
 }
 
@@ -108,14 +114,21 @@ __global__ __launch_bounds__(kRleThreads) void rle_count(const uint32_t *keys, i
     const int64_t start = (int64_t)blockIdx.x * kRleTile;
     TileKeys t;
     load_tile<MODE>(keys, n, start, tid, t, s_keys);
-    int64_t cnt = 0, first = INT64_MAX;
+    int64_t cnt = 0;
     uint64_t mine = 0;  // lane u keeps step u's ballot
 #pragma unroll
     for (int u = 0; u < kRleKeysPerThread; ++u) {
         const uint64_t m = ballot(t.head[u]);
         cnt += popc64(m);
-        if (m && first == INT64_MAX) first = start + u * kRleThreads + wid * 64 + (int)__builtin_ctzll(m);
         if (lane == u) mine = m;
+    }
+    // the wave's first start: the lowest lane of the lowest step that has one
+    const uint64_t steps = ballot(mine != 0ull);
+    int64_t first = INT64_MAX;
+    if (steps) {
+        const int u0 = (int)__builtin_ctzll(steps);
+        const uint64_t m0 = (uint64_t)readlane64((int64_t)mine, u0);
+        first = start + u0 * kRleThreads + wid * 64 + (int)__builtin_ctzll(m0);
     }
     if (lane < kRleKeysPerThread) tile_mask[mask_word(blockIdx.x, lane, wid)] = mine;
     if (lane == 0) {
