@@ -215,3 +215,23 @@ def test_very_wide_rows(feat, rows):
     for op in ("sum", "max"):
         for shares in (None, 7):
             gu.check(vals, off, op, shares=shares, what=f"wide F={feat}")
+
+
+def test_scratch_beyond_device_memory_is_reported():
+    """A call whose scratch cannot be had (2,048 shares x 2^24 features x two
+    8-byte partial slots = 512 GiB) returns SEGRED_ERR_OUT_OF_MEMORY before
+    any launch, and the next call on the same stream works."""
+    import segmented_reduction_amd as sr
+    feat = 1 << 24  # the widest row the library accepts
+    vals = torch.ones((2, feat), dtype=torch.float32, device="cuda")
+    off = torch.tensor([0, 2], dtype=torch.int64, device="cuda")
+    gu.say("scratch beyond device memory F=2^24")
+    with pytest.raises(sr.SegredError) as e:
+        sr.reduce(vals, off, "sum")
+    assert e.value.status == 3
+    del vals
+    torch.cuda.empty_cache()
+    small = torch.arange(12, dtype=torch.float32, device="cuda").reshape(3, 4)
+    out, _ = sr.reduce(small, torch.tensor([0, 1, 3], dtype=torch.int64, device="cuda"), "sum")
+    torch.cuda.synchronize()
+    assert out.cpu().tolist() == [[0, 1, 2, 3], [12, 14, 16, 18]]
