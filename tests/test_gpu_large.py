@@ -235,3 +235,51 @@ def test_scratch_beyond_device_memory_is_reported():
     out, _ = sr.reduce(small, torch.tensor([0, 1, 3], dtype=torch.int64, device="cuda"), "sum")
     torch.cuda.synchronize()
     assert out.cpu().tolist() == [[0, 1, 2, 3], [12, 14, 16, 18]]
+
+
+def test_scatter_and_index_offsets_past_2_31_rows():
+    """2^31 + 123 rows scattered by index r mod 1,000,003 (every destination
+    gets about 2,147 rows spread over the whole input), values (r mod 7) - 3:
+    sums (exact in any order), max with its first row, and the CSR pointer,
+    all in closed form."""
+    import segmented_reduction_amd as sr
+    n, dim = 2 ** 31 + 123, 1_000_003
+    c = dim % 7  # 4: step of the residue from one row of a destination to its next
+    index = torch.empty(n, dtype=torch.int64, device="cuda")
+    vals = torch.empty(n, dtype=torch.float32, device="cuda")
+    for c0 in range(0, n, 1 << 26):
+        c1 = min(n, c0 + (1 << 26))
+        r = torch.arange(c0, c1, dtype=torch.int64, device="cuda")
+        index[c0:c1] = r % dim
+        vals[c0:c1] = (r % 7 - 3).to(torch.float32)
+    del r
+    torch.cuda.synchronize()
+    d = np.arange(dim, dtype=np.int64)
+    K = (n - 1 - d) // dim + 1                      # rows of destination d
+    rem = K % 7                                     # full periods of 7 rows sum to zero
+    want_sum = np.zeros(dim, dtype=np.int64)
+    for j in range(7):
+        k = K - rem + j
+        want_sum += np.where(j < rem, (d + c * k) % 7 - 3, 0)
+    inv = next(x for x in range(1, 7) if (c * x) % 7 == 1)
+    k0 = ((6 - d) * inv) % 7                        # first k with residue 6 (value 3); K >= 7 everywhere
+    want_arg = d + k0 * dim
+    gu.say(f"scatter sum rows={n} dim={dim}")
+    out, _ = sr.scatter(vals, index, dim, "sum")
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().astype(np.int64), want_sum)
+    del out
+    gu.say(f"scatter max rows={n} dim={dim}")
+    out, arg = sr.scatter(vals, index, dim, "max")
+    torch.cuda.synchronize()
+    assert (out.cpu().numpy() == 3.0).all()
+    assert np.array_equal(arg.cpu().numpy(), want_arg)
+    del out, arg
+    gu.say(f"offsets_from_index rows={n} dim={dim}")
+    off = sr.offsets_from_index(index, dim)
+    torch.cuda.synchronize()
+    want_off = np.zeros(dim + 1, dtype=np.int64)
+    np.cumsum(K, out=want_off[1:])
+    assert np.array_equal(off.cpu().numpy(), want_off)
+    del index, vals, off
+    torch.cuda.empty_cache()
