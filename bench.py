@@ -703,6 +703,61 @@ def stream_ceiling(sr, torch, reps=20):
     return rows
 
 
+# ---------------------------------------------------------------- shape sweep
+
+SWEEP_FEATS = (1, 2, 3, 4, 8, 12, 16, 24, 32, 64, 128, 256)
+SWEEP_LENS = (1, 4, 16, 128, 4096, 1 << 20)
+SWEEP_BYTES = 512 << 20  # input per shape: twice the last-level cache
+
+
+def shape_sweep(sr, torch, reps=10):
+    """Per-call rates of segred_reduce (sum, and max with rows) across row
+    widths and mean segment lengths, each on SWEEP_BYTES of float32 normal
+    values generated on the device with segment lengths uniform in
+    [0, 2 * mean] scaled to cover the rows exactly (seeded), two input
+    copies alternated so that no call
+    finds its rows in the cache.  Durations are the pass-1 kernel's own
+    start and stop events (median of `reps`); rates count the algorithmic
+    bytes of the call."""
+    rows_out = []
+    gen = torch.Generator(device="cuda")
+    for feat in SWEEP_FEATS:
+        n = SWEEP_BYTES // (4 * feat)
+        for mean in SWEEP_LENS:
+            gen.manual_seed(feat * 1000003 + mean)
+            segs = max(1, n // mean)
+            lens = torch.randint(0, 2 * mean + 1, (segs,), generator=gen, device="cuda", dtype=torch.int64)
+            # scaled so that the segments cover the n rows exactly
+            lens = torch.floor(lens.double() * (n / max(float(lens.sum().item()), 1.0))).to(torch.int64)
+            lens[0] += n - int(lens.sum().item())
+            off = torch.zeros(segs + 1, dtype=torch.int64, device="cuda")
+            off[1:] = torch.cumsum(lens, 0)
+            total = int(off[-1].item())
+            shape = (n,) if feat == 1 else (n, feat)
+            vals = [torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32) for _ in range(2)]
+            entry = {"feat": feat, "mean_len": mean, "segments": segs, "rows": total}
+            for op in ("sum", "max"):
+                for i in range(2):
+                    sr.reduce(vals[i], off, op)
+                torch.cuda.synchronize()
+                sr.timing_enable(True)
+                sr.timing_read()
+                for i in range(reps):
+                    sr.reduce(vals[i % 2], off, op)
+                torch.cuda.synchronize()
+                _, _, each = sr.timing_read()
+                sr.timing_enable(False)
+                med = float(np.median(each))
+                b = reduce_bytes(total, feat, segs, op)
+                entry[op] = {"median_us": round(med * 1e3, 2), "GBps": round(b / (med * 1e-3) / 1e9, 1),
+                             "frac": round(b / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
+            print(json.dumps(entry), flush=True)
+            rows_out.append(entry)
+            del vals, off, lens
+            torch.cuda.empty_cache()
+    return rows_out
+
+
 # ---------------------------------------------------------------- main
 
 GATED = ["message", "rle", "skew"]  # reported beside the headline (largest) configuration
@@ -859,6 +914,8 @@ def main():
                     help="skip the streaming-ceiling probe (segred_probe_stream over 2 GiB)")
     ap.add_argument("--ceiling-only", action="store_true",
                     help="run only the streaming-ceiling probe and print its figures")
+    ap.add_argument("--sweep", action="store_true",
+                    help="per-call rates across row widths and mean segment lengths (one JSON line per shape)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain device copy of 256 MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -884,6 +941,10 @@ def main():
         return
 
     import segmented_reduction_amd as sr
+
+    if args.sweep:
+        shape_sweep(sr, torch)
+        return
 
     if args.ceiling_only:
         print(json.dumps({"stream_ceiling": stream_ceiling(sr, torch)}), flush=True)

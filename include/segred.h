@@ -106,8 +106,8 @@ int segred_reduce(const void *values, int32_t dtype, int64_t feat,
  *   Arguments, results and errors: as segred_reduce, plus
  *   SEGRED_ERR_SCRATCH_LIMIT when the call needs more than the fixed
  *   scratch: 32 * NS + 16 * NS * feat bytes, NS = the call's share count
- *   (4,096 for rows of at most 128 bytes, 2,048 for 1-D values and wider
- *   rows), i.e. feat up to 510.  Results are bitwise equal to
+ *   (4,096 for rows of 32 features read 16 bytes per lane, 2,048 for all
+ *   other rows and 1-D values), i.e. feat up to 510.  Results are bitwise equal to
  *   segred_reduce's (same kernels, same shares).
  *
  * All calls on one device share that device's array: calls that overlap in

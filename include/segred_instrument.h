@@ -26,8 +26,8 @@ extern "C" {
  * results do not depend on the device.  segred_set_shares(n) overrides it
  * for later calls (rounded up to a multiple of 4); 0 restores the default.
  * With an override the last bits of float sums change (integer, min/max and
- * row results do not), and for rows of at most 128 bytes one share must not
- * hold 4 GiB or more of rows.  Returns SEGRED_ERR_INVALID_ARGUMENT (1) unless
+ * row results do not), and for rows of 32 features read 16 bytes per lane
+ * one share must not hold 4 GiB or more of rows.  Returns SEGRED_ERR_INVALID_ARGUMENT (1) unless
  * shares == 0 or 1 <= shares <= 2^22.
  */
 int segred_set_shares(int64_t shares);

@@ -16,12 +16,12 @@
 // over many waves instead of serialising on one.
 //
 // Inside a share:
-//  - rows of at most 128 bytes (seg_reduce_team): the wave's share is cut
-//    again into equal parts, one per team of L lanes (one row), and each
-//    team walks its part row by row with its own accumulators and queue of
-//    segment ends; the teams' partials of cut segments are folded in team
-//    order at the end;
-//  - wider rows (seg_reduce_rows): the wave walks chunks of G groups x V
+//  - rows of 32 features with 16-byte access (seg_reduce_team): the
+//    wave's share is cut again into equal parts, one per team of L lanes
+//    (one row), and each team walks its part row by row with its own
+//    accumulators and queue of segment ends; the teams' partials of cut
+//    segments are folded in team order at the end;
+//  - all other rows (seg_reduce_rows): the wave walks chunks of G groups x V
 //    consecutive rows; a group walks its rows in order, finishing every
 //    segment that ends inside it, and a segmented scan over the groups
 //    completes the segments cut by group and chunk boundaries;
@@ -1232,10 +1232,14 @@ static int lanes_for(int64_t units, int lo) {
 // Pass-1 kernel for a row width and the alignment of the arrays, and its
 // share count.  Rows take 16-byte access (four features per lane) when they
 // are whole 16-byte units and values, out and arg_out start on 16 bytes,
-// else one feature per lane.  Rows of at most 128 bytes are walked by teams
-// (8 or more rows per load instruction, no per-chunk cross-lane step); wider
-// rows by chunks, whose few row groups per wave make the chunk's cross-lane
-// steps cheap and keep each load instruction on one contiguous stretch.
+// else one feature per lane.  Rows of 32 features with 16-byte access are
+// walked by teams of 8 lanes (8 whole 128-byte rows per load instruction,
+// no per-chunk cross-lane step); all other rows by chunks.  Other rows
+// walked by teams would give each team a piece of 4 to 112 bytes per load
+// instruction, from up to 64 places, and the L2 request rate caps that: on
+// 512 MB of rows of 2 to 24 features the team walk moved 0.04-0.52 of
+// peak, the chunked walk 0.10-0.68, whose load instructions stay within
+// one chunk of the rows.
 struct Pick {
     const void *kernel;
     int64_t waves;  // shares (one per wave) of a call
@@ -1252,20 +1256,20 @@ static Pick pick_kernel(int64_t feat, bool vec4) {
         if (feat == 32) return SEGRED_TEAM(8, 8, 4, 32);
         if (feat == 64) return SEGRED_ROWS(16, 8, 4, 64);
         switch (lanes_for(feat / 4, 1)) {
-        case 1: return SEGRED_TEAM(1, 8, 4, 0);
-        case 2: return SEGRED_TEAM(2, 8, 4, 0);
-        case 4: return SEGRED_TEAM(4, 8, 4, 0);
-        case 8: return SEGRED_TEAM(8, 8, 4, 0);
+        case 1: return SEGRED_ROWS(1, 8, 4, 0);
+        case 2: return SEGRED_ROWS(2, 8, 4, 0);
+        case 4: return SEGRED_ROWS(4, 8, 4, 0);
+        case 8: return SEGRED_ROWS(8, 8, 4, 0);
         case 16: return SEGRED_ROWS(16, 8, 4, 0);
         case 32: return SEGRED_ROWS(32, 8, 4, 0);
         default: return SEGRED_ROWS(64, 8, 4, 0);
         }
     }
     switch (lanes_for(feat, 2)) {
-    case 2: return SEGRED_TEAM(2, 16, 1, 0);
-    case 4: return SEGRED_TEAM(4, 16, 1, 0);
-    case 8: return SEGRED_TEAM(8, 16, 1, 0);
-    case 16: return SEGRED_TEAM(16, 16, 1, 0);
+    case 2: return SEGRED_ROWS(2, 24, 1, 0);
+    case 4: return SEGRED_ROWS(4, 24, 1, 0);
+    case 8: return SEGRED_ROWS(8, 24, 1, 0);
+    case 16: return SEGRED_ROWS(16, 24, 1, 0);
     case 32: return SEGRED_ROWS(32, 24, 1, 0);
     default: return SEGRED_ROWS(64, 24, 1, 0);
     }

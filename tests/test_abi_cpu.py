@@ -237,7 +237,8 @@ def test_share_knob_range():
 # on every device, so float sums repeat across devices and partition modes.
 @pytest.mark.parametrize("dtype,op,feat,shares", [
     (2, 0, 1, 2048), (2, 3, 1, 2048), (0, 0, 1, 2048), (2, 1, 1, 2048), (1, 2, 1, 2048),
-    (2, 0, 32, 4096), (2, 2, 32, 4096), (2, 3, 32, 4096), (2, 0, 8, 4096), (0, 1, 3, 4096),
+    (2, 0, 32, 4096), (2, 2, 32, 4096), (2, 3, 32, 4096), (2, 0, 24, 2048), (2, 0, 8, 2048), (0, 1, 3, 2048),
+    (2, 0, 16, 2048), (1, 2, 4, 2048),
     (2, 0, 64, 2048), (2, 2, 64, 2048), (2, 0, 260, 2048), (2, 0, 33, 2048), (1, 1, 100, 2048),
 ])
 def test_default_share_counts_are_constants(dtype, op, feat, shares):

@@ -73,8 +73,9 @@ def test_descriptors_stay_inside_the_rows(feat):
                     _check(lo, hi, o0 + rb, n * 4, ("scan tails 1-D", nw, rb))
         row_bytes = feat * 4
         vec4 = feat % 4 == 0
-        if vec4 and feat <= 32 or not vec4 and feat <= 16:
-            # seg_reduce_team: one descriptor over the wave's share, from
+        if feat == 32:
+            # seg_reduce_team (rows of 32 features, 16-byte access): one
+            # descriptor over the wave's share, from
             # feature block fbase: make_rsrc(values + (o0 + j0) * F + fbase,
             # (j1 - j0) * F * 4 - fbase * 4)
             units = feat // 4 if vec4 else feat
