@@ -225,6 +225,10 @@ __device__ __forceinline__ void store_final(const KArgs &a, int64_t seg, int64_t
             put(reinterpret_cast<i64x2 *>(a.arg + o), i64x2{ab[0], ab[1]});
             put(reinterpret_cast<i64x2 *>(a.arg + o) + 1, i64x2{ab[2], ab[3]});
         }
+    } else if constexpr (VEC == 2) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        put(reinterpret_cast<u32x2 *>(a.out + o), u32x2{ob[0], ob[1]});
+        if (Red<DT, OP>::kMinMax && a.arg) put(reinterpret_cast<i64x2 *>(a.arg + o), i64x2{ab[0], ab[1]});
     } else {
         put(a.out + o, ob[0]);
         if (Red<DT, OP>::kMinMax && a.arg) put(a.arg + o, ab[0]);
@@ -275,6 +279,12 @@ struct Lanes<1> {
     __device__ static __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) { return ld32(r, off); }
 };
 template <>
+struct Lanes<2> {
+    using type = uint2;
+    __device__ static __forceinline__ uint32_t at(const uint2 &x, int v) { return v == 0 ? x.x : x.y; }
+    __device__ static __forceinline__ uint2 load(__amdgpu_buffer_rsrc_t r, uint32_t off) { return ld64(r, off); }
+};
+template <>
 struct Lanes<4> {
     using type = uint4;
     __device__ static __forceinline__ uint32_t at(const uint4 &x, int v) {
@@ -312,7 +322,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kRowsWpe)))
 
     for (int64_t fbase = 0; fbase < F; fbase += FB) {
         const int64_t f0 = fbase + (int64_t)c * VEC;
-        // VEC = 4 is used only when F is a multiple of 4, so a lane's four
+        // VEC = 4 (2) is used only when F is a multiple of 4 (2), so a lane's
         // features are all inside the row or all past it
         const bool fvalid = f0 < F;
 
@@ -1232,7 +1242,9 @@ static int lanes_for(int64_t units, int lo) {
 // Pass-1 kernel for a row width and the alignment of the arrays, and its
 // share count.  Rows take 16-byte access (four features per lane) when they
 // are whole 16-byte units and values, out and arg_out start on 16 bytes,
-// else one feature per lane.  Rows of 32 features with 16-byte access are
+// 8-byte access (two) when their width is otherwise even under the same
+// condition, else one feature per lane.  Rows of 32 features with 16-byte
+// access are
 // walked by teams of 8 lanes (8 whole 128-byte rows per load instruction,
 // no per-chunk cross-lane step); all other rows by chunks.  Other rows
 // walked by teams would give each team a piece of 4 to 112 bytes per load
@@ -1243,7 +1255,8 @@ static int lanes_for(int64_t units, int lo) {
 // per group (V), so that a load instruction's lanes sit closer together:
 // 4 features V = 2 (0.12-0.21 -> 0.14-0.55 of peak across segment lengths),
 // 8 features V = 4, and one feature per lane on 2 or 4 lanes V = 8 instead
-// of 24 (2 features 0.10-0.12 -> 0.13-0.22).
+// of 24.  Even widths that are not whole 16-byte units take two features
+// per lane (8-byte access): 2 features 0.10-0.12 -> 0.15-0.43 of peak.
 struct Pick {
     const void *kernel;
     int64_t waves;  // shares (one per wave) of a call
@@ -1267,6 +1280,18 @@ static Pick pick_kernel(int64_t feat, bool vec4) {
         case 16: return SEGRED_ROWS(16, 8, 4, 0);
         case 32: return SEGRED_ROWS(32, 8, 4, 0);
         default: return SEGRED_ROWS(64, 8, 4, 0);
+        }
+    }
+    if (vec4 && feat % 2 == 0) {
+        // even widths that are not whole 16-byte units: 8-byte access
+        switch (lanes_for(feat / 2, 1)) {
+        case 1: return SEGRED_ROWS(1, 4, 2, 0);
+        case 2: return SEGRED_ROWS(2, 4, 2, 0);
+        case 4: return SEGRED_ROWS(4, 8, 2, 0);
+        case 8: return SEGRED_ROWS(8, 8, 2, 0);
+        case 16: return SEGRED_ROWS(16, 8, 2, 0);
+        case 32: return SEGRED_ROWS(32, 8, 2, 0);
+        default: return SEGRED_ROWS(64, 8, 2, 0);
         }
     }
     switch (lanes_for(feat, 2)) {

@@ -145,6 +145,12 @@ __device__ __forceinline__ uint32_t ld32(__amdgpu_buffer_rsrc_t r, uint32_t voff
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, kStreamPolicy);
 }
 
+__device__ __forceinline__ uint2 ld64(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    // Range checking is per dword, as for ld128.
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, kStreamPolicy);
+    return make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+}
+
 __device__ __forceinline__ uint4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
     // Range checking is per dword: a 16-byte unit cut by the limit returns its
     // in-range dwords and zeros for the rest.

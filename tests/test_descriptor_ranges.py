@@ -91,12 +91,18 @@ def test_descriptors_stay_inside_the_rows(feat):
             # seg_reduce_rows: chunk of CH rows from row jc and feature block
             # fbase, make_rsrc(values + (o0 + jc) * F + fbase, rmax * row_bytes - fbase * 4)
             for vec, lanes in ((4, min(64, 1 << (max(1, feat // 4) - 1).bit_length())),
+                               (2, min(64, 1 << (max(1, feat // 2) - 1).bit_length())),
                                (1, min(64, 1 << (feat - 1).bit_length()))):
-                if vec == 4 and not vec4:
+                if vec == 4 and not vec4 or vec == 2 and (vec4 or feat % 2):
                     continue
-                lanes = max(lanes, 1 if vec == 4 else 2)
+                lanes = max(lanes, 1 if vec > 1 else 2)
                 # rows per group: fewer for the narrowest rows
-                v = {1: 2, 2: 4}.get(lanes, 8) if vec == 4 else (8 if lanes <= 4 else 24)
+                if vec == 4:
+                    v = {1: 2, 2: 4}.get(lanes, 8)
+                elif vec == 2:
+                    v = 4 if lanes <= 2 else 8
+                else:
+                    v = 8 if lanes <= 4 else 24
                 ch = (64 // lanes) * v
                 for _, _, _, j0, _, j1, _ in _shares(off, nw):
                     for jc in range(j0, j1 + 1):

@@ -20,8 +20,8 @@ from tests.test_gpu_scan import _check as scan_check
 
 pytestmark = pytest.mark.gpu
 
-FEATS = [1, 1, 1, 2, 3, 4, 5, 7, 8, 9, 12, 16, 24, 31, 32, 32, 33, 48, 63, 64, 64, 65, 96, 127, 128, 129,
-         255, 256, 257, 300, 513]
+FEATS = [1, 1, 1, 2, 2, 3, 4, 5, 6, 7, 8, 9, 10, 12, 14, 16, 18, 24, 30, 31, 32, 32, 33, 34, 48, 63, 64, 64,
+         65, 66, 96, 127, 128, 129, 130, 255, 256, 257, 258, 300, 513]
 MIXES = ["uniform", "pareto", "ones", "empty_runs", "few_huge", "zipf_runs"]
 SHARES = [None, None, None, 1, 2, 3, 4, 7, 64, 333, 4096, 5000]
 
