@@ -1240,23 +1240,22 @@ static int lanes_for(int64_t units, int lo) {
 }
 
 // Pass-1 kernel for a row width and the alignment of the arrays, and its
-// share count.  Rows take 16-byte access (four features per lane) when they
-// are whole 16-byte units and values, out and arg_out start on 16 bytes,
-// 8-byte access (two) when their width is otherwise even under the same
-// condition, else one feature per lane.  Rows of 32 features with 16-byte
-// access are
-// walked by teams of 8 lanes (8 whole 128-byte rows per load instruction,
-// no per-chunk cross-lane step); all other rows by chunks.  Other rows
-// walked by teams would give each team a piece of 4 to 112 bytes per load
-// instruction, from up to 64 places, and the L2 request rate caps that: on
-// 512 MB of rows of 2 to 24 features the team walk moved 0.04-0.52 of
-// peak, the chunked walk 0.10-0.68, whose load instructions stay within
-// one chunk of the rows.  For the narrowest rows the chunk holds fewer rows
-// per group (V), so that a load instruction's lanes sit closer together:
-// 4 features V = 2 (0.12-0.21 -> 0.14-0.55 of peak across segment lengths),
-// 8 features V = 4, and one feature per lane on 2 or 4 lanes V = 8 instead
-// of 24.  Even widths that are not whole 16-byte units take two features
-// per lane (8-byte access): 2 features 0.10-0.12 -> 0.15-0.43 of peak.
+// share count.  When values, out and arg_out start on 16 bytes, rows that
+// are whole 16-byte units take 16-byte access (four features per lane) and
+// other even widths 8-byte access (two); all other rows one feature per
+// lane.  Rows of 32 features with 16-byte access are walked by teams of 8
+// lanes (8 whole 128-byte rows per load instruction, no per-chunk
+// cross-lane step); all other rows by chunks.  Other rows walked by teams
+// would give each team a piece of 4 to 112 bytes per load instruction,
+// from up to 64 places, and the L2 request rate caps that: on 512 MB of
+// rows of 2 to 24 features the team walk moved 0.04-0.52 of peak, the
+// chunked walk 0.10-0.68, whose load instructions stay within one chunk of
+// the rows.  For the narrowest rows the chunk holds fewer rows per group
+// (V), so that a load instruction's lanes sit closer together: 4 features
+// V = 2 (0.12-0.21 -> 0.14-0.50 of peak across segment lengths), 8
+// features V = 4, 2 features (8-byte access) V = 4 (0.10-0.12 with 4-byte
+// access -> 0.15-0.43), and one feature per lane on 2 or 4 lanes V = 8
+// instead of 24.
 struct Pick {
     const void *kernel;
     int64_t waves;  // shares (one per wave) of a call
@@ -1266,10 +1265,10 @@ struct Pick {
 #define SEGRED_ROWS(L, V, VEC, FC) \
     Pick{reinterpret_cast<const void *>(&seg_reduce_rows<DT, OP, L, V, VEC, FC>), kShareSimds * kRowsWpe}
 template <int DT, int OP>
-static Pick pick_kernel(int64_t feat, bool vec4) {
+static Pick pick_kernel(int64_t feat, bool aligned16) {
     if (feat == 1)
         return Pick{reinterpret_cast<const void *>(&seg_reduce_flat<DT, OP>), kShareSimds * flat_wpe<DT, OP>()};
-    if (vec4 && feat % 4 == 0) {
+    if (aligned16 && feat % 4 == 0) {
         if (feat == 32) return SEGRED_TEAM(8, 8, 4, 32);
         if (feat == 64) return SEGRED_ROWS(16, 8, 4, 64);
         switch (lanes_for(feat / 4, 1)) {
@@ -1282,7 +1281,7 @@ static Pick pick_kernel(int64_t feat, bool vec4) {
         default: return SEGRED_ROWS(64, 8, 4, 0);
         }
     }
-    if (vec4 && feat % 2 == 0) {
+    if (aligned16 && feat % 2 == 0) {
         // even widths that are not whole 16-byte units: 8-byte access
         switch (lanes_for(feat / 2, 1)) {
         case 1: return SEGRED_ROWS(1, 4, 2, 0);
@@ -1342,8 +1341,8 @@ static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 // beyond the fixed scratch an error instead.
 template <int DT, int OP>
 static int run(KArgs k, hipStream_t st, void *fixed_scratch) {
-    const bool vec4 = aligned(k.values, 16) && aligned(k.out, 16) && (!k.arg || aligned(k.arg, 16));
-    const Pick pk = pick_kernel<DT, OP>(k.F, vec4);
+    const bool a16 = aligned(k.values, 16) && aligned(k.out, 16) && (!k.arg || aligned(k.arg, 16));
+    const Pick pk = pick_kernel<DT, OP>(k.F, a16);
     const int64_t nw = shares_for(pk);
     const int64_t ns = nw;
     const size_t bytes = scratch_bytes(ns, k.F);
