@@ -246,6 +246,15 @@ __device__ __forceinline__ int count_le(const uint32_t *arr, int n, uint32_t x) 
     return lo;
 }
 
+// LDS place (in 16-byte units) of unit c of the 8 consecutive units that a
+// lane owns, where a load instruction's lanes read 1 KB of consecutive units
+// (8 lanes per owner): the low three bits are rotated by the owner so that
+// the writes (8 owners x 8 units) and the reads (64 owners, one unit each)
+// both spread over the banks.
+__device__ __forceinline__ int flat_unit(int owner, int c) {
+    return owner * 8 + (c ^ ((owner & 7) ^ ((owner >> 3) & 1)));
+}
+
 // Header of a share for the combine kernel: [split head segment or -1,
 // continuing tail segment or -1, first row of the share, share holding the
 // split head segment's first row].
@@ -257,8 +266,9 @@ __device__ __forceinline__ void write_header(const KArgs &a, int64_t wave, const
 }
 
 // Pass 1 for rows of F >= 2 features: each lane owns VEC consecutive
-// features of a row (VEC = 4: 16-byte loads and stores; VEC = 1: one 4-byte
-// feature, for rows whose width or alignment rules out 16-byte access).
+// features of a row (VEC = 4: 16-byte pieces; VEC = 2: 8-byte pieces for
+// other even widths; VEC = 1: one 4-byte feature, for rows whose width or
+// alignment rules out the others).
 //   L   lanes per row (the power of two >= F / VEC, at most 64; wider rows
 //       are done in blocks of 64 * VEC features); G = 64 / L row groups per
 //       wave
@@ -269,7 +279,10 @@ __device__ __forceinline__ void write_header(const KArgs &a, int64_t wave, const
 // no cross-lane step is needed at all.  A chunk's rows are fetched together
 // with its first 64 segment ends before its row count is known (up to CH
 // rows; rows past the chunk are fetched again by the next chunk), and the
-// next chunk is fetched while the current one is processed.
+// next chunk is fetched while the current one is processed: straight into
+// the lanes' pieces, or, for fixed widths below 32 features, as whole 1 KB
+// stretches that pass through LDS (the 1-D kernel's placement of 16-byte
+// units), so that no load instruction gathers small pieces from many rows.
 template <int VEC>
 struct Lanes;
 template <>
@@ -306,6 +319,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kRowsWpe)))
     const int64_t F = FC > 0 ? (int64_t)FC : a.F;
 
     __shared__ __attribute__((aligned(16))) uint32_t s_ends[4][CH];
+    // Rows narrower than 32 features whose width is fixed at compile time:
+    // a chunk's bytes (at most 8 KB, one feature block) are read by load
+    // instructions of 1 KB of consecutive bytes each and reach their lanes
+    // through LDS, instead of load instructions whose lanes read pieces of 4
+    // to 16 bytes from up to 64 rows.
+    constexpr bool STG = FC > 0 && FC < 32;
+    constexpr int CB = STG ? CH * FC * 4 : 0;  // bytes per chunk
+    constexpr int NL = (CB + 1023) / 1024;      // 1 KB load instructions per chunk
+    static_assert(!STG || (FB >= FC && NL <= 8), "a staged chunk is one feature block of at most 8 KB");
+    __shared__ __attribute__((aligned(16))) uint32_t s_stage[4][STG ? NL * 256 : 4];
 
     const int wid = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -363,12 +386,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kRowsWpe)))
             return voff + (uint32_t)t * (FC > 0 ? (uint32_t)(FC * 4) : rstep);
         };
         x_t x[V];
+        uint4 xr[STG ? NL : 1];  // STG: the next chunk as loaded
         int64_t ic = sh.i0, jc = sh.j0;
         int64_t en = off[min(ic + 1 + lane, S)];
         {
             const auto rs = rows_of(ic, jc);
+            if constexpr (STG) {
 #pragma unroll
-            for (int t = 0; t < V; ++t) x[t] = LN::load(rs, row_off(t));
+                for (int u = 0; u < NL; ++u) xr[u] = ld128(rs, (uint32_t)(lane * 16 + u * 1024));
+            } else {
+#pragma unroll
+                for (int t = 0; t < V; ++t) x[t] = LN::load(rs, row_off(t));
+            }
         }
         while (ic + jc < sh.d1) {
             if constexpr (FC == 0) asm volatile("" : "+s"(rstep));
@@ -410,6 +439,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kRowsWpe)))
             }
             const auto rsn = rows_of(icn, jcn);
             const uint32_t relbase = (uint32_t)(jc - sh.j0);
+            if constexpr (STG) {
+                // Stage this chunk (16-byte unit k at LDS unit flat_unit(k / 8,
+                // k % 8)), start loading the next one, and take the lane's
+                // piece of each of its V rows back in row order.  Lanes past
+                // the row's features read row 0's piece, which they do not use.
+                const char *sb = reinterpret_cast<const char *>(s_stage[wid]);
+                uint32_t *sx = s_stage[wid];
+#pragma unroll
+                for (int u = 0; u < NL; ++u)
+                    *reinterpret_cast<uint4 *>(&sx[flat_unit(8 * u + (lane >> 3), lane & 7) * 4]) = xr[u];
+#pragma unroll
+                for (int u = 0; u < NL; ++u) xr[u] = ld128(rsn, (uint32_t)(lane * 16 + u * 1024));
+                wave_lds_sync();
+                const uint32_t b0 = fvalid ? voff : 0u;
+#pragma unroll
+                for (int t = 0; t < V; ++t) {
+                    const uint32_t b = b0 + (uint32_t)(t * FC * 4);
+                    const uint32_t k = b >> 4;
+                    x[t] = *reinterpret_cast<const x_t *>(sb + flat_unit((int)(k >> 3), (int)(k & 7u)) * 16 + (b & 15u));
+                }
+            }
 
             if (ne == 0) {
                 // No segment ends here: every row continues the open segment.
@@ -420,7 +470,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kRowsWpe)))
 #pragma unroll
                         for (int v = 0; v < VEC; ++v) open[v] = R::comb(open[v], R::lift(LN::at(x[t], v), relbase + r));
                     }
-                    x[t] = LN::load(rsn, row_off(t));
+                    if constexpr (!STG) x[t] = LN::load(rsn, row_off(t));
                 }
                 open_spread = G > 1;
                 ic = icn;
@@ -503,7 +553,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kRowsWpe)))
 #pragma unroll
                     for (int v = 0; v < VEC; ++v) acc[v] = R::comb(acc[v], R::lift(LN::at(x[t], v), relbase + r));
                 }
-                x[t] = LN::load(rsn, row_off(t));
+                if constexpr (!STG) x[t] = LN::load(rsn, row_off(t));
             }
             while (k < a_hi) finish();
 
@@ -849,6 +899,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kTeamWpe)))
     if (lane == 0) write_header(a, wave, sh);
 }
 
+// Weight of a segment end against one 1-D element in the merge-path shares.
+// An end costs an offsets read and an output store (and a row for min/max),
+// and a chunk holds at most EC of them, against 4 bytes per element; with
+// equal weights the shares over stretches of very short segments finish
+// last.  Measured on 16M sorted Zipf keys (0.71M runs): sum 30.8 -> 27.3 us,
+// min+row 37.1 -> 31.3 us from weight 1 to 8 (4: 29.2 / 33.4, 16: 27.6 /
+// 30.6, 32: 28.3 / 35.6); 50M elements in 1M segments unchanged.
+constexpr int kFlatEndWeight = 8;
+
 // Pass 1 for one feature per row (1-D values).
 //
 // A chunk is up to 2048 elements and up to 128 segment ends.  Its elements
@@ -874,19 +933,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kTeamWpe)))
 // the best element so far (MIN complements the key, so both are a maximum);
 // only its position byte is kept in LDS and the store looks the element up
 // again in the staged chunk.
-__device__ __forceinline__ int flat_unit(int owner, int c) {
-    return owner * 8 + (c ^ ((owner & 7) ^ ((owner >> 3) & 1)));
-}
-
-// Weight of a segment end against one 1-D element in the merge-path shares.
-// An end costs an offsets read and an output store (and a row for min/max),
-// and a chunk holds at most EC of them, against 4 bytes per element; with
-// equal weights the shares over stretches of very short segments finish
-// last.  Measured on 16M sorted Zipf keys (0.71M runs): sum 30.8 -> 27.3 us,
-// min+row 37.1 -> 31.3 us from weight 1 to 8 (4: 29.2 / 33.4, 16: 27.6 /
-// 30.6, 32: 28.3 / 35.6); 50M elements in 1M segments unchanged.
-constexpr int kFlatEndWeight = 8;
-
 template <int DT, int OP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(flat_wpe<DT, OP>())))
 void seg_reduce_flat(const KArgs a) {
@@ -1249,13 +1295,16 @@ static int lanes_for(int64_t units, int lo) {
 // would give each team a piece of 4 to 112 bytes per load instruction,
 // from up to 64 places, and the L2 request rate caps that: on 512 MB of
 // rows of 2 to 24 features the team walk moved 0.04-0.52 of peak, the
-// chunked walk 0.10-0.68, whose load instructions stay within one chunk of
-// the rows.  For the narrowest rows the chunk holds fewer rows per group
-// (V), so that a load instruction's lanes sit closer together: 4 features
-// V = 2 (0.12-0.21 -> 0.14-0.50 of peak across segment lengths), 8
-// features V = 4, 2 features (8-byte access) V = 4 (0.10-0.12 with 4-byte
-// access -> 0.15-0.43), and one feature per lane on 2 or 4 lanes V = 8
-// instead of 24.
+// chunked walk 0.10-0.68.  The chunked walk's pieces still come from many
+// rows per instruction, so the usual widths below 32 features (2, 3, 4, 6,
+// 8, 12, 16, 24) get kernels of their own that read each chunk (6 or 8 KB)
+// in whole 1 KB stretches through LDS: on the same 512 MB, sum and max+row
+// over segments of 4,096 rows and more went from 0.25-0.68 to 0.60-0.80 of
+// peak, over segments of 16 rows from 0.14-0.47 to 0.25-0.50.  The same
+// staging for 32 features (by chunks instead of teams) and for 64 moved less
+// on segments of 1 to 16 rows and on the power-law graph (0.58 -> 0.54 of
+// peak), so those keep their direct loads.  One feature per lane on 2 or 4
+// lanes takes V = 8 instead of 24.
 struct Pick {
     const void *kernel;
     int64_t waves;  // shares (one per wave) of a call
@@ -1271,9 +1320,12 @@ static Pick pick_kernel(int64_t feat, bool aligned16) {
     if (aligned16 && feat % 4 == 0) {
         if (feat == 32) return SEGRED_TEAM(8, 8, 4, 32);
         if (feat == 64) return SEGRED_ROWS(16, 8, 4, 64);
+        if (feat == 4) return SEGRED_ROWS(1, 8, 4, 4);
+        if (feat == 8) return SEGRED_ROWS(2, 8, 4, 8);
+        if (feat == 12) return SEGRED_ROWS(4, 8, 4, 12);
+        if (feat == 16) return SEGRED_ROWS(4, 8, 4, 16);
+        if (feat == 24) return SEGRED_ROWS(8, 8, 4, 24);
         switch (lanes_for(feat / 4, 1)) {
-        case 1: return SEGRED_ROWS(1, 2, 4, 0);
-        case 2: return SEGRED_ROWS(2, 4, 4, 0);
         case 4: return SEGRED_ROWS(4, 8, 4, 0);
         case 8: return SEGRED_ROWS(8, 8, 4, 0);
         case 16: return SEGRED_ROWS(16, 8, 4, 0);
@@ -1283,9 +1335,9 @@ static Pick pick_kernel(int64_t feat, bool aligned16) {
     }
     if (aligned16 && feat % 2 == 0) {
         // even widths that are not whole 16-byte units: 8-byte access
+        if (feat == 2) return SEGRED_ROWS(1, 16, 2, 2);
+        if (feat == 6) return SEGRED_ROWS(4, 16, 2, 6);
         switch (lanes_for(feat / 2, 1)) {
-        case 1: return SEGRED_ROWS(1, 4, 2, 0);
-        case 2: return SEGRED_ROWS(2, 4, 2, 0);
         case 4: return SEGRED_ROWS(4, 8, 2, 0);
         case 8: return SEGRED_ROWS(8, 8, 2, 0);
         case 16: return SEGRED_ROWS(16, 8, 2, 0);
@@ -1293,6 +1345,7 @@ static Pick pick_kernel(int64_t feat, bool aligned16) {
         default: return SEGRED_ROWS(64, 8, 2, 0);
         }
     }
+    if (feat == 3) return SEGRED_ROWS(4, 32, 1, 3);
     switch (lanes_for(feat, 2)) {
     case 2: return SEGRED_ROWS(2, 8, 1, 0);
     case 4: return SEGRED_ROWS(4, 8, 1, 0);

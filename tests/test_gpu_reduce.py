@@ -61,7 +61,7 @@ def test_empty_segments_fixture(kind):
             assert arg[:, 0].tolist() == g["arg" + op]
 
 
-FEATS = [1, 2, 3, 4, 5, 8, 16, 32, 33, 64, 65, 128, 256, 260]
+FEATS = [1, 2, 3, 4, 5, 6, 8, 12, 16, 24, 32, 33, 64, 65, 128, 256, 260]
 
 
 @pytest.mark.parametrize("feat", FEATS)
@@ -83,7 +83,7 @@ def test_random_ragged(kind, feat):
             gu.assert_parity(vals, off, op, out, arg, orc=orc, what=f"ragged F={feat} shares={shares}")
 
 
-@pytest.mark.parametrize("feat", [1, 3, 4, 32, 64])
+@pytest.mark.parametrize("feat", [1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 64])
 @pytest.mark.parametrize("kind", ["u32", "i32", "f32"])
 def test_ties_go_to_lower_row(kind, feat):
     off, vals = W.ragged(seed=100 + feat, segments=2000, mean_len=15, feat=feat, dtype=kind, values="ties",
@@ -94,7 +94,7 @@ def test_ties_go_to_lower_row(kind, feat):
             gu.assert_parity(vals, off, op, out, arg, what=f"ties F={feat} shares={shares}")
 
 
-@pytest.mark.parametrize("feat", [1, 4, 32, 64, 5])
+@pytest.mark.parametrize("feat", [1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 64, 5])
 def test_integer_valued_floats_sum_exactly(feat):
     """Small integer-valued floats add exactly in any order: the GPU sum must
     equal the oracle's bit for bit (pins indexing independently of rounding)."""
@@ -165,10 +165,12 @@ def test_zero_segments_is_a_no_op():
     assert out.shape == (0,) and arg.shape == (0,)
 
 
-def test_unaligned_rows_use_the_scalar_path():
-    """values starting 4 bytes past an allocation (F = 4): 16-byte loads do not
-    apply and the 4-byte path must give the same results."""
-    off, vals = W.ragged(seed=9, segments=3000, mean_len=10, feat=4, dtype="f32")
+@pytest.mark.parametrize("feat", [3, 4, 6, 24])
+def test_unaligned_rows_use_the_scalar_path(feat):
+    """values starting 4 bytes past an allocation: 16- and 8-byte pieces per
+    lane do not apply and the 4-byte path must give the same results (rows
+    of 3 features also load 16-byte units from a 4-byte aligned chunk)."""
+    off, vals = W.ragged(seed=9 + feat, segments=3000, mean_len=10, feat=feat, dtype="f32")
     big = torch.zeros(vals.size + 1, dtype=torch.float32, device="cuda")
     big[1:] = gu.to_gpu(vals.reshape(-1))
     v = big[1:].view(vals.shape)
