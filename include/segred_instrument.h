@@ -20,7 +20,10 @@ extern "C" {
  * Work partition of segred_reduce.  The rows and segment ends of a call are
  * split into equal shares of the merged (rows + segment ends) sequence, one
  * per wave of the streaming kernel; segments cut by a share boundary are
- * finished by a fixed-order combine.  By default the share count is a
+ * finished by a fixed-order combine.  For rows of 32 features read 16 bytes
+ * per lane, a share size within 4 KB of rows of a multiple of 64 KB grows
+ * to that distance (aligned waves would load from the same memory channels
+ * together), and the last shares are then shorter or empty.  By default the share count is a
  * constant of the chosen kernel (one share per wave of a whole MI355X: 256
  * CUs x 4 SIMDs x the waves per SIMD the kernel is built for), so float
  * results do not depend on the device.  segred_set_shares(n) overrides it

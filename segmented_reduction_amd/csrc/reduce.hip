@@ -679,7 +679,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kTeamWpe)))
     const int64_t *off = a.offsets;
     __shared__ int64_t s_probe[kProbesA];
     const int64_t S = seg_count(a);
-    const Share sh = find_share(off, S, a.NW, wave, lane, s_probe, 1, G);
+    // period: 64 KB of rows, in items
+    const Share sh = find_share(off, S, a.NW, wave, lane, s_probe, 1, G, 65536 / (F * 4));
     const int64_t o0 = sh.o0;
     const int64_t dT = sh.D / G;  // items per team part
     auto rebase = [](acc_t p, uint32_t delta) __attribute__((always_inline)) -> acc_t {

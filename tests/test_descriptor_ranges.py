@@ -19,14 +19,23 @@ import workloads as W
 FEATS = [1, 2, 3, 4, 5, 6, 8, 12, 16, 24, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 255, 256, 257, 260]
 
 
-def _shares(off, nw, cw=1, gran=1, min_share=1):
-    """Merge-path shares (d0, d1, i0, j0, i1, j1), rows relative to off[0]."""
+def _shares(off, nw, cw=1, gran=1, min_share=1, period=0):
+    """Merge-path shares (d0, d1, i0, j0, i1, j1), rows relative to off[0];
+    with a period, share sizes within period / 16 of a multiple of it grow
+    to the band's edge."""
     o0 = int(off[0])
     s = len(off) - 1
     keys = off - o0 + cw * np.arange(s + 1)
     t = int(keys[-1])  # rows + cw * S
     dg = max(-(-t // (nw * gran)), -(-min_share // gran))
     d = dg * gran
+    if period > 0 and d >= period:
+        m, r = period // 16, d % period
+        if r < m:
+            d += m - r
+        elif r > period - m:
+            d += period - r + m
+        d = -(-d // gran) * gran
 
     def at(diag):
         i = int(np.searchsorted(keys, diag, side="right")) - 1
@@ -83,7 +92,7 @@ def test_descriptors_stay_inside_the_rows(feat):
             while lanes < units and lanes < 64:
                 lanes *= 2
             fb = lanes * (4 if vec4 else 1)
-            for _, _, _, j0, _, j1, _ in _shares(off, nw, gran=64 // lanes):
+            for _, _, _, j0, _, j1, _ in _shares(off, nw, gran=64 // lanes, period=65536 // (feat * 4)):
                 for fbase in range(0, feat, fb):
                     size = (j1 - j0) * feat * 4 - fbase * 4 if j1 > j0 else 0
                     _check(lo, hi, (o0 + j0) * feat + fbase, size, ("team", nw, fbase))

@@ -351,3 +351,26 @@ def test_extreme_keys_keep_the_first_row(kind, feat):
                 gu.say(f"extreme keys kind={kind} F={feat} op={op} mixed={mixed} shares={shares}")
                 out, arg = gu.run_gpu(vals, off, op, shares=shares)
                 gu.assert_parity(vals, off, op, out, arg, what=f"extreme {kind} F={feat} {op} mixed={mixed}")
+
+
+@pytest.mark.parametrize("shares,size", [(1, 1024), (2, 1000), (2, 1016), (2, 1024), (3, 1032), (3, 1048), (7, 1028),
+                                         (7, 1536), (5, 2040)])
+def test_team_share_sizes_near_64k_multiples(shares, size):
+    """Rows of 32 features with share sizes (rows + segment ends) within 32
+    of a multiple of 512 (64 KB of rows): the kernel grows the share size to
+    the band's edge, so the last shares are shorter or empty; results must
+    not change.  A few long segments, an empty one, a unit one."""
+    rng = np.random.default_rng(shares * 10007 + size)
+    segs = 6
+    total = shares * size - segs  # items = rows + segment ends
+    cuts = np.sort(rng.integers(0, total - 1, segs - 3))
+    lens = np.diff(np.concatenate([[0], cuts, [total - 1]])).astype(np.int64)
+    lens = np.concatenate([lens[:1], [0, 1], lens[1:]])
+    off = np.zeros(segs + 1, dtype=np.int64)
+    np.cumsum(lens, out=off[1:])
+    assert off[-1] + segs == shares * size and (lens >= 0).all()
+    vals = rng.standard_normal((int(off[-1]), 32)).astype(np.float32)
+    for op in ("sum", "max", "mean"):
+        gu.say(f"team band shares={shares} size={size} op={op}")
+        out, arg = gu.run_gpu(vals, off, op, shares=shares)
+        gu.assert_parity(vals, off, op, out, arg, what=f"team band shares={shares} size={size}")
