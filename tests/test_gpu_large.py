@@ -154,9 +154,12 @@ def test_one_dimensional_u32_sums_wrap_past_2_31_rows():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("feat,m,rows", [(64, 1, 21_000_000), (32, 4, 42_000_000)])
+@pytest.mark.parametrize("feat,m,rows", [(64, 1, 21_000_000), (32, 4, 42_000_000), (4, 4, 340_000_000),
+                                         (3, 3, 450_000_000), (2, 2, 2_200_000_000)])
 def test_rows_past_4_gib(feat, m, rows):
-    """5.4 GB of rows of 256 bytes (chunked walk) and of 128 bytes (team walk)."""
+    """5.4 GB of rows of 256 bytes (chunked walk), of 128 bytes (team walk),
+    of 16 and 12 bytes (chunks staged through LDS), and 17.6 GB of rows of
+    8 bytes: past 2^31 rows."""
     rng = np.random.default_rng(feat)
     ln = _lengths(rng, rows, 300, giant=rows // 3)
     off = np.zeros(ln.size + 1, dtype=np.int64)
