@@ -758,6 +758,71 @@ def shape_sweep(sr, torch, reps=10):
     return rows_out
 
 
+SCAN_SWEEP_FEATS = (1, 2, 3, 4, 8, 16, 32, 64, 128, 256)
+SCAN_SWEEP_LENS = (16, 4096)
+
+
+def scan_sweep(sr, torch, reps=10):
+    """Per-call rates of segred_scan (inclusive sum and max) across row widths
+    and mean segment lengths, on SWEEP_BYTES of float32 normal values with
+    the shape sweep's segment lengths.  A call's duration is the sum of its
+    two kernels' own start-to-stop times (the tails and the main kernel);
+    rates count the algorithmic bytes (values read once, outputs written
+    once, the offsets).  The first line is the library's streaming probe
+    reading and writing equal amounts, as context."""
+    n = SWEEP_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty(n, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        sr.probe_stream(src, 1, 2048, dst)
+    torch.cuda.synchronize()
+    sr.timing_enable(True)
+    sr.timing_read()
+    for _ in range(reps):
+        sr.probe_stream(src, 1, 2048, dst)
+    torch.cuda.synchronize()
+    _, _, each = sr.timing_read()
+    sr.timing_enable(False)
+    gbs = 2 * SWEEP_BYTES / (float(np.median(each)) * 1e-3) / 1e9
+    print(json.dumps({"probe": "read and write equal bytes", "GBps": round(gbs, 1),
+                      "frac": round(gbs / PEAK_HBM_GBS, 3)}), flush=True)
+    del src, dst
+    gen = torch.Generator(device="cuda")
+    for feat in SCAN_SWEEP_FEATS:
+        n = SWEEP_BYTES // (4 * feat)
+        gen.manual_seed(feat)
+        vals = torch.randn((n,) if feat == 1 else (n, feat), generator=gen, device="cuda", dtype=torch.float32)
+        out = torch.empty_like(vals)
+        for mean in SCAN_SWEEP_LENS:
+            gen.manual_seed(feat * 1000003 + mean)
+            segs = max(1, n // mean)
+            lens = torch.randint(0, 2 * mean + 1, (segs,), generator=gen, device="cuda", dtype=torch.int64)
+            lens = torch.floor(lens.double() * (n / max(float(lens.sum().item()), 1.0))).to(torch.int64)
+            lens[0] += n - int(lens.sum().item())
+            off = torch.zeros(segs + 1, dtype=torch.int64, device="cuda")
+            off[1:] = torch.cumsum(lens, 0)
+            entry = {"feat": feat, "mean_len": mean, "segments": segs}
+            for op in ("sum", "max"):
+                for _ in range(2):
+                    sr.scan(vals, off, op, out=out)
+                torch.cuda.synchronize()
+                sr.timing_enable(True)
+                sr.timing_read()
+                for _ in range(reps):
+                    sr.scan(vals, off, op, out=out)
+                torch.cuda.synchronize()
+                total_ms, _, _ = sr.timing_read()
+                sr.timing_enable(False)
+                per = total_ms / reps
+                b = 2 * n * feat * 4 + (segs + 1) * 8
+                entry[op] = {"call_us": round(per * 1e3, 2), "GBps": round(b / (per * 1e-3) / 1e9, 1),
+                             "frac": round(b / (per * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
+            print(json.dumps(entry), flush=True)
+            del off, lens
+        del vals, out
+        torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- main
 
 GATED = ["message", "rle", "skew"]  # reported beside the headline (largest) configuration
@@ -916,6 +981,8 @@ def main():
                     help="run only the streaming-ceiling probe and print its figures")
     ap.add_argument("--sweep", action="store_true",
                     help="per-call rates across row widths and mean segment lengths (one JSON line per shape)")
+    ap.add_argument("--scan-sweep", action="store_true",
+                    help="the same for the segmented scan (one JSON line per shape)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain device copy of 256 MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -944,6 +1011,9 @@ def main():
 
     if args.sweep:
         shape_sweep(sr, torch)
+        return
+    if args.scan_sweep:
+        scan_sweep(sr, torch)
         return
 
     if args.ceiling_only:
