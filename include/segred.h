@@ -80,9 +80,9 @@ enum segred_status {
  * Rows whose width is a multiple of 4 features are read and written 16
  * bytes per lane when values, out and arg_out start on 16-byte boundaries,
  * other even widths 8 bytes per lane under the same condition, other rows
- * one element per lane; rows of 2, 3, 4, 6, 8, 12, 16 or 24 features are
- * fetched in whole 1 KB stretches and reach the lanes through LDS.  Results
- * are the same either way.
+ * one element per lane; rows of fewer than 32 features (and of 32 features
+ * not on 16-byte boundaries) are fetched in whole 1 KB stretches and reach
+ * the lanes through LDS.  Results are the same either way.
  *
  * Errors: SEGRED_ERR_INVALID_ARGUMENT for S < 0, feat < 1, an unknown dtype
  * or op, a NULL values/offsets/out with S > 0, values/out not 4-byte aligned,

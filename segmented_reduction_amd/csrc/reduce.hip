@@ -280,7 +280,7 @@ __device__ __forceinline__ void write_header(const KArgs &a, int64_t wave, const
 // with its first 64 segment ends before its row count is known (up to CH
 // rows; rows past the chunk are fetched again by the next chunk), and the
 // next chunk is fetched while the current one is processed: straight into
-// the lanes' pieces, or, for fixed widths below 32 features, as whole 1 KB
+// the lanes' pieces, or, for rows of fewer than 32 features, as whole 1 KB
 // stretches that pass through LDS (the 1-D kernel's placement of 16-byte
 // units), so that no load instruction gathers small pieces from many rows.
 template <int VEC>
@@ -319,14 +319,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kRowsWpe)))
     const int64_t F = FC > 0 ? (int64_t)FC : a.F;
 
     __shared__ __attribute__((aligned(16))) uint32_t s_ends[4][CH];
-    // Rows narrower than 32 features whose width is fixed at compile time:
-    // a chunk's bytes (at most 8 KB, one feature block) are read by load
-    // instructions of 1 KB of consecutive bytes each and reach their lanes
-    // through LDS, instead of load instructions whose lanes read pieces of 4
-    // to 16 bytes from up to 64 rows.
-    constexpr bool STG = FC > 0 && FC < 32;
-    constexpr int CB = STG ? CH * FC * 4 : 0;  // bytes per chunk
-    constexpr int NL = (CB + 1023) / 1024;      // 1 KB load instructions per chunk
+    // Rows narrower than 32 features (a width fixed at compile time below
+    // 32, or any width the one feature block of at most 32 features holds):
+    // a chunk's bytes (at most 8 KB) are read by load instructions of 1 KB
+    // of consecutive bytes each and reach their lanes through LDS, instead
+    // of load instructions whose lanes read pieces of 4 to 16 bytes from up
+    // to 64 rows.
+    constexpr bool STG = FC > 0 ? FC < 32 : FB <= 32;
+    constexpr int CB = STG ? CH * (FC > 0 ? FC : FB) * 4 : 0;  // bytes per chunk (at most)
+    constexpr int NL = (CB + 1023) / 1024;                     // 1 KB load instructions per chunk
     static_assert(!STG || (FB >= FC && NL <= 8), "a staged chunk is one feature block of at most 8 KB");
     __shared__ __attribute__((aligned(16))) uint32_t s_stage[4][STG ? NL * 256 : 4];
 
@@ -386,14 +387,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kRowsWpe)))
             return voff + (uint32_t)t * (FC > 0 ? (uint32_t)(FC * 4) : rstep);
         };
         x_t x[V];
-        uint4 xr[STG ? NL : 1];  // STG: the next chunk as loaded
+        uint4 xr[STG ? NL : 1] = {};  // STG: the next chunk as loaded
+        // STG with the width read at run time: the loads this width needs
+        const int nl = FC > 0 ? NL : (int)((CH * F * 4 + 1023) / 1024);
         int64_t ic = sh.i0, jc = sh.j0;
         int64_t en = off[min(ic + 1 + lane, S)];
         {
             const auto rs = rows_of(ic, jc);
             if constexpr (STG) {
 #pragma unroll
-                for (int u = 0; u < NL; ++u) xr[u] = ld128(rs, (uint32_t)(lane * 16 + u * 1024));
+                for (int u = 0; u < NL; ++u)
+                    if (u < nl) xr[u] = ld128(rs, (uint32_t)(lane * 16 + u * 1024));
             } else {
 #pragma unroll
                 for (int t = 0; t < V; ++t) x[t] = LN::load(rs, row_off(t));
@@ -448,14 +452,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kRowsWpe)))
                 uint32_t *sx = s_stage[wid];
 #pragma unroll
                 for (int u = 0; u < NL; ++u)
-                    *reinterpret_cast<uint4 *>(&sx[flat_unit(8 * u + (lane >> 3), lane & 7) * 4]) = xr[u];
+                    if (u < nl) *reinterpret_cast<uint4 *>(&sx[flat_unit(8 * u + (lane >> 3), lane & 7) * 4]) = xr[u];
 #pragma unroll
-                for (int u = 0; u < NL; ++u) xr[u] = ld128(rsn, (uint32_t)(lane * 16 + u * 1024));
+                for (int u = 0; u < NL; ++u)
+                    if (u < nl) xr[u] = ld128(rsn, (uint32_t)(lane * 16 + u * 1024));
                 wave_lds_sync();
                 const uint32_t b0 = fvalid ? voff : 0u;
 #pragma unroll
                 for (int t = 0; t < V; ++t) {
-                    const uint32_t b = b0 + (uint32_t)(t * FC * 4);
+                    const uint32_t b = b0 + (uint32_t)t * (FC > 0 ? (uint32_t)(FC * 4) : rstep);
                     const uint32_t k = b >> 4;
                     x[t] = *reinterpret_cast<const x_t *>(sb + flat_unit((int)(k >> 3), (int)(k & 7u)) * 16 + (b & 15u));
                 }
@@ -1297,15 +1302,20 @@ static int lanes_for(int64_t units, int lo) {
 // from up to 64 places, and the L2 request rate caps that: on 512 MB of
 // rows of 2 to 24 features the team walk moved 0.04-0.52 of peak, the
 // chunked walk 0.10-0.68.  The chunked walk's pieces still come from many
-// rows per instruction, so the usual widths below 32 features (2, 3, 4, 6,
-// 8, 12, 16, 24) get kernels of their own that read each chunk (6 or 8 KB)
-// in whole 1 KB stretches through LDS: on the same 512 MB, sum and max+row
-// over segments of 4,096 rows and more went from 0.25-0.68 to 0.60-0.80 of
-// peak, over segments of 16 rows from 0.14-0.47 to 0.25-0.50.  The same
-// staging for 32 features (by chunks instead of teams) and for 64 moved less
-// on segments of 1 to 16 rows and on the power-law graph (0.58 -> 0.54 of
-// peak), so those keep their direct loads.  One feature per lane on 2 or 4
-// lanes takes V = 8 instead of 24.
+// rows per instruction, so rows of fewer than 32 features read each chunk
+// in whole 1 KB stretches through LDS.  The usual widths (2, 3, 4, 6, 8, 12,
+// 16, 24) get kernels of their own, with the width fixed and chunks of 6 or
+// 8 KB: on the same 512 MB, sum and max+row over segments of 4,096 rows and
+// more went from 0.25-0.68 to 0.60-0.80 of peak, over segments of 16 rows
+// from 0.14-0.47 to 0.25-0.50.  The other widths below 32 share the kernels
+// of their lane count, the width read at run time (chunks of 2 to 8 KB):
+// 5, 7, 10, 20 and 30 features on long segments went from 0.24-0.64 to
+// 0.39-0.77, on segments of 128 rows from 0.23-0.56 to 0.23-0.60, and lost
+// up to 0.05 on segments of 4 and 16 rows.  The same staging for 32
+// features (by chunks instead of teams) and for 64 moved less on segments
+// of 1 to 16 rows and on the power-law graph (0.58 -> 0.54 of peak), so
+// those keep their direct loads.  One feature per lane on 2 or 4 lanes
+// takes V = 8 instead of 24.
 struct Pick {
     const void *kernel;
     int64_t waves;  // shares (one per wave) of a call

@@ -165,7 +165,7 @@ def test_zero_segments_is_a_no_op():
     assert out.shape == (0,) and arg.shape == (0,)
 
 
-@pytest.mark.parametrize("feat", [3, 4, 6, 24])
+@pytest.mark.parametrize("feat", [3, 4, 6, 24, 31, 32])
 def test_unaligned_rows_use_the_scalar_path(feat):
     """values starting 4 bytes past an allocation: 16- and 8-byte pieces per
     lane do not apply and the 4-byte path must give the same results (rows
