@@ -705,7 +705,7 @@ def stream_ceiling(sr, torch, reps=20):
 
 # ---------------------------------------------------------------- shape sweep
 
-SWEEP_FEATS = (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 64, 128, 256)
+SWEEP_FEATS = (1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 20, 24, 32, 64, 128, 256)
 SWEEP_LENS = (1, 4, 16, 128, 4096, 1 << 20)
 SWEEP_BYTES = 512 << 20  # input per shape: twice the last-level cache
 
