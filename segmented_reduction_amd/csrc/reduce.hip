@@ -1314,8 +1314,10 @@ static int lanes_for(int64_t units, int lo) {
 // up to 0.05 on segments of 4 and 16 rows.  The same staging for 32
 // features (by chunks instead of teams) and for 64 moved less on segments
 // of 1 to 16 rows and on the power-law graph (0.58 -> 0.54 of peak), so
-// those keep their direct loads.  One feature per lane on 2 or 4 lanes
-// takes V = 8 instead of 24.
+// those keep their direct loads.  The kernels that read the width take V
+// rows per group so that a chunk holds up to 8 KB (32 for one feature per
+// lane, 16 for two): against V = 24 and 8, segments of 16 rows of 10, 14
+// and 30 features went from 0.23-0.35 to 0.30-0.46 of peak.
 struct Pick {
     const void *kernel;
     int64_t waves;  // shares (one per wave) of a call
@@ -1350,19 +1352,19 @@ static Pick pick_kernel(int64_t feat, bool aligned16) {
         if (feat == 6) return SEGRED_ROWS(4, 16, 2, 6);
         switch (lanes_for(feat / 2, 1)) {
         case 4: return SEGRED_ROWS(4, 8, 2, 0);
-        case 8: return SEGRED_ROWS(8, 8, 2, 0);
-        case 16: return SEGRED_ROWS(16, 8, 2, 0);
+        case 8: return SEGRED_ROWS(8, 16, 2, 0);
+        case 16: return SEGRED_ROWS(16, 16, 2, 0);
         case 32: return SEGRED_ROWS(32, 8, 2, 0);
         default: return SEGRED_ROWS(64, 8, 2, 0);
         }
     }
     if (feat == 3) return SEGRED_ROWS(4, 32, 1, 3);
     switch (lanes_for(feat, 2)) {
-    case 2: return SEGRED_ROWS(2, 8, 1, 0);
-    case 4: return SEGRED_ROWS(4, 8, 1, 0);
-    case 8: return SEGRED_ROWS(8, 24, 1, 0);
-    case 16: return SEGRED_ROWS(16, 24, 1, 0);
-    case 32: return SEGRED_ROWS(32, 24, 1, 0);
+    case 2: return SEGRED_ROWS(2, 32, 1, 0);
+    case 4: return SEGRED_ROWS(4, 32, 1, 0);
+    case 8: return SEGRED_ROWS(8, 32, 1, 0);
+    case 16: return SEGRED_ROWS(16, 32, 1, 0);
+    case 32: return SEGRED_ROWS(32, 32, 1, 0);
     default: return SEGRED_ROWS(64, 24, 1, 0);
     }
 }

@@ -16,7 +16,7 @@ import pytest
 
 import workloads as W
 
-FEATS = [1, 2, 3, 4, 5, 6, 8, 12, 16, 24, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 255, 256, 257, 260]
+FEATS = [1, 2, 3, 4, 5, 6, 8, 10, 12, 14, 16, 18, 24, 30, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 255, 256, 257, 260]
 
 
 def _shares(off, nw, cw=1, gran=1, min_share=1, period=0):
@@ -105,15 +105,15 @@ def test_descriptors_stay_inside_the_rows(feat):
                 if vec == 4 and not vec4 or vec == 2 and (vec4 or feat % 2):
                     continue
                 lanes = max(lanes, 1 if vec > 1 else 2)
-                # rows per group (rows of 2, 3, 4, 6, 8, 12, 16 and 24
-                # features are read through LDS, 1 KB per load instruction:
-                # the same bytes of the same descriptor)
+                # rows per group (rows of fewer than 32 features are read
+                # through LDS, 1 KB per load instruction: the same bytes of
+                # the same descriptor)
                 if vec == 4:
                     v = 8
                 elif vec == 2:
-                    v = 16 if feat in (2, 6) else 8
+                    v = 16 if feat in (2, 6) or lanes in (8, 16) else 8
                 else:
-                    v = 32 if feat == 3 else 8 if lanes <= 4 else 24
+                    v = 32 if lanes <= 32 else 24
                 ch = (64 // lanes) * v
                 for _, _, _, j0, _, j1, _ in _shares(off, nw):
                     for jc in range(j0, j1 + 1):
